@@ -1,0 +1,209 @@
+"""CPU oracle for the one-GPU MoE expert-parallel layout / dispatch / combine path.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The product library under
+``combine_get_dispatch_03_amd/`` never imports it, and it imports nothing from there.
+
+The arithmetic lives in ``ep_oracle.c`` (plain C, single thread, gcc ``-O2 -ffp-contract=off``); this module
+only builds that file and marshals numpy arrays into it.  See ``ep_oracle.c`` for the definitions, their
+citations and the list of pins; the FP8 scale recipe is a reading the pages do not fix (parity unpinned for
+that choice; the e4m3 codec itself is pinned).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ep_oracle.c")
+_LIB = os.path.join(_HERE, "libep_oracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile ep_oracle.c with gcc into oracle/libep_oracle.so and return its path."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
+               "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    build()
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    I64 = ctypes.c_int64
+    lib.oracle_bf16_to_f32.restype = ctypes.c_float
+    lib.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.oracle_f64_to_bf16.restype = ctypes.c_uint16
+    lib.oracle_f64_to_bf16.argtypes = [ctypes.c_double]
+    lib.oracle_e4m3_decode.restype = ctypes.c_float
+    lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+    lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+    lib.oracle_e4m3_encode_array.restype = None
+    lib.oracle_e4m3_encode_array.argtypes = [P, I64, P]
+    lib.oracle_f64_to_bf16_array.restype = None
+    lib.oracle_f64_to_bf16_array.argtypes = [P, I64, P]
+    lib.oracle_recv_capacity.restype = I64
+    lib.oracle_recv_capacity.argtypes = [I, I, I, I]
+    lib.oracle_layout.restype = I
+    lib.oracle_layout.argtypes = [P, I, I, I, I, I, I, P, P, P, P, P, P, I64, P, P]
+    lib.oracle_quantize_row.restype = None
+    lib.oracle_quantize_row.argtypes = [P, I, P, P]
+    lib.oracle_dispatch.restype = I
+    lib.oracle_dispatch.argtypes = [P, I, I, I, P, P, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P]
+    lib.oracle_combine.restype = None
+    lib.oracle_combine.argtypes = [P, I, P, P, I, I, P, P]
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    """Contiguous array of exactly this dtype (no silent conversion of a differently typed input)."""
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.dtype(dtype):
+        raise TypeError("expected %s array, got %s" % (np.dtype(dtype), a.dtype))
+    return a
+
+
+# ---- number formats ---------------------------------------------------------------------------------
+
+def bf16_to_f32(bits):
+    """BF16 bit patterns (uint16) -> float32 values."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def f64_to_bf16(v):
+    """float64 values -> BF16 bit patterns, round to nearest even."""
+    v = _c(np.asarray(v, dtype=np.float64), np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    _load().oracle_f64_to_bf16_array(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def e4m3_encode(v):
+    """float32 values -> e4m3fn codes (uint8), RNE, saturating."""
+    v = _c(np.asarray(v, dtype=np.float32), np.float32)
+    out = np.empty(v.shape, dtype=np.uint8)
+    _load().oracle_e4m3_encode_array(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def e4m3_decode(codes):
+    lib = _load()
+    codes = np.asarray(codes, dtype=np.uint8)
+    return np.array([lib.oracle_e4m3_decode(int(c)) for c in codes.ravel()], dtype=np.float32).reshape(codes.shape)
+
+
+# ---- layout / dispatch / combine --------------------------------------------------------------------
+
+def recv_capacity(num_tokens, num_topk, num_local_experts, expert_alignment):
+    return int(_load().oracle_recv_capacity(num_tokens, num_topk, num_local_experts, expert_alignment))
+
+
+def layout(topk_idx, num_experts, num_ranks=1, rank=0, expert_alignment=1):
+    """Returns a dict of numpy arrays: cnt, ntok_rank, in_rank, psum, slot, row_src, send_slot, num_invalid,
+    plus cap (int)."""
+    topk_idx = _c(topk_idx, np.int64)
+    T, K = topk_idx.shape
+    E, R, A = num_experts, num_ranks, expert_alignment
+    El = E // R
+    cap = recv_capacity(T, K, El, A)
+    out = dict(
+        cnt=np.empty(E, np.int32), ntok_rank=np.empty(R, np.int32), in_rank=np.empty((T, R), np.uint8),
+        psum=np.empty(El + 1, np.int32), slot=np.empty((T, K), np.int32), row_src=np.empty(cap, np.int32),
+        send_slot=np.empty((T, R), np.int32), num_invalid=np.empty(1, np.int32))
+    rc = _load().oracle_layout(_ptr(topk_idx), T, K, E, R, rank, A, _ptr(out["cnt"]), _ptr(out["ntok_rank"]),
+                               _ptr(out["in_rank"]), _ptr(out["psum"]), _ptr(out["slot"]), _ptr(out["row_src"]),
+                               cap, _ptr(out["send_slot"]), _ptr(out["num_invalid"]))
+    if rc != 0:
+        raise ValueError("oracle_layout rejected its arguments")
+    out["cap"] = cap
+    return out
+
+
+def quantize_row(x_bits):
+    x_bits = _c(x_bits, np.uint16)
+    H = x_bits.shape[-1]
+    q = np.empty(H, np.uint8)
+    s = np.empty(H // 128, np.float32)
+    _load().oracle_quantize_row(_ptr(x_bits), H, _ptr(q), _ptr(s))
+    return q, s
+
+
+def dispatch(x_bits, topk_idx, topk_weights, lay, num_experts, num_ranks=1, rank=0, expert_alignment=1,
+             fp8=False, zero_pad=False, recv_fill=None, want_meta=True, want_send_meta=True):
+    """Oracle dispatch.  x_bits: uint16 [T,H] (BF16 bits).  lay: the dict from layout().
+
+    recv_fill: optional (data_byte, scale_value) canary used to initialise the receive buffers, so that rows
+    the dispatch must leave untouched can be checked.  Returns a dict of numpy arrays."""
+    x_bits = _c(x_bits, np.uint16)
+    topk_idx = _c(topk_idx, np.int64)
+    T, H = x_bits.shape
+    K = topk_idx.shape[1]
+    R = num_ranks
+    cap = lay["cap"]
+    G = H // 128 if fp8 else 0
+    fill_b, fill_s = recv_fill if recv_fill is not None else (0, 0.0)
+    if fp8:
+        recv_x = np.full((cap, H), fill_b, np.uint8)
+        recv_scales = np.full((cap, G), fill_s, np.float32)
+    else:
+        recv_x = np.full((cap, H * 2), fill_b, np.uint8)
+        recv_scales = None
+    out = dict(recv_x=recv_x, recv_scales=recv_scales)
+    out["recv_src"] = np.full(cap, -7, np.int32) if want_meta else None
+    out["recv_w"] = np.full(cap, -7.0, np.float32) if want_meta else None
+    if R > 1:
+        rowb = H if fp8 else 2 * H
+        out["send_x"] = np.full((R, T, rowb), fill_b, np.uint8)
+        out["send_scales"] = np.full((R, T, G), fill_s, np.float32) if fp8 else None
+        out["send_src"] = np.full((R, T), -7, np.int32) if want_send_meta else None
+        out["send_topk_idx"] = np.full((R, T, K), -7, np.int64) if want_send_meta else None
+        out["send_topk_w"] = np.full((R, T, K), -7.0, np.float32) if want_send_meta else None
+    else:
+        for k in ("send_x", "send_scales", "send_src", "send_topk_idx", "send_topk_w"):
+            out[k] = None
+    w = None if topk_weights is None else _c(topk_weights, np.float32)
+    rc = _load().oracle_dispatch(
+        _ptr(x_bits), T, H, K, _ptr(w), _ptr(topk_idx), num_experts, R, rank, expert_alignment, int(fp8),
+        int(zero_pad), _ptr(lay["cnt"]), _ptr(lay["psum"]), _ptr(lay["slot"]), _ptr(lay["send_slot"]),
+        _ptr(out["recv_x"]), _ptr(out["recv_scales"]), _ptr(out["recv_src"]), _ptr(out["recv_w"]),
+        _ptr(out["send_x"]), _ptr(out["send_scales"]), _ptr(out["send_src"]), _ptr(out["send_topk_idx"]),
+        _ptr(out["send_topk_w"]))
+    if rc != 0:
+        raise ValueError("oracle_dispatch rejected its arguments")
+    if not fp8:
+        out["recv_x"] = out["recv_x"].view(np.uint16)
+        if out["send_x"] is not None:
+            out["send_x"] = out["send_x"].view(np.uint16)
+    return out
+
+
+def combine(y_bits, slot, topk_weights=None, bias_bits=None):
+    """Oracle combine in float64.  y_bits: uint16 [rows,H]; slot: int32 [T,K]; bias_bits: uint16 [T,H]."""
+    y_bits = _c(y_bits, np.uint16)
+    slot = _c(slot, np.int32)
+    T, K = slot.shape
+    H = y_bits.shape[1]
+    w = None if topk_weights is None else _c(topk_weights, np.float32)
+    b = None if bias_bits is None else _c(bias_bits, np.uint16)
+    out = np.empty((T, H), np.float64)
+    _load().oracle_combine(_ptr(y_bits), H, _ptr(slot), _ptr(w), T, K, _ptr(b), _ptr(out))
+    return out
