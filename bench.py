@@ -1,0 +1,284 @@
+"""Benchmark of the MoE expert-parallel layout / dispatch / combine path on one MI355X.
+
+A step is one pass of the whole path over one batch of the prefill workload: ep_get_layout, then FP8 dispatch
+with zero padding, then the weighted BF16 combine (4096 tokens, hidden 7168, 256 experts in 8 groups with
+group-limited top-4-group / top-8 routing, alignment 128).  Inputs and expert outputs are resident in HBM
+before timing starts.  W untimed warm-up steps, then exactly K timed steps bracketed by device syncs; HIP
+events on the launch stream give each kernel's average duration over the timed steps.
+
+Prints one JSON line.  `value` is the step's effective HBM throughput: the algorithmic bytes of layout +
+dispatch + combine per step divided by the measured step time.  Algorithmic bytes are what the method must
+move: every token row read once, every routed row written once, padding rows when zero padding is requested,
+the expert rows gathered once by combine and the output written once (the byte model is in
+bytes_model()).  Two extra objects: `roofline` for the dominant kernel and `cpu_baseline` (the oracle timed
+on the host).
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--flush-samples 50] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0        # MI355X published HBM3E peak
+WORKLOAD = "prefill"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill.json")
+KERNEL_SOURCES = {
+    "k_dispatch_fp8": "ep_dispatch.hip",
+    "k_combine": "ep_combine.hip",
+    "layout": "ep_layout.hip",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--flush-samples", type=int, default=50,
+                    help="per-kernel samples with a cache flush before each (0 = skip)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before the steps (counter calibration)")
+    ap.add_argument("--workload", default=WORKLOAD)
+    return ap.parse_args()
+
+
+def bytes_model(cfg, counts):
+    """Algorithmic bytes of each operation for one step.  counts: V (valid local rows), P (padding rows),
+    N_send (send-window rows)."""
+    T, H, K, E, R = cfg.num_tokens, cfg.hidden, cfg.num_topk, cfg.num_experts, cfg.num_ranks
+    El = E // R
+    V, P, S = counts["V"], counts["P"], counts["N_send"]
+    row_b = (H + 4 * (H // 128)) if cfg.fp8 else 2 * H
+    layout = T * K * 8 + T * K * 4 + T * R + 4 * (E + R + El + 2) + (T * R * 4 if R > 1 else 0)
+    dispatch = (T * 2 * H                      # x, read once
+                + T * K * 4 + T * K * 4        # slot map + routing weights
+                + (T * R * 4 if R > 1 else 0)  # send slots
+                + V * (row_b + 8)              # routed rows + row metadata (src idx, weight)
+                + P * 8 + (P * row_b if cfg.zero_padding else 0)
+                + S * (row_b + 4 + K * 12))    # send rows + src idx + topk idx (int64) / weight
+    combine = V * 2 * H + T * K * 8 + T * 2 * H + (T * 2 * H if cfg.bias else 0)
+    return dict(layout=layout, dispatch=dispatch, combine=combine, row_bytes=row_b)
+
+
+def source_hash(fname):
+    p = os.path.join(ROOT, "combine_get_dispatch_03_amd", "csrc", fname)
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(kernel):
+    """HBM bytes per launch from the committed counter summary, or None if absent or stale."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    if not k or k.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, y_bits, cfg):
+    """The oracle as it stands (single thread, plain C) on the full workload; median of 3 runs."""
+    import numpy as np
+
+    import oracle as O
+    import workloads as W
+
+    idx = inp["topk_idx"].numpy()
+    w = inp["topk_weights"].numpy()
+    x = W.bf16_bits(inp["x"])
+    bias = W.bf16_bits(inp["bias"]) if inp["bias"] is not None else None
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        lay = O.layout(idx, cfg.num_experts, cfg.num_ranks, cfg.rank, cfg.expert_alignment)
+        O.dispatch(x, idx, w, lay, cfg.num_experts, cfg.num_ranks, cfg.rank, cfg.expert_alignment, fp8=cfg.fp8,
+                   zero_pad=cfg.zero_padding, recv_fill=None)
+        O.combine(y_bits, lay["slot"], w, bias)
+        times.append(time.perf_counter() - t0)
+    El = cfg.num_experts // cfg.num_ranks
+    cnt = lay["cnt"][cfg.rank * El:(cfg.rank + 1) * El]
+    V = int(cnt.sum())
+    counts = dict(V=V, P=int(lay["psum"][-1]) - V, N_send=int(sum(lay["ntok_rank"][r] for r in range(cfg.num_ranks)
+                                                                    if r != cfg.rank)))
+    bm = bytes_model(cfg, counts)
+    total = bm["layout"] + bm["dispatch"] + bm["combine"]
+    med = float(np.median(times))
+    return dict(value=round(total / med / 1e9, 3), unit="GB/s", cores=1, kind="oracle",
+                sample="full %s workload (layout + FP8 dispatch + combine), median of 3 runs, %.2f s each"
+                       % (cfg.name, med))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import combine_get_dispatch_03_amd as ep
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = W.make_inputs(args.workload)
+    cfg = inp["cfg"]
+    idx = inp["topk_idx"].to(dev)
+    w = inp["topk_weights"].to(dev)
+    x = inp["x"].to(dev)
+    bias = inp["bias"].to(dev) if inp["bias"] is not None else None
+
+    # persistent buffers (allocated once, outside the timed region)
+    T, K, E, R = cfg.num_tokens, cfg.num_topk, cfg.num_experts, cfg.num_ranks
+    ws = torch.empty(ep.ep_layout_workspace_bytes(T, K, E, R), dtype=torch.uint8, device=dev)
+    lay_out = dict(num_tokens_per_rank=torch.empty(R, dtype=torch.int32, device=dev),
+                   num_tokens_per_expert=torch.empty(E, dtype=torch.int32, device=dev),
+                   is_token_in_rank=torch.empty((T, R), dtype=torch.uint8, device=dev),
+                   psum_num_recv_tokens_per_expert=torch.empty(E // R + 1, dtype=torch.int32, device=dev),
+                   num_invalid_topk=torch.empty(1, dtype=torch.int32, device=dev))
+    h0, _ = ep.ep_get_layout(idx, E, R, cfg.rank, cfg.expert_alignment, workspace=ws, outputs=lay_out)
+    dout = ep.alloc_dispatch_outputs(h0, cfg.hidden, cfg.fp8, device=dev)
+    y = W.random_expert_outputs(h0.recv_capacity, cfg.hidden, seed=1234, device=dev)
+    out = torch.empty((T, cfg.hidden), dtype=torch.bfloat16, device=dev)
+    h0.free()
+
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        h, _ = ep.ep_get_layout(idx, E, R, cfg.rank, cfg.expert_alignment, workspace=ws, outputs=lay_out)
+        if ev is not None:
+            ev[1].record(stream)
+        ep.ep_dispatch(h, x, w, fp8=cfg.fp8, do_zero_padding=cfg.zero_padding, out=dout)
+        if ev is not None:
+            ev[2].record(stream)
+        ep.ep_combine(h, y, w, bias, out=out)
+        if ev is not None:
+            ev[3].record(stream)
+        return h
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    k_ms = {"layout": [], "dispatch": [], "combine": []}
+    for e in evs:
+        k_ms["layout"].append(e[0].elapsed_time(e[1]))
+        k_ms["dispatch"].append(e[1].elapsed_time(e[2]))
+        k_ms["combine"].append(e[2].elapsed_time(e[3]))
+    avg = {k: float(np.mean(v)) for k, v in k_ms.items()}
+
+    # per-kernel samples with a cache flush before each (10 warm-up + N samples, the pages' method)
+    flushed = None
+    if args.flush_samples > 0:
+        junk = torch.empty(2 << 30, dtype=torch.uint8, device=dev).fill_(3)
+        fl = {"layout": [], "dispatch": [], "combine": []}
+        for i in range(10 + args.flush_samples):
+            junk.sum(dtype=torch.int64)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            step(ev)
+            torch.cuda.synchronize()
+            if i >= 10:
+                fl["layout"].append(ev[0].elapsed_time(ev[1]))
+                fl["dispatch"].append(ev[1].elapsed_time(ev[2]))
+                fl["combine"].append(ev[2].elapsed_time(ev[3]))
+        del junk
+        flushed = {k: float(np.median(v)) for k, v in fl.items()}
+
+    # device counts after the timed loop
+    cnt = lay_out["num_tokens_per_expert"].cpu().numpy()
+    psum = lay_out["psum_num_recv_tokens_per_expert"].cpu().numpy()
+    ntr = lay_out["num_tokens_per_rank"].cpu().numpy()
+    El = E // R
+    V = int(cnt[cfg.rank * El:(cfg.rank + 1) * El].sum())
+    counts = dict(V=V, P=int(psum[-1]) - V, N_send=int(sum(ntr[r] for r in range(R) if r != cfg.rank)))
+    bm = bytes_model(cfg, counts)
+    step_bytes = bm["layout"] + bm["dispatch"] + bm["combine"]
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    def gbps(b, ms):
+        return b / (ms * 1e-3) / 1e9
+
+    kern = {
+        "layout": dict(us=round(avg["layout"] * 1e3, 2), bytes=bm["layout"]),
+        "dispatch": dict(us=round(avg["dispatch"] * 1e3, 2), bytes=bm["dispatch"],
+                         GBps=round(gbps(bm["dispatch"], avg["dispatch"]), 1),
+                         pct_peak=round(100 * gbps(bm["dispatch"], avg["dispatch"]) / HBM_PEAK_GBPS, 1)),
+        "combine": dict(us=round(avg["combine"] * 1e3, 2), bytes=bm["combine"],
+                        GBps=round(gbps(bm["combine"], avg["combine"]), 1),
+                        pct_peak=round(100 * gbps(bm["combine"], avg["combine"]) / HBM_PEAK_GBPS, 1)),
+    }
+    if flushed is not None:
+        for k in ("dispatch", "combine"):
+            kern[k]["us_flushed_median"] = round(flushed[k] * 1e3, 2)
+            kern[k]["GBps_flushed"] = round(gbps(bm[k], flushed[k]), 1)
+        kern["layout"]["us_flushed_median"] = round(flushed["layout"] * 1e3, 2)
+
+    dom = "dispatch" if avg["dispatch"] >= avg["combine"] else "combine"
+    dom_kernel = {"dispatch": "k_dispatch_fp8", "combine": "k_combine"}[dom]
+    achieved = gbps(bm[dom], avg[dom])
+    roofline = dict(bound="hbm", kernel=dom_kernel, achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=load_traffic(dom_kernel),
+                    algorithmic_bytes=bm[dom], avg_launch_us=round(avg[dom] * 1e3, 2))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        y_bits = y.cpu().view(torch.int16).numpy().view(np.uint16)
+        cpu = cpu_baseline(inp, y_bits, cfg)
+
+    line = dict(
+        metric="dispatch/combine effective HBM GB/s + % of peak, 4096 tok x 7168 top-8, 1 GPU",
+        value=round(value, 1), unit="GB/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=round(ms_per_step, 4), higher_is_better=True, scaling="weak", vs_baseline=None,
+        dtype="fp32", data="synthetic",
+        config=dict(workload="%s: %d tok x hidden %d, %d experts%s, top-%d, FP8 e4m3 per-128 dispatch%s, "
+                              "BF16 combine, alignment %d" % (
+                                  cfg.name, T, cfg.hidden, E,
+                                  " (8 groups, top-4 groups)" if cfg.routing == "grouped" else "", K,
+                                  " + zero padding" if cfg.zero_padding else "", cfg.expert_alignment),
+                    tokens=T, hidden=cfg.hidden, experts=E, topk=K, ranks=R, expert_alignment=cfg.expert_alignment,
+                    valid_rows=V, pad_rows=counts["P"], A_pad=round(int(psum[-1]) / max(V, 1), 4),
+                    data_dtypes="x bf16 -> recv e4m3 + fp32 scales; y bf16 -> out bf16 (fp32 accumulate)"),
+        tokens_per_s=round(T / (ms_per_step * 1e-3), 1),
+        kernels=kern,
+        roofline=roofline,
+        cpu_baseline=cpu,
+    )
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,267 @@
+"""Python binding of libep_mi355x.so (include/ep.h): MoE expert-parallel layout, dispatch and combine on one
+MI355X (gfx950) GPU.
+
+The functions keep the C names (ep_get_layout, ep_dispatch, ep_combine, ep_handle_free, ep_recv_capacity,
+ep_layout_workspace_bytes).  They only marshal arguments: tensors become device pointers, the stream is
+torch's current HIP stream, and output tensors are allocated by torch when the caller does not pass them.
+Every step of the path runs in the HIP kernels of the library; there is no other implementation, and if
+the library is not built or cannot be loaded the import of this binding fails.
+
+    h, lay = ep_get_layout(topk_idx, num_experts=256, expert_alignment=128)
+    d = ep_dispatch(h, x, topk_weights, fp8=True, do_zero_padding=True)
+    out = ep_combine(h, y, topk_weights, bias=None)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libep_mi355x.so")
+
+EP_OK = 0
+EP_DTYPE_BF16 = 0
+EP_DTYPE_FP8_E4M3 = 1
+
+
+class EPError(RuntimeError):
+    pass
+
+
+class _DispatchOut(ctypes.Structure):
+    _fields_ = [
+        ("recv_x", ctypes.c_void_p), ("recv_x_scales", ctypes.c_void_p), ("recv_src_idx", ctypes.c_void_p),
+        ("recv_topk_weights", ctypes.c_void_p), ("recv_capacity", ctypes.c_int64),
+        ("send_x", ctypes.c_void_p), ("send_x_scales", ctypes.c_void_p), ("send_src_idx", ctypes.c_void_p),
+        ("send_topk_idx", ctypes.c_void_p), ("send_topk_weights", ctypes.c_void_p),
+    ]
+
+
+def _load_library():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libep_mi355x.so is not built: run `python -m combine_get_dispatch_03_amd.build` "
+                          "(or __graft_entry__.build())")
+    # torch is imported first, so the HIP runtime the library links (soname libamdhip64.so.7) resolves to the
+    # one torch already loaded: streams and device pointers then belong to the same runtime.
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    lib.ep_recv_capacity.restype = I64
+    lib.ep_recv_capacity.argtypes = [I, I, I, I]
+    lib.ep_layout_workspace_bytes.restype = SZ
+    lib.ep_layout_workspace_bytes.argtypes = [I, I, I, I]
+    lib.ep_status_string.restype = ctypes.c_char_p
+    lib.ep_status_string.argtypes = [I]
+    lib.ep_last_error.restype = ctypes.c_char_p
+    lib.ep_last_error.argtypes = []
+    lib.ep_get_layout.restype = I
+    lib.ep_get_layout.argtypes = [P, I, I, I, I, I, I, P, SZ, P, P, P, P, P, ctypes.POINTER(P), P]
+    lib.ep_dispatch.restype = I
+    lib.ep_dispatch.argtypes = [P, P, I, P, I, I, I, ctypes.POINTER(_DispatchOut), P]
+    lib.ep_combine.restype = I
+    lib.ep_combine.argtypes = [P, P, I, I64, P, P, P, P]
+    lib.ep_handle_free.restype = I
+    lib.ep_handle_free.argtypes = [P]
+    return lib
+
+
+_lib = _load_library()
+
+
+def hip_runtimes_loaded() -> list[str]:
+    """Paths of the libamdhip64 copies mapped into this process (exactly one is expected)."""
+    paths = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64" in line:
+                paths.add(line.split()[-1])
+    return sorted(paths)
+
+
+def _check(status: int, what: str):
+    if status != EP_OK:
+        msg = _lib.ep_last_error().decode(errors="replace")
+        raise EPError("%s failed: %s (%s)" % (what, _lib.ep_status_string(status).decode(), msg))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, dtype, name, device=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    return t
+
+
+def ep_recv_capacity(num_tokens, num_topk, num_local_experts, expert_alignment) -> int:
+    return int(_lib.ep_recv_capacity(num_tokens, num_topk, num_local_experts, expert_alignment))
+
+
+def ep_layout_workspace_bytes(num_tokens, num_topk, num_experts, num_ranks=1) -> int:
+    return int(_lib.ep_layout_workspace_bytes(num_tokens, num_topk, num_experts, num_ranks))
+
+
+class Handle:
+    """Owns an ep_handle_t plus references to the tensors it points into (topk_idx and the workspace)."""
+
+    def __init__(self, ptr, topk_idx, workspace, num_tokens, num_topk, num_experts, num_ranks, rank,
+                 expert_alignment):
+        self._ptr = ptr
+        self.topk_idx = topk_idx
+        self.workspace = workspace
+        self.num_tokens, self.num_topk, self.num_experts = num_tokens, num_topk, num_experts
+        self.num_ranks, self.rank, self.expert_alignment = num_ranks, rank, expert_alignment
+        self.num_local_experts = num_experts // num_ranks
+        self.recv_capacity = ep_recv_capacity(num_tokens, num_topk, self.num_local_experts, expert_alignment)
+
+    @property
+    def ptr(self):
+        if self._ptr is None:
+            raise EPError("handle already freed")
+        return self._ptr
+
+    def free(self):
+        if self._ptr is not None and _lib is not None:
+            _check(_lib.ep_handle_free(self._ptr), "ep_handle_free")
+        self._ptr = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def ep_get_layout(topk_idx, num_experts, num_ranks=1, rank=0, expert_alignment=1, workspace=None, outputs=None,
+                  stream=None):
+    """Layout of `topk_idx` (int64 [T, K] on the GPU).  Returns (Handle, dict) with the device outputs
+    num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank, psum_num_recv_tokens_per_expert and
+    num_invalid_topk.  `outputs` may supply any of those tensors (or None entries to skip them)."""
+    _need(topk_idx, torch.int64, "topk_idx")
+    if topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be [num_tokens, num_topk]")
+    T, K = topk_idx.shape
+    dev = topk_idx.device
+    nbytes = ep_layout_workspace_bytes(T, K, num_experts, num_ranks)
+    if nbytes == 0:
+        raise EPError("ep_layout_workspace_bytes rejected the sizes (T=%d K=%d E=%d R=%d)"
+                      % (T, K, num_experts, num_ranks))
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    El = num_experts // max(num_ranks, 1)
+    if outputs is None:
+        outputs = dict(
+            num_tokens_per_rank=torch.empty(num_ranks, dtype=torch.int32, device=dev),
+            num_tokens_per_expert=torch.empty(num_experts, dtype=torch.int32, device=dev),
+            is_token_in_rank=torch.empty((T, num_ranks), dtype=torch.uint8, device=dev),
+            psum_num_recv_tokens_per_expert=torch.empty(El + 1, dtype=torch.int32, device=dev),
+            num_invalid_topk=torch.empty(1, dtype=torch.int32, device=dev))
+    h = ctypes.c_void_p()
+    _check(_lib.ep_get_layout(
+        _ptr(topk_idx), T, K, num_experts, num_ranks, rank, expert_alignment, _ptr(workspace), workspace.numel(),
+        _ptr(outputs.get("num_tokens_per_rank")), _ptr(outputs.get("num_tokens_per_expert")),
+        _ptr(outputs.get("is_token_in_rank")), _ptr(outputs.get("psum_num_recv_tokens_per_expert")),
+        _ptr(outputs.get("num_invalid_topk")), ctypes.byref(h), _stream(stream)), "ep_get_layout")
+    return Handle(h, topk_idx, workspace, T, K, num_experts, num_ranks, rank, expert_alignment), outputs
+
+
+def alloc_dispatch_outputs(handle: Handle, hidden: int, fp8: bool, want_meta=True, want_send_meta=True,
+                           device=None, recv_capacity=None):
+    """Allocate (uninitialised) dispatch output tensors for `handle`."""
+    dev = device if device is not None else handle.topk_idx.device
+    cap = handle.recv_capacity if recv_capacity is None else recv_capacity
+    T, K, R = handle.num_tokens, handle.num_topk, handle.num_ranks
+    G = hidden // 128
+    o = {}
+    if fp8:
+        o["recv_x"] = torch.empty((cap, hidden), dtype=torch.uint8, device=dev)
+        o["recv_x_scales"] = torch.empty((cap, G), dtype=torch.float32, device=dev)
+    else:
+        o["recv_x"] = torch.empty((cap, hidden), dtype=torch.bfloat16, device=dev)
+        o["recv_x_scales"] = None
+    o["recv_src_idx"] = torch.empty(cap, dtype=torch.int32, device=dev) if want_meta else None
+    o["recv_topk_weights"] = torch.empty(cap, dtype=torch.float32, device=dev) if want_meta else None
+    if R > 1:
+        o["send_x"] = torch.empty((R, T, hidden), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
+        o["send_x_scales"] = torch.empty((R, T, G), dtype=torch.float32, device=dev) if fp8 else None
+        o["send_src_idx"] = torch.empty((R, T), dtype=torch.int32, device=dev) if want_send_meta else None
+        o["send_topk_idx"] = torch.empty((R, T, K), dtype=torch.int64, device=dev) if want_send_meta else None
+        o["send_topk_weights"] = torch.empty((R, T, K), dtype=torch.float32, device=dev) if want_send_meta else None
+    else:
+        for k in ("send_x", "send_x_scales", "send_src_idx", "send_topk_idx", "send_topk_weights"):
+            o[k] = None
+    return o
+
+
+def ep_dispatch(handle: Handle, x, topk_weights=None, fp8=True, do_expand=True, do_zero_padding=False, out=None,
+                want_meta=True, want_send_meta=True, stream=None):
+    """Dispatch `x` (bf16 [T, H]) through `handle`.  Returns the dict of output tensors (allocated here unless
+    `out` is given; rows that the call does not write keep whatever the tensors held)."""
+    _need(x, torch.bfloat16, "x")
+    if x.dim() != 2 or x.shape[0] != handle.num_tokens:
+        raise ValueError("x must be [num_tokens, hidden]")
+    H = x.shape[1]
+    if topk_weights is not None:
+        _need(topk_weights, torch.float32, "topk_weights", shape=(handle.num_tokens, handle.num_topk))
+    if out is None:
+        out = alloc_dispatch_outputs(handle, H, fp8, want_meta, want_send_meta, device=x.device)
+    cap = out["recv_x"].shape[0]
+    s = _DispatchOut(
+        recv_x=out["recv_x"].data_ptr(),
+        recv_x_scales=out["recv_x_scales"].data_ptr() if out.get("recv_x_scales") is not None else None,
+        recv_src_idx=out["recv_src_idx"].data_ptr() if out.get("recv_src_idx") is not None else None,
+        recv_topk_weights=out["recv_topk_weights"].data_ptr() if out.get("recv_topk_weights") is not None else None,
+        recv_capacity=cap,
+        send_x=out["send_x"].data_ptr() if out.get("send_x") is not None else None,
+        send_x_scales=out["send_x_scales"].data_ptr() if out.get("send_x_scales") is not None else None,
+        send_src_idx=out["send_src_idx"].data_ptr() if out.get("send_src_idx") is not None else None,
+        send_topk_idx=out["send_topk_idx"].data_ptr() if out.get("send_topk_idx") is not None else None,
+        send_topk_weights=out["send_topk_weights"].data_ptr() if out.get("send_topk_weights") is not None else None)
+    _check(_lib.ep_dispatch(handle.ptr, _ptr(x), H, _ptr(topk_weights),
+                            EP_DTYPE_FP8_E4M3 if fp8 else EP_DTYPE_BF16, int(bool(do_expand)),
+                            int(bool(do_zero_padding)), ctypes.byref(s), _stream(stream)), "ep_dispatch")
+    return out
+
+
+def ep_combine(handle: Handle, y, topk_weights=None, bias=None, out=None, stream=None):
+    """Combine expert outputs `y` (bf16 [>= recv_capacity, H]) back to token order.  Returns out [T, H] bf16."""
+    _need(y, torch.bfloat16, "y")
+    if y.dim() != 2:
+        raise ValueError("y must be [rows, hidden]")
+    H = y.shape[1]
+    T = handle.num_tokens
+    if topk_weights is not None:
+        _need(topk_weights, torch.float32, "topk_weights", shape=(T, handle.num_topk))
+    if bias is not None:
+        _need(bias, torch.bfloat16, "bias", shape=(T, H))
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    else:
+        _need(out, torch.bfloat16, "out", shape=(T, H))
+    _check(_lib.ep_combine(handle.ptr, _ptr(y), H, y.shape[0], _ptr(topk_weights), _ptr(bias), _ptr(out),
+                           _stream(stream)), "ep_combine")
+    return out
+
+
+def ep_handle_free(handle: Handle):
+    handle.free()
+
+
+__all__ = ["ep_get_layout", "ep_dispatch", "ep_combine", "ep_handle_free", "ep_recv_capacity",
+           "ep_layout_workspace_bytes", "alloc_dispatch_outputs", "Handle", "EPError", "LIB_PATH",
+           "hip_runtimes_loaded"]

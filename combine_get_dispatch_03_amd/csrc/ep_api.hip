@@ -1,0 +1,234 @@
+// ep_api.hip -- the C ABI of include/ep.h: argument validation, workspace carve-up, handle lifetime and the
+// kernel launches.  Validation runs entirely on the host before anything is enqueued; nothing here
+// allocates device memory or synchronises.
+#include <cstdarg>
+#include <cstdio>
+#include <new>
+
+#include "ep_internal.hpp"
+
+namespace ep {
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+ep_status_t fail(ep_status_t s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+ep_status_t hip_fail(hipError_t e, const char* what) {
+    return fail(EP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shared shape checks of ep_get_layout / ep_layout_workspace_bytes / ep_recv_capacity.
+const char* check_shape(int T, int K, int E, int R, int rank, int A) {
+    if (T < 0) return "num_tokens must be >= 0";
+    if (K < 1 || K > kMaxTopk) return "num_topk must be in [1, 32]";
+    if (E < 1 || E > kMaxExperts) return "num_experts must be in [1, 1024]";
+    if (R < 1 || R > kMaxRanks) return "num_ranks must be in [1, 64]";
+    if (E % R != 0) return "num_experts must be a multiple of num_ranks";
+    if (rank < 0 || rank >= R) return "rank must be in [0, num_ranks)";
+    if (A < 1 || A > kMaxAlignment) return "expert_alignment must be in [1, 65536]";
+    const int64_t cap = (int64_t)T * K + (int64_t)(E / R) * (A - 1);
+    if (cap > INT32_MAX) return "receive capacity exceeds int32 rows";
+    return nullptr;
+}
+
+const Handle* check_handle(ep_handle_t h) {
+    const Handle* hd = reinterpret_cast<const Handle*>(h);
+    if (hd == nullptr || hd->magic != kHandleMagic) return nullptr;
+    return hd;
+}
+
+}  // namespace
+
+Workspace carve_workspace(void* base, int T, int K, int E, int R) {
+    const int ntiles = (T + kLayoutTileTokens - 1) / kLayoutTileTokens;
+    const int El = E / R;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + bytes, 256);
+        return o;
+    };
+    const size_t o_hist = take(sizeof(int32_t) * (size_t)ntiles * E);
+    const size_t o_rank = take(sizeof(int32_t) * (size_t)ntiles * R);
+    const size_t o_inv = take(sizeof(int32_t) * (size_t)ntiles);
+    const size_t o_slot = take(sizeof(int32_t) * (size_t)T * K);
+    const size_t o_send = take(R > 1 ? sizeof(int32_t) * (size_t)T * R : 0);
+    const size_t o_cnt = take(sizeof(int32_t) * (size_t)El);
+    const size_t o_psum = take(sizeof(int32_t) * (size_t)(El + 1));
+    Workspace w;
+    char* b = static_cast<char*>(base);
+    auto at = [&](size_t o) { return b ? reinterpret_cast<int32_t*>(b + o) : nullptr; };
+    w.tile_hist = at(o_hist);
+    w.tile_rank = at(o_rank);
+    w.tile_inv = at(o_inv);
+    w.slot = at(o_slot);
+    w.send_slot = R > 1 ? at(o_send) : nullptr;
+    w.cnt_local = at(o_cnt);
+    w.psum = at(o_psum);
+    w.bytes = off;
+    return w;
+}
+
+}  // namespace ep
+
+using namespace ep;
+
+extern "C" {
+
+int64_t ep_recv_capacity(int num_tokens, int num_topk, int num_local_experts, int expert_alignment) {
+    if (num_tokens < 0 || num_topk < 1 || num_topk > kMaxTopk || num_local_experts < 1 ||
+        num_local_experts > kMaxExperts || expert_alignment < 1 || expert_alignment > kMaxAlignment)
+        return -1;
+    const int64_t cap = (int64_t)num_tokens * num_topk + (int64_t)num_local_experts * (expert_alignment - 1);
+    return cap > INT32_MAX ? -1 : cap;
+}
+
+size_t ep_layout_workspace_bytes(int num_tokens, int num_topk, int num_experts, int num_ranks) {
+    if (check_shape(num_tokens, num_topk, num_experts, num_ranks, 0, 1) != nullptr) return 0;
+    return carve_workspace(nullptr, num_tokens, num_topk, num_experts, num_ranks).bytes;
+}
+
+const char* ep_status_string(ep_status_t s) {
+    switch (s) {
+        case EP_OK: return "ok";
+        case EP_ERR_INVALID_ARG: return "invalid argument";
+        case EP_ERR_UNSUPPORTED: return "unsupported mode";
+        case EP_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+const char* ep_last_error(void) { return g_last_error; }
+
+ep_status_t ep_get_layout(const int64_t* topk_idx, int num_tokens, int num_topk, int num_experts, int num_ranks,
+                          int rank, int expert_alignment, void* workspace, size_t workspace_bytes,
+                          int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert, uint8_t* is_token_in_rank,
+                          int32_t* psum_num_recv_tokens_per_expert, int32_t* num_invalid_topk,
+                          ep_handle_t* handle_out, void* stream) {
+    g_last_error[0] = '\0';
+    if (handle_out == nullptr) return fail(EP_ERR_INVALID_ARG, "handle_out is NULL");
+    if (const char* why = check_shape(num_tokens, num_topk, num_experts, num_ranks, rank, expert_alignment))
+        return fail(EP_ERR_INVALID_ARG, "%s", why);
+    if (num_tokens > 0 && topk_idx == nullptr) return fail(EP_ERR_INVALID_ARG, "topk_idx is NULL");
+    if (workspace == nullptr) return fail(EP_ERR_INVALID_ARG, "workspace is NULL");
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(EP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    const Workspace ws = carve_workspace(workspace, num_tokens, num_topk, num_experts, num_ranks);
+    if (workspace_bytes < ws.bytes)
+        return fail(EP_ERR_INVALID_ARG, "workspace_bytes %zu < required %zu", workspace_bytes, ws.bytes);
+
+    Handle* h = new (std::nothrow) Handle;
+    if (h == nullptr) return fail(EP_ERR_INVALID_ARG, "out of host memory for the handle");
+    h->magic = kHandleMagic;
+    h->T = num_tokens;
+    h->K = num_topk;
+    h->E = num_experts;
+    h->R = num_ranks;
+    h->rank = rank;
+    h->A = expert_alignment;
+    h->El = num_experts / num_ranks;
+    h->lo = rank * h->El;
+    h->ntiles = (num_tokens + kLayoutTileTokens - 1) / kLayoutTileTokens;
+    h->cap = (int64_t)num_tokens * num_topk + (int64_t)h->El * (expert_alignment - 1);
+    h->topk_idx = topk_idx;
+    h->ws = ws;
+
+    const LayoutOutputs out{num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank,
+                            psum_num_recv_tokens_per_expert, num_invalid_topk};
+    const hipError_t err = launch_layout(*h, out, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) {
+        h->magic = 0;
+        delete h;
+        return hip_fail(err, "layout launch");
+    }
+    *handle_out = reinterpret_cast<ep_handle_t>(h);
+    return EP_OK;
+}
+
+ep_status_t ep_dispatch(ep_handle_t handle, const void* x, int hidden, const float* topk_weights,
+                        ep_dtype_t recv_dtype, int do_expand, int do_zero_padding, const ep_dispatch_out_t* out,
+                        void* stream) {
+    g_last_error[0] = '\0';
+    const Handle* h = check_handle(handle);
+    if (h == nullptr) return fail(EP_ERR_INVALID_ARG, "invalid handle");
+    if (do_expand == 0) return fail(EP_ERR_UNSUPPORTED, "do_expand = 0 (token-major receive layout) is not implemented");
+    if (recv_dtype != EP_DTYPE_BF16 && recv_dtype != EP_DTYPE_FP8_E4M3)
+        return fail(EP_ERR_INVALID_ARG, "recv_dtype must be EP_DTYPE_BF16 or EP_DTYPE_FP8_E4M3");
+    const bool fp8 = recv_dtype == EP_DTYPE_FP8_E4M3;
+    if (hidden < 8 || hidden > kMaxHidden || hidden % 8 != 0)
+        return fail(EP_ERR_INVALID_ARG, "hidden must be a multiple of 8 in [8, 32768]");
+    if (fp8 && hidden % 128 != 0) return fail(EP_ERR_INVALID_ARG, "FP8 dispatch needs hidden % 128 == 0");
+    if (out == nullptr) return fail(EP_ERR_INVALID_ARG, "out is NULL");
+    if (h->T > 0) {
+        if (x == nullptr || !aligned16(x)) return fail(EP_ERR_INVALID_ARG, "x must be non-NULL and 16-byte aligned");
+        if (out->recv_x == nullptr || !aligned16(out->recv_x))
+            return fail(EP_ERR_INVALID_ARG, "recv_x must be non-NULL and 16-byte aligned");
+        if (out->recv_capacity < h->cap)
+            return fail(EP_ERR_INVALID_ARG, "recv_capacity %lld < required %lld", (long long)out->recv_capacity,
+                        (long long)h->cap);
+        if (fp8 && out->recv_x_scales == nullptr) return fail(EP_ERR_INVALID_ARG, "FP8 needs recv_x_scales");
+        if (h->R > 1) {
+            if (out->send_x == nullptr || !aligned16(out->send_x))
+                return fail(EP_ERR_INVALID_ARG, "num_ranks > 1 needs a 16-byte aligned send_x");
+            if (fp8 && out->send_x_scales == nullptr)
+                return fail(EP_ERR_INVALID_ARG, "num_ranks > 1 with FP8 needs send_x_scales");
+        }
+    }
+    DispatchArgs a;
+    a.x = x;
+    a.topk_weights = topk_weights;
+    a.hidden = hidden;
+    a.fp8 = fp8;
+    a.zero_pad = do_zero_padding != 0;
+    a.out = *out;
+    const hipError_t err = launch_dispatch(*h, a, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return hip_fail(err, "dispatch launch");
+    return EP_OK;
+}
+
+ep_status_t ep_combine(ep_handle_t handle, const void* y, int hidden, int64_t y_rows, const float* topk_weights,
+                       const void* bias, void* out, void* stream) {
+    g_last_error[0] = '\0';
+    const Handle* h = check_handle(handle);
+    if (h == nullptr) return fail(EP_ERR_INVALID_ARG, "invalid handle");
+    if (hidden < 8 || hidden > kMaxHidden || hidden % 8 != 0)
+        return fail(EP_ERR_INVALID_ARG, "hidden must be a multiple of 8 in [8, 32768]");
+    if (h->T > 0) {
+        if (y == nullptr || !aligned16(y)) return fail(EP_ERR_INVALID_ARG, "y must be non-NULL and 16-byte aligned");
+        if (y_rows < h->cap)
+            return fail(EP_ERR_INVALID_ARG, "y_rows %lld < required %lld", (long long)y_rows, (long long)h->cap);
+        if (out == nullptr || !aligned16(out)) return fail(EP_ERR_INVALID_ARG, "out must be non-NULL and 16-byte aligned");
+        if (bias != nullptr && !aligned16(bias)) return fail(EP_ERR_INVALID_ARG, "bias must be 16-byte aligned");
+    }
+    CombineArgs a;
+    a.y = y;
+    a.topk_weights = topk_weights;
+    a.bias = bias;
+    a.out = out;
+    a.hidden = hidden;
+    const hipError_t err = launch_combine(*h, a, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return hip_fail(err, "combine launch");
+    return EP_OK;
+}
+
+ep_status_t ep_handle_free(ep_handle_t handle) {
+    Handle* h = reinterpret_cast<Handle*>(handle);
+    if (h == nullptr) return EP_OK;
+    if (h->magic != kHandleMagic) return fail(EP_ERR_INVALID_ARG, "invalid handle");
+    h->magic = 0;
+    delete h;
+    return EP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,129 @@
+// ep_combine.hip -- top-k reduction back to token order on gfx950 ([DeepEP->MegaMoE] §2.3 and §2.5: per
+// token, element-wise accumulation of the top-k expert output rows; §3.2 phase 6: accumulate then store the
+// token's output row; [MoE-comm] §一: the shared-expert output enters as bias).
+//
+// One wave per token.  The token's valid (slot, weight) pairs are compacted into lanes 0..nv-1 and read
+// back as scalars, so every gather is a 64-lane x 16-byte row segment at a uniform base.  Each pass covers
+// two 1024-byte segments of the output row and issues up to 16 gathers before the first FMA, so enough
+// bytes are in flight per wave.  fp32 accumulation in ascending k, one RNE rounding to bf16 at the end.
+#include "ep_device.hpp"
+#include "ep_internal.hpp"
+
+namespace ep {
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int kBatch = 8;       // gathers issued per k-batch and per segment
+
+struct Params {
+    const uint16_t* y;
+    const float* w;
+    const uint16_t* bias;
+    uint16_t* out;
+    const int32_t* slot;
+    int T, H, K;
+};
+
+__device__ __forceinline__ void fma8(float* acc, float wgt, u32x4 v) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        acc[2 * k] = fmaf(wgt, bf16lo(v[k]), acc[2 * k]);
+        acc[2 * k + 1] = fmaf(wgt, bf16hi(v[k]), acc[2 * k + 1]);
+    }
+}
+
+__device__ __forceinline__ void add8(float* acc, u32x4 v) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        acc[2 * k] += bf16lo(v[k]);
+        acc[2 * k + 1] += bf16hi(v[k]);
+    }
+}
+
+__device__ __forceinline__ u32x4 pack8(const float* acc) {
+    u32x4 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r[k] = pack_bf16x2(acc[2 * k], acc[2 * k + 1]);
+    return r;
+}
+
+__global__ __launch_bounds__(kBlock) void k_combine(Params p) {
+    __shared__ int cs_lds[kWavesPerBlock][kWave];
+    __shared__ float cw_lds[kWavesPerBlock][kWave];
+    const int lane = lane_id(), wv = threadIdx.x >> 6;
+    const int t = blockIdx.x * kWavesPerBlock + wv;
+    if (t >= p.T) return;
+
+    // compact the token's valid slots (ascending k) into lanes 0..nv-1
+    const int s = lane < p.K ? p.slot[(int64_t)t * p.K + lane] : -1;
+    const float wk = lane < p.K ? (p.w != nullptr ? p.w[(int64_t)t * p.K + lane] : 1.0f) : 0.0f;
+    const uint64_t vm = ballot(s >= 0);
+    const int nv = popc64(vm);
+    if (s >= 0) {
+        const int pos = popc64(vm & lanemask_lt());
+        cs_lds[wv][pos] = s;
+        cw_lds[wv][pos] = wk;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int cs = lane < nv ? cs_lds[wv][lane] : 0;
+    const float cw = lane < nv ? cw_lds[wv][lane] : 0.0f;
+
+    const int nchunk = p.H / 8;                                   // 16-byte chunks per row
+    const u32x4* bias = p.bias ? reinterpret_cast<const u32x4*>(p.bias + (int64_t)t * p.H) : nullptr;
+    u32x4* out = reinterpret_cast<u32x4*>(p.out + (int64_t)t * p.H);
+    for (int c0 = lane; c0 - lane < nchunk; c0 += 2 * kWave) {
+        const int c1 = c0 + kWave;
+        const bool a0 = c0 < nchunk, a1 = c1 < nchunk;
+        float acc0[8], acc1[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc0[k] = acc1[k] = 0.0f;
+        for (int kb = 0; kb < nv; kb += kBatch) {
+            u32x4 v0[kBatch], v1[kBatch];
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) {
+                if (kb + i < nv) {
+                    const u32x4* row = reinterpret_cast<const u32x4*>(p.y + (int64_t)readlane(cs, kb + i) * p.H);
+                    if (a0) v0[i] = ld_nt(row + c0);
+                    if (a1) v1[i] = ld_nt(row + c1);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) {
+                if (kb + i < nv) {
+                    const float wgt = readlane_f(cw, kb + i);
+                    if (a0) fma8(acc0, wgt, v0[i]);
+                    if (a1) fma8(acc1, wgt, v1[i]);
+                }
+            }
+        }
+        if (bias != nullptr) {
+            if (a0) add8(acc0, bias[c0]);
+            if (a1) add8(acc1, bias[c1]);
+        }
+        if (a0) st_nt(out + c0, pack8(acc0));
+        if (a1) st_nt(out + c1, pack8(acc1));
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const Handle& h, const CombineArgs& a, hipStream_t stream) {
+    if (h.T == 0) return hipSuccess;
+    Params p;
+    p.y = static_cast<const uint16_t*>(a.y);
+    p.w = a.topk_weights;
+    p.bias = static_cast<const uint16_t*>(a.bias);
+    p.out = static_cast<uint16_t*>(a.out);
+    p.slot = h.ws.slot;
+    p.T = h.T;
+    p.H = a.hidden;
+    p.K = h.K;
+    const unsigned nblocks = (unsigned)((h.T + kWavesPerBlock - 1) / kWavesPerBlock);
+    hipLaunchKernelGGL(k_combine, dim3(nblocks), dim3(kBlock), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace ep

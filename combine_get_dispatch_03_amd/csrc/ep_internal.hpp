@@ -1,0 +1,78 @@
+// ep_internal.hpp -- host-side internals shared by the library's translation units: the handle, the
+// workspace carve-up and the kernel launchers.  Nothing here is part of the C ABI (include/ep.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "ep.h"
+
+namespace ep {
+
+constexpr uint32_t kHandleMagic = 0x45504831u;   // "EPH1"
+constexpr int kLayoutTileTokens = 256;           // tokens per layout tile (4 waves x 64 tokens)
+constexpr int kMaxTopk = 32;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxRanks = 64;
+constexpr int kMaxAlignment = 65536;
+constexpr int kMaxHidden = 32768;
+
+// Device arrays carved out of the caller's workspace.  All int32.
+struct Workspace {
+    int32_t* tile_hist;   // [ntiles, E]  per-tile expert counts
+    int32_t* tile_rank;   // [ntiles, R]  per-tile token-in-rank counts
+    int32_t* tile_inv;    // [ntiles]     per-tile invalid entries
+    int32_t* slot;        // [T, K]       expert-major row of each entry, -1 if not local
+    int32_t* send_slot;   // [T, R]       row in the send window of rank r, -1 if none (R > 1 only)
+    int32_t* cnt_local;   // [El]         routed entries of each local expert
+    int32_t* psum;        // [El + 1]     aligned exclusive row starts of the local experts
+    size_t bytes;         // total bytes used
+};
+
+// Offsets of the carve-up for the given sizes; with base == nullptr only `bytes` is meaningful.
+Workspace carve_workspace(void* base, int T, int K, int E, int R);
+
+struct Handle {
+    uint32_t magic;
+    int T, K, E, R, rank, A;
+    int El;        // local experts E / R
+    int lo;        // first local expert rank * El
+    int ntiles;    // ceil(T / kLayoutTileTokens)
+    int64_t cap;   // receive capacity in rows
+    const int64_t* topk_idx;
+    Workspace ws;
+};
+
+// ---- launchers (each enqueues on `stream` and returns hipGetLastError()) -----------------------------
+
+struct LayoutOutputs {
+    int32_t* num_tokens_per_rank;
+    int32_t* num_tokens_per_expert;
+    uint8_t* is_token_in_rank;
+    int32_t* psum;
+    int32_t* num_invalid;
+};
+hipError_t launch_layout(const Handle& h, const LayoutOutputs& out, hipStream_t stream);
+
+struct DispatchArgs {
+    const void* x;
+    const float* topk_weights;
+    int hidden;
+    bool fp8;
+    bool zero_pad;
+    ep_dispatch_out_t out;
+};
+hipError_t launch_dispatch(const Handle& h, const DispatchArgs& a, hipStream_t stream);
+
+struct CombineArgs {
+    const void* y;
+    const float* topk_weights;
+    const void* bias;
+    void* out;
+    int hidden;
+};
+hipError_t launch_combine(const Handle& h, const CombineArgs& a, hipStream_t stream);
+
+}  // namespace ep

@@ -1,0 +1,167 @@
+/*
+ * ep.h -- C ABI of the one-GPU MoE expert-parallel layout / dispatch / combine library (libep_mi355x.so).
+ *
+ * The library computes, on one GPU (gfx950, MI355X), the data-parallel share of DeepEP-style expert-parallel
+ * dispatch and combine:
+ *   ep_get_layout  routing table -> per-expert / per-rank counts, token-in-rank membership, aligned
+ *                  per-expert row starts, and the slot of every routed entry (kept in a handle);
+ *   ep_dispatch    permute token rows into an expert-major, alignment-padded receive buffer, optionally
+ *                  cast to FP8 e4m3 with per-128-channel fp32 scales, and pack per-destination send windows
+ *                  for experts owned by other ranks;
+ *   ep_combine     weighted top-k reduction of expert outputs back to token order in BF16, plus bias.
+ *
+ * Page names used in the citations:
+ *   [DeepEP->MegaMoE]  "从 DeepEP 到 Mega MoE：MoE Runtime 演进的三向验证分析" (backyes.github.io)
+ *   [DeepEP-hotdry]    DeepEP expert-parallel communication article (blog.hotdry.top)
+ *   [MoE-comm]         "MoE 为什么容易卡在通信上？" (locsic.com)
+ *   [flops-record]     inference-research record "deepep-expert-parallel-dispatch-combine" (phantomic12)
+ *   [repo-map]         "第 2 章 仓库地图与模块职责" (bowenzhou.top)
+ *
+ * Conventions for every call:
+ *   - Device pointers are plain device addresses (hipMalloc / torch CUDA tensors); host pointers are named.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the default stream).  No call allocates device
+ *     memory, copies to the host or synchronises: counts stay on the device, as with do_cpu_sync off
+ *     ([MoE-comm] §二; [flops-record]: capacity-sized outputs and a device psum for the grouped GEMM).
+ *   - Every argument is validated on the host before anything is enqueued.  On an error nothing is enqueued,
+ *     no output is touched, the call returns a non-zero status and ep_last_error() describes it.
+ *   - Memory is owned by the caller.  A buffer or handle must not be freed, resized or reused while an
+ *     operation using it is still pending on its stream ([MoE-comm] §二, buffer and handle reuse).
+ *   - Row-major layouts throughout.  x, y, out, bias, recv_x and send_x must be 16-byte aligned.
+ *
+ * Limits: 0 <= num_tokens; 1 <= num_topk <= 32; 1 <= num_experts <= 1024; 1 <= num_ranks <= 64 with
+ * num_experts % num_ranks == 0; 0 <= rank < num_ranks; 1 <= expert_alignment <= 65536; the receive capacity
+ * must fit in int32; hidden % 8 == 0, 8 <= hidden <= 32768, and hidden % 128 == 0 for FP8.
+ */
+#ifndef EP_MI355X_H
+#define EP_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ep_status {
+    EP_OK = 0,
+    EP_ERR_INVALID_ARG = 1,   /* an argument is out of range, misaligned, NULL where required, or a size is short */
+    EP_ERR_UNSUPPORTED = 2,   /* a mode this version does not implement (do_expand = 0)                           */
+    EP_ERR_HIP = 3            /* a HIP launch failed; the stream state is whatever HIP reports                    */
+} ep_status_t;
+
+typedef enum ep_dtype {
+    EP_DTYPE_BF16 = 0,        /* bf16 rows, bit copies of x                                                        */
+    EP_DTYPE_FP8_E4M3 = 1     /* OCP e4m3fn rows + one fp32 scale per 128 channels                                 */
+} ep_dtype_t;
+
+typedef struct ep_handle* ep_handle_t;   /* opaque host object created by ep_get_layout */
+
+/* Rows the expert-major receive buffers (recv_x and friends, and y of ep_combine) must have:
+ * num_tokens * num_topk + num_local_experts * (expert_alignment - 1), the worst case of padding every local
+ * expert up to a multiple of the alignment ([flops-record]: outputs sized to configured capacity; [MoE-comm]
+ * §一: equal, fixed capacity).  Host only.  Returns -1 for arguments outside the limits. */
+int64_t ep_recv_capacity(int num_tokens, int num_topk, int num_local_experts, int expert_alignment);
+
+/* Bytes of device workspace ep_get_layout needs for these sizes.  Host only.  Returns 0 for arguments
+ * outside the limits (a valid call always needs more than 0 bytes). */
+size_t ep_layout_workspace_bytes(int num_tokens, int num_topk, int num_experts, int num_ranks);
+
+/* Static description of a status code, and a thread-local description of the last failure in this thread. */
+const char* ep_status_string(ep_status_t status);
+const char* ep_last_error(void);
+
+/*
+ * ep_get_layout -- layout of one rank's routing table ([repo-map] §2.1: layout.cu reduces top-k indices to
+ * rank counts, expert counts and token-in-rank membership; [DeepEP->MegaMoE] §2.2: per-expert counts and
+ * their prefix sum; §2.4: the prefix sum is the start cursor of each expert's rows).
+ *
+ *   topk_idx             device, int64 [num_tokens, num_topk]: expert of each routed entry; -1 = unused.
+ *                        Entries < -1 or >= num_experts are dropped and counted in num_invalid_topk.
+ *                        The handle keeps this pointer: keep the array alive and unchanged while the
+ *                        handle is used.
+ *   num_experts          global expert count E; expert e belongs to rank e / (E / num_ranks).
+ *   num_ranks, rank      EP group size and this rank.
+ *   expert_alignment     A: every local expert's segment starts at and spans a multiple of A rows
+ *                        ([MoE-comm] §一 expert_alignment; §三 padding).  An empty expert spans 0 rows.
+ *   workspace            device scratch of at least ep_layout_workspace_bytes(...) bytes, 256-byte aligned,
+ *                        owned by the caller; the handle keeps the slot map in it, so it must outlive every
+ *                        dispatch/combine that uses the handle.  No initial contents are required.
+ *   num_tokens_per_rank  device int32 [num_ranks] out, nullable: tokens with >= 1 expert on rank r
+ *                        (a token counts once per rank).
+ *   num_tokens_per_expert device int32 [num_experts] out, nullable: routed entries per expert.
+ *   is_token_in_rank     device uint8 [num_tokens, num_ranks] out, nullable: 0/1 membership.
+ *   psum_num_recv_tokens_per_expert  device int32 [num_experts / num_ranks + 1] out, nullable: aligned
+ *                        exclusive row starts of the local experts, psum[0] = 0; local expert j owns rows
+ *                        [psum[j], psum[j+1]) of which the first num_tokens_per_expert[rank*El + j] are valid.
+ *   num_invalid_topk     device int32 [1] out, nullable.
+ *   handle_out           host out: a new handle (free with ep_handle_free).  Rows of one expert are ordered
+ *                        by ascending flat entry index t * num_topk + k.
+ */
+ep_status_t ep_get_layout(const int64_t* topk_idx, int num_tokens, int num_topk, int num_experts, int num_ranks,
+                          int rank, int expert_alignment, void* workspace, size_t workspace_bytes,
+                          int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert, uint8_t* is_token_in_rank,
+                          int32_t* psum_num_recv_tokens_per_expert, int32_t* num_invalid_topk,
+                          ep_handle_t* handle_out, void* stream);
+
+/* Outputs of ep_dispatch.  All device memory owned by the caller; NULL = not requested where allowed. */
+typedef struct ep_dispatch_out {
+    void*    recv_x;            /* required: [recv_capacity, hidden] e4m3 bytes (FP8) or bf16 (BF16)            */
+    float*   recv_x_scales;     /* FP8: required, [recv_capacity, hidden / 128] fp32 scales; BF16: ignored       */
+    int32_t* recv_src_idx;      /* nullable: [recv_capacity] source token of each row; -1 on padding rows        */
+    float*   recv_topk_weights; /* nullable: [recv_capacity] routing weight of each row; 0 on padding rows      */
+    int64_t  recv_capacity;     /* rows allocated in the recv arrays; must be >= ep_recv_capacity(...)          */
+    void*    send_x;            /* num_ranks > 1: required, [num_ranks, num_tokens, hidden] rows (window per rank)*/
+    float*   send_x_scales;     /* num_ranks > 1 and FP8: required, [num_ranks, num_tokens, hidden / 128]        */
+    int32_t* send_src_idx;      /* nullable: [num_ranks, num_tokens] source token of each window row            */
+    int64_t* send_topk_idx;     /* nullable: [num_ranks, num_tokens, num_topk] expert id local to the window's
+                                   rank, -1 where that rank does not own the entry's expert                       */
+    float*   send_topk_weights; /* nullable: [num_ranks, num_tokens, num_topk] routing weights                   */
+} ep_dispatch_out_t;
+
+/*
+ * ep_dispatch -- expert-major dispatch of this rank's tokens ([MoE-comm] §一 dispatch arguments;
+ * [DeepEP->MegaMoE] §2.2 dispatch kernel: read the token row, store to the send buffer; §2.4 copy epilogue:
+ * place rows expert-major; [DeepEP-hotdry] key techniques: FP8 dispatch, BF16 combine).
+ *
+ *   handle          from ep_get_layout; may be reused for any number of dispatches with new x ("cached" use).
+ *   x               device bf16 [num_tokens, hidden], read once per token.
+ *   topk_weights    device fp32 [num_tokens, num_topk], nullable (weights of 1); copied into
+ *                   recv_topk_weights and send_topk_weights only.
+ *   recv_dtype      EP_DTYPE_BF16 or EP_DTYPE_FP8_E4M3.  FP8: per token and 128-channel group,
+ *                   a = max(max|x|, 1e-4), scale = a / 448, q = e4m3_rne_saturating(x * (448 / a)).
+ *   do_expand       must be 1 (expert-major rows, one per routed entry); 0 returns EP_ERR_UNSUPPORTED.
+ *   do_zero_padding 1: padding rows [psum[j] + count_j, psum[j+1]) get zero bytes and zero scales;
+ *                   0: their data bytes and scales are left untouched.  Their recv_src_idx / weights are
+ *                   written (-1 / 0) either way.  Rows >= psum[El] are never written.
+ *   Send windows (num_ranks > 1): for every other rank r, row j of window r holds the j-th token (ascending)
+ *   with an expert on r: the same bytes and scales as the token's local rows.  Rows past the window's count
+ *   are untouched; window `rank` is untouched.
+ */
+ep_status_t ep_dispatch(ep_handle_t handle, const void* x, int hidden, const float* topk_weights,
+                        ep_dtype_t recv_dtype, int do_expand, int do_zero_padding, const ep_dispatch_out_t* out,
+                        void* stream);
+
+/*
+ * ep_combine -- top-k reduction back to token order ([DeepEP->MegaMoE] §2.3 and §2.5: element-wise
+ * accumulation of the top-k expert outputs of a token; [MoE-comm] §一: the shared expert's output joins
+ * as bias).
+ *
+ *   y             device bf16 [y_rows, hidden], same row layout as recv_x of the handle's dispatch;
+ *                 y_rows must be >= ep_recv_capacity(...).  Padding rows are never read.
+ *   topk_weights  device fp32 [num_tokens, num_topk], nullable.  Non-NULL: out = sum_k w[t,k] * y[slot];
+ *                 NULL: out = sum_k y[slot] (rows already weighted by the expert computation).
+ *   bias          device bf16 [num_tokens, hidden], nullable; added after the expert terms.
+ *   out           device bf16 [num_tokens, hidden]; every row is written.  A token with no local slot
+ *                 gets its bias row (or zeros).
+ *   Accumulation is fp32 in ascending k, then one round-to-nearest-even to bf16.
+ */
+ep_status_t ep_combine(ep_handle_t handle, const void* y, int hidden, int64_t y_rows, const float* topk_weights,
+                       const void* bias, void* out, void* stream);
+
+/* Free the host object of a handle (never blocks, never touches device memory).  NULL is allowed. */
+ep_status_t ep_handle_free(ep_handle_t handle);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EP_MI355X_H */
