@@ -3,8 +3,10 @@
 A step is one pass of the whole path over one batch of the prefill workload: ep_get_layout, then FP8 dispatch
 with zero padding, then the weighted BF16 combine (4096 tokens, hidden 7168, 256 experts in 8 groups with
 group-limited top-4-group / top-8 routing, alignment 128).  Inputs and expert outputs are resident in HBM
-before timing starts.  W untimed warm-up steps, then exactly K timed steps bracketed by device syncs; HIP
-events on the launch stream give each kernel's average duration over the timed steps.
+before timing starts.  One step is captured into a HIP graph; W untimed warm-up replays, then exactly K timed
+replays bracketed by device syncs (the graph keeps host launch overhead out of the GPU's way).  Each
+call's average duration comes from HIP events on the launch stream around K back-to-back launches of that
+call, enqueued by the host ahead of the GPU.
 
 Prints one JSON line.  `value` is the step's effective HBM throughput: the algorithmic bytes of layout +
 dispatch + combine per step divided by the measured step time.  Algorithmic bytes are what the method must
@@ -13,7 +15,7 @@ the expert rows gathered once by combine and the output written once (the byte m
 bytes_model()).  Two extra objects: `roofline` for the dominant kernel and `cpu_baseline` (the oracle timed
 on the host).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--flush-samples 50] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--flush-samples 50] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -41,8 +43,8 @@ KERNEL_SOURCES = {
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--flush-samples", type=int, default=50,
                     help="per-kernel samples with a cache flush before each (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -90,7 +92,8 @@ def load_traffic(kernel):
 
 
 def cpu_baseline(inp, y_bits, cfg):
-    """The oracle as it stands (single thread, plain C) on the full workload; median of 3 runs."""
+    """The oracle as it stands (single thread, plain C) on the full workload, repeated until about 10 s of
+    CPU time have been spent (at least 3 runs); the median run is reported."""
     import numpy as np
 
     import oracle as O
@@ -101,7 +104,7 @@ def cpu_baseline(inp, y_bits, cfg):
     x = W.bf16_bits(inp["x"])
     bias = W.bf16_bits(inp["bias"]) if inp["bias"] is not None else None
     times = []
-    for _ in range(3):
+    while len(times) < 3 or sum(times) < 10.0:
         t0 = time.perf_counter()
         lay = O.layout(idx, cfg.num_experts, cfg.num_ranks, cfg.rank, cfg.expert_alignment)
         O.dispatch(x, idx, w, lay, cfg.num_experts, cfg.num_ranks, cfg.rank, cfg.expert_alignment, fp8=cfg.fp8,
@@ -117,8 +120,8 @@ def cpu_baseline(inp, y_bits, cfg):
     total = bm["layout"] + bm["dispatch"] + bm["combine"]
     med = float(np.median(times))
     return dict(value=round(total / med / 1e9, 3), unit="GB/s", cores=1, kind="oracle",
-                sample="full %s workload (layout + FP8 dispatch + combine), median of 3 runs, %.2f s each"
-                       % (cfg.name, med))
+                sample="full %s workload (layout + FP8 dispatch + combine), median of %d runs, %.2f s each"
+                       % (cfg.name, len(times), med))
 
 
 def main():
@@ -145,7 +148,7 @@ def main():
 
     # persistent buffers (allocated once, outside the timed region)
     T, K, E, R = cfg.num_tokens, cfg.num_topk, cfg.num_experts, cfg.num_ranks
-    ws = torch.empty(ep.ep_layout_workspace_bytes(T, K, E, R), dtype=torch.uint8, device=dev)
+    ws = torch.empty(ep.ep_layout_workspace_bytes(T, K, E, R, cfg.expert_alignment), dtype=torch.uint8, device=dev)
     lay_out = dict(num_tokens_per_rank=torch.empty(R, dtype=torch.int32, device=dev),
                    num_tokens_per_expert=torch.empty(E, dtype=torch.int32, device=dev),
                    is_token_in_rank=torch.empty((T, R), dtype=torch.uint8, device=dev),
@@ -166,9 +169,8 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    stream = torch.cuda.current_stream()
-
     def step(ev=None):
+        stream = torch.cuda.current_stream()
         if ev is not None:
             ev[0].record(stream)
         h, _ = ep.ep_get_layout(idx, E, R, cfg.rank, cfg.expert_alignment, workspace=ws, outputs=lay_out)
@@ -182,24 +184,50 @@ def main():
             ev[3].record(stream)
         return h
 
-    for _ in range(args.warmup):
+    # eager warm-up, then capture one step (layout -> dispatch -> combine) into a HIP graph
+    for _ in range(2):
         step()
     torch.cuda.synchronize()
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        graph_handle = step()
     torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps (graph replays), bracketed by device syncs
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
+    for _ in range(args.steps):
+        graph.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    k_ms = {"layout": [], "dispatch": [], "combine": []}
-    for e in evs:
-        k_ms["layout"].append(e[0].elapsed_time(e[1]))
-        k_ms["dispatch"].append(e[1].elapsed_time(e[2]))
-        k_ms["combine"].append(e[2].elapsed_time(e[3]))
-    avg = {k: float(np.mean(v)) for k, v in k_ms.items()}
+
+    # per-kernel durations: HIP events on the launch stream bracketing N back-to-back launches of one call
+    # (an event marker between kernels costs several microseconds of GPU time, so each kernel is timed in a run
+    # of its own launches and the marker cost is divided by N); the calls are the same as inside the step
+    def timed(fn, n):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(2.4e9 * 0.02))   # ~20 ms of GPU spin while the host enqueues the launches
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    hk, _ = ep.ep_get_layout(idx, E, R, cfg.rank, cfg.expert_alignment, workspace=ws, outputs=lay_out)
+    avg = {
+        "layout": timed(lambda: ep.ep_get_layout(idx, E, R, cfg.rank, cfg.expert_alignment, workspace=ws,
+                                                 outputs=lay_out), args.steps),
+        "dispatch": timed(lambda: ep.ep_dispatch(hk, x, w, fp8=cfg.fp8, do_zero_padding=cfg.zero_padding,
+                                                 out=dout), args.steps),
+        "combine": timed(lambda: ep.ep_combine(hk, y, w, bias, out=out), args.steps),
+    }
 
     # per-kernel samples with a cache flush before each (10 warm-up + N samples, the pages' method)
     flushed = None
@@ -212,7 +240,7 @@ def main():
             step(ev)
             torch.cuda.synchronize()
             if i >= 10:
-                fl["layout"].append(ev[0].elapsed_time(ev[1]))
+                fl["layout"].append(ev[0].elapsed_time(ev[1]))  # includes event-marker overhead
                 fl["dispatch"].append(ev[1].elapsed_time(ev[2]))
                 fl["combine"].append(ev[2].elapsed_time(ev[3]))
         del junk
@@ -273,6 +301,8 @@ def main():
                     valid_rows=V, pad_rows=counts["P"], A_pad=round(int(psum[-1]) / max(V, 1), 4),
                     data_dtypes="x bf16 -> recv e4m3 + fp32 scales; y bf16 -> out bf16 (fp32 accumulate)"),
         tokens_per_s=round(T / (ms_per_step * 1e-3), 1),
+        timing="step: HIP graph replay of layout (2 kernels) + dispatch + combine; per call: events around K "
+               "back-to-back launches",
         kernels=kern,
         roofline=roofline,
         cpu_baseline=cpu,

@@ -50,7 +50,7 @@ def _load_library():
     lib.ep_recv_capacity.restype = I64
     lib.ep_recv_capacity.argtypes = [I, I, I, I]
     lib.ep_layout_workspace_bytes.restype = SZ
-    lib.ep_layout_workspace_bytes.argtypes = [I, I, I, I]
+    lib.ep_layout_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.ep_status_string.restype = ctypes.c_char_p
     lib.ep_status_string.argtypes = [I]
     lib.ep_last_error.restype = ctypes.c_char_p
@@ -112,8 +112,8 @@ def ep_recv_capacity(num_tokens, num_topk, num_local_experts, expert_alignment) 
     return int(_lib.ep_recv_capacity(num_tokens, num_topk, num_local_experts, expert_alignment))
 
 
-def ep_layout_workspace_bytes(num_tokens, num_topk, num_experts, num_ranks=1) -> int:
-    return int(_lib.ep_layout_workspace_bytes(num_tokens, num_topk, num_experts, num_ranks))
+def ep_layout_workspace_bytes(num_tokens, num_topk, num_experts, num_ranks=1, expert_alignment=1) -> int:
+    return int(_lib.ep_layout_workspace_bytes(num_tokens, num_topk, num_experts, num_ranks, expert_alignment))
 
 
 class Handle:
@@ -157,10 +157,10 @@ def ep_get_layout(topk_idx, num_experts, num_ranks=1, rank=0, expert_alignment=1
         raise ValueError("topk_idx must be [num_tokens, num_topk]")
     T, K = topk_idx.shape
     dev = topk_idx.device
-    nbytes = ep_layout_workspace_bytes(T, K, num_experts, num_ranks)
+    nbytes = ep_layout_workspace_bytes(T, K, num_experts, num_ranks, expert_alignment)
     if nbytes == 0:
-        raise EPError("ep_layout_workspace_bytes rejected the sizes (T=%d K=%d E=%d R=%d)"
-                      % (T, K, num_experts, num_ranks))
+        raise EPError("ep_layout_workspace_bytes rejected the sizes (T=%d K=%d E=%d R=%d A=%d)"
+                      % (T, K, num_experts, num_ranks, expert_alignment))
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     El = num_experts // max(num_ranks, 1)

@@ -50,7 +50,7 @@ const Handle* check_handle(ep_handle_t h) {
 
 }  // namespace
 
-Workspace carve_workspace(void* base, int T, int K, int E, int R) {
+Workspace carve_workspace(void* base, int T, int K, int E, int R, int A) {
     const int ntiles = (T + kLayoutTileTokens - 1) / kLayoutTileTokens;
     const int El = E / R;
     size_t off = 0;
@@ -59,23 +59,23 @@ Workspace carve_workspace(void* base, int T, int K, int E, int R) {
         off = align_up(off + bytes, 256);
         return o;
     };
-    const size_t o_hist = take(sizeof(int32_t) * (size_t)ntiles * E);
-    const size_t o_rank = take(sizeof(int32_t) * (size_t)ntiles * R);
-    const size_t o_inv = take(sizeof(int32_t) * (size_t)ntiles);
+    const size_t o_hist = take(sizeof(int32_t) * (size_t)ntiles * (size_t)(E + R + 1));
     const size_t o_slot = take(sizeof(int32_t) * (size_t)T * K);
     const size_t o_send = take(R > 1 ? sizeof(int32_t) * (size_t)T * R : 0);
     const size_t o_cnt = take(sizeof(int32_t) * (size_t)El);
     const size_t o_psum = take(sizeof(int32_t) * (size_t)(El + 1));
+    const size_t o_pad = take(sizeof(int32_t) * (size_t)El * (size_t)(A - 1));
+    const size_t o_padn = take(sizeof(int32_t));
     Workspace w;
     char* b = static_cast<char*>(base);
     auto at = [&](size_t o) { return b ? reinterpret_cast<int32_t*>(b + o) : nullptr; };
     w.tile_hist = at(o_hist);
-    w.tile_rank = at(o_rank);
-    w.tile_inv = at(o_inv);
     w.slot = at(o_slot);
     w.send_slot = R > 1 ? at(o_send) : nullptr;
     w.cnt_local = at(o_cnt);
     w.psum = at(o_psum);
+    w.pad_rows = A > 1 ? at(o_pad) : nullptr;
+    w.pad_total = at(o_padn);
     w.bytes = off;
     return w;
 }
@@ -94,9 +94,9 @@ int64_t ep_recv_capacity(int num_tokens, int num_topk, int num_local_experts, in
     return cap > INT32_MAX ? -1 : cap;
 }
 
-size_t ep_layout_workspace_bytes(int num_tokens, int num_topk, int num_experts, int num_ranks) {
-    if (check_shape(num_tokens, num_topk, num_experts, num_ranks, 0, 1) != nullptr) return 0;
-    return carve_workspace(nullptr, num_tokens, num_topk, num_experts, num_ranks).bytes;
+size_t ep_layout_workspace_bytes(int num_tokens, int num_topk, int num_experts, int num_ranks, int expert_alignment) {
+    if (check_shape(num_tokens, num_topk, num_experts, num_ranks, 0, expert_alignment) != nullptr) return 0;
+    return carve_workspace(nullptr, num_tokens, num_topk, num_experts, num_ranks, expert_alignment).bytes;
 }
 
 const char* ep_status_string(ep_status_t s) {
@@ -124,7 +124,7 @@ ep_status_t ep_get_layout(const int64_t* topk_idx, int num_tokens, int num_topk,
     if (workspace == nullptr) return fail(EP_ERR_INVALID_ARG, "workspace is NULL");
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return fail(EP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-    const Workspace ws = carve_workspace(workspace, num_tokens, num_topk, num_experts, num_ranks);
+    const Workspace ws = carve_workspace(workspace, num_tokens, num_topk, num_experts, num_ranks, expert_alignment);
     if (workspace_bytes < ws.bytes)
         return fail(EP_ERR_INVALID_ARG, "workspace_bytes %zu < required %zu", workspace_bytes, ws.bytes);
 

@@ -2,10 +2,11 @@
 // token, element-wise accumulation of the top-k expert output rows; §3.2 phase 6: accumulate then store the
 // token's output row; [MoE-comm] §一: the shared-expert output enters as bias).
 //
-// One wave per token.  The token's valid (slot, weight) pairs are compacted into lanes 0..nv-1 and read
-// back as scalars, so every gather is a 64-lane x 16-byte row segment at a uniform base.  Each pass covers
-// two 1024-byte segments of the output row and issues up to 16 gathers before the first FMA, so enough
-// bytes are in flight per wave.  fp32 accumulation in ascending k, one RNE rounding to bf16 at the end.
+// Work items are 1 KiB output segments (512 channels): item (t, s) is segment s of token t's output row, so
+// a token's row is produced by several short waves instead of one long one, which keeps more gathers in
+// flight across the chip.  The token's valid (slot, weight) pairs are compacted into lanes 0..nv-1 and read
+// back as scalars, so every gather is a 64-lane x 16-byte row segment at a uniform base; up to kBatch gathers
+// are issued before the first FMA.  fp32 accumulation in ascending k, one RNE rounding to bf16 at the end.
 #include "ep_device.hpp"
 #include "ep_internal.hpp"
 
@@ -14,7 +15,7 @@ namespace {
 
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
-constexpr int kBatch = 8;       // gathers issued per k-batch and per segment
+constexpr int kBatch = 8;       // gathers issued before the first FMA
 
 struct Params {
     const uint16_t* y;
@@ -23,6 +24,8 @@ struct Params {
     uint16_t* out;
     const int32_t* slot;
     int T, H, K;
+    int nseg;          // 1 KiB segments per row
+    int64_t nitems;    // T * nseg
 };
 
 __device__ __forceinline__ void fma8(float* acc, float wgt, u32x4 v) {
@@ -52,8 +55,9 @@ __global__ __launch_bounds__(kBlock) void k_combine(Params p) {
     __shared__ int cs_lds[kWavesPerBlock][kWave];
     __shared__ float cw_lds[kWavesPerBlock][kWave];
     const int lane = lane_id(), wv = threadIdx.x >> 6;
-    const int t = blockIdx.x * kWavesPerBlock + wv;
-    if (t >= p.T) return;
+    const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + wv;
+    if (item >= p.nitems) return;
+    const int t = (int)(item / p.nseg), seg = (int)(item % p.nseg);
 
     // compact the token's valid slots (ascending k) into lanes 0..nv-1
     const int s = lane < p.K ? p.slot[(int64_t)t * p.K + lane] : -1;
@@ -71,41 +75,26 @@ __global__ __launch_bounds__(kBlock) void k_combine(Params p) {
     const int cs = lane < nv ? cs_lds[wv][lane] : 0;
     const float cw = lane < nv ? cw_lds[wv][lane] : 0.0f;
 
-    const int nchunk = p.H / 8;                                   // 16-byte chunks per row
-    const u32x4* bias = p.bias ? reinterpret_cast<const u32x4*>(p.bias + (int64_t)t * p.H) : nullptr;
-    u32x4* out = reinterpret_cast<u32x4*>(p.out + (int64_t)t * p.H);
-    for (int c0 = lane; c0 - lane < nchunk; c0 += 2 * kWave) {
-        const int c1 = c0 + kWave;
-        const bool a0 = c0 < nchunk, a1 = c1 < nchunk;
-        float acc0[8], acc1[8];
+    const int c = seg * kWave + lane;                      // 16-byte chunk of the row
+    const bool active = c < p.H / 8;
+    float acc[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) acc0[k] = acc1[k] = 0.0f;
-        for (int kb = 0; kb < nv; kb += kBatch) {
-            u32x4 v0[kBatch], v1[kBatch];
+    for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
+    for (int kb = 0; kb < nv; kb += kBatch) {
+        u32x4 v[kBatch];
 #pragma unroll
-            for (int i = 0; i < kBatch; ++i) {
-                if (kb + i < nv) {
-                    const u32x4* row = reinterpret_cast<const u32x4*>(p.y + (int64_t)readlane(cs, kb + i) * p.H);
-                    if (a0) v0[i] = ld_nt(row + c0);
-                    if (a1) v1[i] = ld_nt(row + c1);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < kBatch; ++i) {
-                if (kb + i < nv) {
-                    const float wgt = readlane_f(cw, kb + i);
-                    if (a0) fma8(acc0, wgt, v0[i]);
-                    if (a1) fma8(acc1, wgt, v1[i]);
-                }
-            }
+        for (int i = 0; i < kBatch; ++i) {
+            if (kb + i < nv && active)
+                v[i] = ld_nt(reinterpret_cast<const u32x4*>(p.y + (int64_t)readlane(cs, kb + i) * p.H) + c);
         }
-        if (bias != nullptr) {
-            if (a0) add8(acc0, bias[c0]);
-            if (a1) add8(acc1, bias[c1]);
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            if (kb + i < nv && active) fma8(acc, readlane_f(cw, kb + i), v[i]);
         }
-        if (a0) st_nt(out + c0, pack8(acc0));
-        if (a1) st_nt(out + c1, pack8(acc1));
     }
+    if (!active) return;
+    if (p.bias != nullptr) add8(acc, reinterpret_cast<const u32x4*>(p.bias + (int64_t)t * p.H)[c]);
+    st_nt(reinterpret_cast<u32x4*>(p.out + (int64_t)t * p.H) + c, pack8(acc));
 }
 
 }  // namespace
@@ -121,7 +110,9 @@ hipError_t launch_combine(const Handle& h, const CombineArgs& a, hipStream_t str
     p.T = h.T;
     p.H = a.hidden;
     p.K = h.K;
-    const unsigned nblocks = (unsigned)((h.T + kWavesPerBlock - 1) / kWavesPerBlock);
+    p.nseg = (a.hidden / 8 + kWave - 1) / kWave;
+    p.nitems = (int64_t)h.T * p.nseg;
+    const unsigned nblocks = (unsigned)((p.nitems + kWavesPerBlock - 1) / kWavesPerBlock);
     hipLaunchKernelGGL(k_combine, dim3(nblocks), dim3(kBlock), 0, stream, p);
     return hipGetLastError();
 }

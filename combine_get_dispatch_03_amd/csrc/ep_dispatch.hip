@@ -2,13 +2,18 @@
 // and stored to the send buffer; §2.4: rows are placed expert-major at their expert's cursor; [MoE-comm] §一:
 // expert_alignment and do_zero_padding; [DeepEP-hotdry] key techniques: FP8 dispatch).
 //
-// One wave per token.  FP8: each lane loads 32 contiguous bytes (16 bf16 channels) per 1024-channel
-// step, eight lanes form one 128-channel group whose max |x| is reduced with three xor-shuffles, and the
-// lane casts its 16 channels to 16 e4m3 bytes, which it then stores as one 16-byte vector to every
-// destination row (the token's local slots and its send-window rows).  The group scales go through LDS so
-// each destination gets them in one contiguous store.  BF16: 16-byte bit copies.
-// Padding rows are handled by extra blocks after the token blocks, one group of blocks per local expert.
-// Nothing here decides a position: every row index comes from the layout's slot maps.
+// Work items are row segments, so that many short waves keep the write path busy:
+//   token item (t, s)  FP8: channels [1024 s, 1024 s + 1024) of token t.  Each lane loads 32 contiguous bytes
+//                      (16 bf16 channels), eight lanes form one 128-channel group whose max |x| comes from
+//                      three xor-shuffles, the lane casts its 16 channels to 16 e4m3 bytes and stores them as
+//                      one 16-byte vector to every destination row of the token (its local slots and its
+//                      send-window rows), together with the segment's 8 group scales.
+//                      BF16: one 512-channel (1 KiB) segment, bit copies.
+//   padding item (p, s) segment s of padding row pad_rows[p] (zeros; its metadata on segment 0).
+// Wave w runs token item w (if any) and then padding items w, w + W, w + 2W, ... (at most kPadItemsPerWave of
+// them).  The grid is sized on the host from the number of tokens and the worst-case padding; the actual
+// padding count is read on the device.
+// Nothing here decides a position: every row index comes from the layout.
 #include "ep_device.hpp"
 #include "ep_internal.hpp"
 
@@ -17,9 +22,7 @@ namespace {
 
 constexpr int kBlock = 256;                 // 4 waves
 constexpr int kWavesPerBlock = kBlock / kWave;
-constexpr int kSeg = 8;                     // steps held in registers before the stores
-constexpr int kPadRowsPerPart = 16;         // padding rows per pad block
-constexpr int kMaxGroups = kMaxHidden / 128;
+constexpr int kPadItemsPerWave = 2;         // worst-case padding items per wave used to size the grid
 
 struct Params {
     const uint16_t* x;
@@ -27,8 +30,8 @@ struct Params {
     const int64_t* topk_idx;
     const int32_t* slot;
     const int32_t* send_slot;
-    const int32_t* cnt_local;
-    const int32_t* psum;
+    const int32_t* pad_rows;
+    const int32_t* pad_total;
     uint8_t* recv_x;
     float* recv_scales;
     int32_t* recv_src;
@@ -39,23 +42,27 @@ struct Params {
     int64_t* send_topk_idx;
     float* send_topk_w;
     int T, H, K, R, epr;
-    int ntok_blocks;
-    int pad_parts;
+    int nstep;        // segments per row
+    int64_t ntok_items;   // T * nstep
+    int pad_sub;      // padding items per padding row (nstep with zero padding, 1 for metadata only, 0 none)
     int zero_pad;
+    int64_t nwaves;   // waves in the grid
 };
 
-// Metadata of the token's destinations; returns (via refs) the slot and send-row masks.
-__device__ __forceinline__ void token_meta(const Params& p, int t, int lane, int& ds, int& js, uint64_t& lmask,
-                                           uint64_t& smask) {
+// Per-token destinations: the local slots (lanes < K) and send rows (lanes < R); segment 0 also writes the
+// per-row metadata.
+__device__ __forceinline__ void token_dests(const Params& p, int t, bool meta, int lane, int& ds, int& js,
+                                            uint64_t& lmask, uint64_t& smask) {
     ds = lane < p.K ? p.slot[(int64_t)t * p.K + lane] : -1;
+    js = (p.send_slot != nullptr && lane < p.R) ? p.send_slot[(int64_t)t * p.R + lane] : -1;
+    lmask = ballot(ds >= 0);
+    smask = ballot(js >= 0);
+    if (!meta) return;
     const float wk = (lane < p.K && p.w != nullptr) ? p.w[(int64_t)t * p.K + lane] : 1.0f;
     if (ds >= 0) {
         if (p.recv_src) p.recv_src[ds] = t;
         if (p.recv_w) p.recv_w[ds] = wk;
     }
-    js = (p.send_slot != nullptr && lane < p.R) ? p.send_slot[(int64_t)t * p.R + lane] : -1;
-    lmask = ballot(ds >= 0);
-    smask = ballot(js >= 0);
     if (smask != 0 && (p.send_src || p.send_topk_idx || p.send_topk_w)) {
         const int64_t e = lane < p.K ? p.topk_idx[(int64_t)t * p.K + lane] : -1;
         for (uint64_t m = smask; m != 0; m &= m - 1) {
@@ -71,52 +78,63 @@ __device__ __forceinline__ void token_meta(const Params& p, int t, int lane, int
     }
 }
 
-__global__ __launch_bounds__(kBlock) void k_dispatch_fp8(Params p) {
-    __shared__ float sc_lds[kWavesPerBlock][kMaxGroups];
-    const int lane = lane_id(), wv = threadIdx.x >> 6;
-    if ((int)blockIdx.x >= p.ntok_blocks) {
-        // ---- padding rows of local expert j ------------------------------------------------------------------
-        const int pb = blockIdx.x - p.ntok_blocks;
-        const int j = pb / p.pad_parts, part = pb % p.pad_parts;
-        const int start = p.psum[j] + p.cnt_local[j], end = p.psum[j + 1];
-        const int r0 = start + part * kPadRowsPerPart, r1 = min(end, r0 + kPadRowsPerPart);
-        const int G = p.H / 128;
-        for (int row = r0 + wv; row < r1; row += kWavesPerBlock) {
-            if (lane == 0) {
-                if (p.recv_src) p.recv_src[row] = -1;
-                if (p.recv_w) p.recv_w[row] = 0.0f;
-            }
-            if (p.zero_pad) {
-                u32x4* dst = reinterpret_cast<u32x4*>(p.recv_x + (int64_t)row * p.H);
-                const u32x4 z = {0u, 0u, 0u, 0u};
-                for (int c = lane; c < p.H / 16; c += kWave) st_nt(dst + c, z);
-                for (int g = lane; g < G; g += kWave) p.recv_scales[(int64_t)row * G + g] = 0.0f;
-            }
-        }
-        return;
-    }
+// Padding items of wave gw are gw + j * nwaves for j < kPadItemsPerWave (the grid is sized so that no wave
+// has more).  Their row indices are fetched before the token work so the loads overlap it.
+struct PadWork {
+    int64_t nitems;
+    int row[kPadItemsPerWave];
+};
 
-    const int t = blockIdx.x * kWavesPerBlock + wv;
-    if (t >= p.T) return;
-    int ds, js;
-    uint64_t lmask, smask;
-    token_meta(p, t, lane, ds, js, lmask, smask);
-    if ((lmask | smask) == 0) return;
-
-    const int H = p.H, G = H / 128;
-    const int nstep = (H + 1023) / 1024;
-    const uint16_t* xrow = p.x + (int64_t)t * H;
-    float* sc = sc_lds[wv];
-    for (int seg = 0; seg < nstep; seg += kSeg) {
-        u32x4 q[kSeg];
+__device__ __forceinline__ void pad_prefetch(const Params& p, int64_t gw, PadWork& pw) {
+    pw.nitems = p.pad_sub == 0 ? 0 : (int64_t)(*p.pad_total) * p.pad_sub;
 #pragma unroll
-        for (int i = 0; i < kSeg; ++i) {
-            const int st = seg + i;
-            const int ch = (st * kWave + lane) * 16;
-            const bool active = st < nstep && ch < H;
+    for (int j = 0; j < kPadItemsPerWave; ++j) {
+        const int64_t i = gw + j * p.nwaves;
+        pw.row[j] = i < pw.nitems ? p.pad_rows[i / p.pad_sub] : 0;
+    }
+}
+
+template <bool FP8>
+__device__ __forceinline__ void pad_items(const Params& p, int64_t gw, int lane, const PadWork& pw) {
+    const int G = p.H / 128;
+    const int nchunk = FP8 ? p.H / 16 : p.H / 8;    // 16-byte chunks per row
+    const int64_t row_bytes = FP8 ? p.H : 2 * (int64_t)p.H;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < kPadItemsPerWave; ++j) {
+        const int64_t i = gw + j * p.nwaves;
+        if (i >= pw.nitems) break;
+        const int s = (int)(i % p.pad_sub);
+        const int row = pw.row[j];
+        if (p.zero_pad) {
+            const int c = s * kWave + lane;
+            if (c < nchunk) st_nt(reinterpret_cast<u32x4*>(p.recv_x + row * row_bytes) + c, z);
+            if (FP8 && lane < 8 && s * 8 + lane < G) p.recv_scales[(int64_t)row * G + s * 8 + lane] = 0.0f;
+        }
+        if (s == 0 && lane == 0) {
+            if (p.recv_src) p.recv_src[row] = -1;
+            if (p.recv_w) p.recv_w[row] = 0.0f;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void k_dispatch_fp8(Params p) {
+    const int lane = lane_id();
+    const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    PadWork pw;
+    pad_prefetch(p, gw, pw);
+    if (gw < p.ntok_items) {
+        const int t = (int)(gw / p.nstep), st = (int)(gw % p.nstep);
+        int ds, js;
+        uint64_t lmask, smask;
+        token_dests(p, t, st == 0, lane, ds, js, lmask, smask);
+        if ((lmask | smask) != 0) {
+            const int H = p.H, G = H / 128;
+            const int ch = (st * kWave + lane) * 16;      // first channel of this lane
+            const bool active = ch < H;
             u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
             if (active) {
-                const u32x4* src = reinterpret_cast<const u32x4*>(xrow + ch);
+                const u32x4* src = reinterpret_cast<const u32x4*>(p.x + (int64_t)t * H + ch);
                 a = ld_nt(src);
                 b = ld_nt(src + 1);
             }
@@ -131,114 +149,61 @@ __global__ __launch_bounds__(kBlock) void k_dispatch_fp8(Params p) {
             float m = 0.0f;
 #pragma unroll
             for (int k = 0; k < 16; ++k) m = fmaxf(m, fabsf(f[k]));
-            if (st < nstep) m = group8_max(m);           // uniform condition: all lanes shuffle together
+            m = group8_max(m);
             const float amax = fmaxf(m, 1e-4f);
             const float scale = amax / 448.0f;           // IEEE division (correctly rounded)
             const float inv = 448.0f / amax;
+            u32x4 q;
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-                q[i][k] = pack_e4m3x4(f[4 * k] * inv, f[4 * k + 1] * inv, f[4 * k + 2] * inv, f[4 * k + 3] * inv);
-            if (active && (lane & 7) == 0) sc[st * 8 + (lane >> 3)] = scale;
-        }
-        // stores: every destination row gets the same 16-byte vectors
-        for (uint64_t m = lmask; m != 0; m &= m - 1) {
-            const int s = readlane(ds, __builtin_ctzll(m));
-            u32x4* dst = reinterpret_cast<u32x4*>(p.recv_x + (int64_t)s * H);
-#pragma unroll
-            for (int i = 0; i < kSeg; ++i) {
-                const int st = seg + i;
-                const int ch = (st * kWave + lane) * 16;
-                if (st < nstep && ch < H) st_nt(dst + ch / 16, q[i]);
+                q[k] = pack_e4m3x4(f[4 * k] * inv, f[4 * k + 1] * inv, f[4 * k + 2] * inv, f[4 * k + 3] * inv);
+            // lane g < 8 takes the scale of group 8 st + g, held by lane 8 g
+            const float sg = __shfl(scale, 8 * (lane & 7));
+            const int g = st * 8 + lane;
+            const bool sc_lane = lane < 8 && g < G;
+            for (uint64_t mm = lmask; mm != 0; mm &= mm - 1) {
+                const int s = readlane(ds, __builtin_ctzll(mm));
+                if (active) st_nt(reinterpret_cast<u32x4*>(p.recv_x + (int64_t)s * H) + st * kWave + lane, q);
+                if (sc_lane) p.recv_scales[(int64_t)s * G + g] = sg;
             }
-        }
-        for (uint64_t m = smask; m != 0; m &= m - 1) {
-            const int r = __builtin_ctzll(m);
-            const int64_t row = (int64_t)r * p.T + readlane(js, r);
-            u32x4* dst = reinterpret_cast<u32x4*>(p.send_x + row * H);
-#pragma unroll
-            for (int i = 0; i < kSeg; ++i) {
-                const int st = seg + i;
-                const int ch = (st * kWave + lane) * 16;
-                if (st < nstep && ch < H) st_nt(dst + ch / 16, q[i]);
+            for (uint64_t mm = smask; mm != 0; mm &= mm - 1) {
+                const int r = __builtin_ctzll(mm);
+                const int64_t row = (int64_t)r * p.T + readlane(js, r);
+                if (active) st_nt(reinterpret_cast<u32x4*>(p.send_x + row * H) + st * kWave + lane, q);
+                if (sc_lane) p.send_scales[row * G + g] = sg;
             }
         }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    for (int g0 = 0; g0 < G; g0 += kWave) {
-        const int g = g0 + lane;
-        const float s_g = g < G ? sc[g] : 0.0f;
-        for (uint64_t m = lmask; m != 0; m &= m - 1) {
-            const int s = readlane(ds, __builtin_ctzll(m));
-            if (g < G) p.recv_scales[(int64_t)s * G + g] = s_g;
-        }
-        for (uint64_t m = smask; m != 0; m &= m - 1) {
-            const int r = __builtin_ctzll(m);
-            const int64_t row = (int64_t)r * p.T + readlane(js, r);
-            if (g < G) p.send_scales[row * G + g] = s_g;
-        }
-    }
+    pad_items<true>(p, gw, lane, pw);
 }
 
 __global__ __launch_bounds__(kBlock) void k_dispatch_bf16(Params p) {
-    const int lane = lane_id(), wv = threadIdx.x >> 6;
-    const int nchunk = p.H / 8;                            // 16-byte chunks per row
-    if ((int)blockIdx.x >= p.ntok_blocks) {
-        const int pb = blockIdx.x - p.ntok_blocks;
-        const int j = pb / p.pad_parts, part = pb % p.pad_parts;
-        const int start = p.psum[j] + p.cnt_local[j], end = p.psum[j + 1];
-        const int r0 = start + part * kPadRowsPerPart, r1 = min(end, r0 + kPadRowsPerPart);
-        for (int row = r0 + wv; row < r1; row += kWavesPerBlock) {
-            if (lane == 0) {
-                if (p.recv_src) p.recv_src[row] = -1;
-                if (p.recv_w) p.recv_w[row] = 0.0f;
+    const int lane = lane_id();
+    const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    PadWork pw;
+    pad_prefetch(p, gw, pw);
+    if (gw < p.ntok_items) {
+        const int t = (int)(gw / p.nstep), st = (int)(gw % p.nstep);
+        int ds, js;
+        uint64_t lmask, smask;
+        token_dests(p, t, st == 0, lane, ds, js, lmask, smask);
+        const int c = st * kWave + lane;                  // 16-byte chunk of the row
+        const bool active = c < p.H / 8;
+        if ((lmask | smask) != 0) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (active) v = ld_nt(reinterpret_cast<const u32x4*>(p.x + (int64_t)t * p.H) + c);
+            for (uint64_t mm = lmask; mm != 0; mm &= mm - 1) {
+                const int s = readlane(ds, __builtin_ctzll(mm));
+                if (active) st_nt(reinterpret_cast<u32x4*>(p.recv_x + (int64_t)s * p.H * 2) + c, v);
             }
-            if (p.zero_pad) {
-                u32x4* dst = reinterpret_cast<u32x4*>(p.recv_x + (int64_t)row * p.H * 2);
-                const u32x4 z = {0u, 0u, 0u, 0u};
-                for (int c = lane; c < nchunk; c += kWave) st_nt(dst + c, z);
-            }
-        }
-        return;
-    }
-
-    const int t = blockIdx.x * kWavesPerBlock + wv;
-    if (t >= p.T) return;
-    int ds, js;
-    uint64_t lmask, smask;
-    token_meta(p, t, lane, ds, js, lmask, smask);
-    if ((lmask | smask) == 0) return;
-
-    const int nstep = (nchunk + kWave - 1) / kWave;
-    const u32x4* src = reinterpret_cast<const u32x4*>(p.x + (int64_t)t * p.H);
-    for (int seg = 0; seg < nstep; seg += kSeg) {
-        u32x4 v[kSeg];
-#pragma unroll
-        for (int i = 0; i < kSeg; ++i) {
-            const int c = (seg + i) * kWave + lane;
-            if (seg + i < nstep && c < nchunk) v[i] = ld_nt(src + c);
-        }
-        for (uint64_t m = lmask; m != 0; m &= m - 1) {
-            const int s = readlane(ds, __builtin_ctzll(m));
-            u32x4* dst = reinterpret_cast<u32x4*>(p.recv_x + (int64_t)s * p.H * 2);
-#pragma unroll
-            for (int i = 0; i < kSeg; ++i) {
-                const int c = (seg + i) * kWave + lane;
-                if (seg + i < nstep && c < nchunk) st_nt(dst + c, v[i]);
-            }
-        }
-        for (uint64_t m = smask; m != 0; m &= m - 1) {
-            const int r = __builtin_ctzll(m);
-            const int64_t row = (int64_t)r * p.T + readlane(js, r);
-            u32x4* dst = reinterpret_cast<u32x4*>(p.send_x + row * p.H * 2);
-#pragma unroll
-            for (int i = 0; i < kSeg; ++i) {
-                const int c = (seg + i) * kWave + lane;
-                if (seg + i < nstep && c < nchunk) st_nt(dst + c, v[i]);
+            for (uint64_t mm = smask; mm != 0; mm &= mm - 1) {
+                const int r = __builtin_ctzll(mm);
+                const int64_t row = (int64_t)r * p.T + readlane(js, r);
+                if (active) st_nt(reinterpret_cast<u32x4*>(p.send_x + row * p.H * 2) + c, v);
             }
         }
     }
+    pad_items<false>(p, gw, lane, pw);
 }
 
 }  // namespace
@@ -251,8 +216,8 @@ hipError_t launch_dispatch(const Handle& h, const DispatchArgs& a, hipStream_t s
     p.topk_idx = h.topk_idx;
     p.slot = h.ws.slot;
     p.send_slot = h.R > 1 ? h.ws.send_slot : nullptr;
-    p.cnt_local = h.ws.cnt_local;
-    p.psum = h.ws.psum;
+    p.pad_rows = h.ws.pad_rows;
+    p.pad_total = h.ws.pad_total;
     p.recv_x = static_cast<uint8_t*>(a.out.recv_x);
     p.recv_scales = a.fp8 ? a.out.recv_x_scales : nullptr;
     p.recv_src = a.out.recv_src_idx;
@@ -268,10 +233,16 @@ hipError_t launch_dispatch(const Handle& h, const DispatchArgs& a, hipStream_t s
     p.R = h.R;
     p.epr = h.El;
     p.zero_pad = a.zero_pad ? 1 : 0;
-    p.ntok_blocks = (h.T + kWavesPerBlock - 1) / kWavesPerBlock;
-    const bool pads = h.A > 1 && (a.zero_pad || p.recv_src != nullptr || p.recv_w != nullptr);
-    p.pad_parts = pads ? (h.A - 1 + kPadRowsPerPart - 1) / kPadRowsPerPart : 1;
-    const int64_t nblocks = (int64_t)p.ntok_blocks + (pads ? (int64_t)h.El * p.pad_parts : 0);
+    p.nstep = a.fp8 ? (a.hidden + 1023) / 1024 : (a.hidden / 8 + kWave - 1) / kWave;
+    p.ntok_items = (int64_t)h.T * p.nstep;
+    const bool meta = p.recv_src != nullptr || p.recv_w != nullptr;
+    p.pad_sub = h.A > 1 ? (a.zero_pad ? p.nstep : (meta ? 1 : 0)) : 0;
+    const int64_t max_pad_items = (int64_t)h.El * (h.A - 1) * p.pad_sub;
+    int64_t nwaves = p.ntok_items;
+    const int64_t pad_waves = (max_pad_items + kPadItemsPerWave - 1) / kPadItemsPerWave;
+    if (pad_waves > nwaves) nwaves = pad_waves;
+    const int64_t nblocks = (nwaves + kWavesPerBlock - 1) / kWavesPerBlock;
+    p.nwaves = nblocks * kWavesPerBlock;
     if (a.fp8)
         hipLaunchKernelGGL(k_dispatch_fp8, dim3((unsigned)nblocks), dim3(kBlock), 0, stream, p);
     else

@@ -21,18 +21,18 @@ constexpr int kMaxHidden = 32768;
 
 // Device arrays carved out of the caller's workspace.  All int32.
 struct Workspace {
-    int32_t* tile_hist;   // [ntiles, E]  per-tile expert counts
-    int32_t* tile_rank;   // [ntiles, R]  per-tile token-in-rank counts
-    int32_t* tile_inv;    // [ntiles]     per-tile invalid entries
+    int32_t* tile_hist;   // [ntiles, E + R + 1]  per tile: expert counts | token-in-rank counts | invalid
     int32_t* slot;        // [T, K]       expert-major row of each entry, -1 if not local
     int32_t* send_slot;   // [T, R]       row in the send window of rank r, -1 if none (R > 1 only)
     int32_t* cnt_local;   // [El]         routed entries of each local expert
     int32_t* psum;        // [El + 1]     aligned exclusive row starts of the local experts
+    int32_t* pad_rows;    // [El * (A-1)] dense list of padding rows, expert by expert (A > 1 only)
+    int32_t* pad_total;   // [1]          number of padding rows
     size_t bytes;         // total bytes used
 };
 
 // Offsets of the carve-up for the given sizes; with base == nullptr only `bytes` is meaningful.
-Workspace carve_workspace(void* base, int T, int K, int E, int R);
+Workspace carve_workspace(void* base, int T, int K, int E, int R, int A);
 
 struct Handle {
     uint32_t magic;

@@ -64,7 +64,7 @@ int64_t ep_recv_capacity(int num_tokens, int num_topk, int num_local_experts, in
 
 /* Bytes of device workspace ep_get_layout needs for these sizes.  Host only.  Returns 0 for arguments
  * outside the limits (a valid call always needs more than 0 bytes). */
-size_t ep_layout_workspace_bytes(int num_tokens, int num_topk, int num_experts, int num_ranks);
+size_t ep_layout_workspace_bytes(int num_tokens, int num_topk, int num_experts, int num_ranks, int expert_alignment);
 
 /* Static description of a status code, and a thread-local description of the last failure in this thread. */
 const char* ep_status_string(ep_status_t status);

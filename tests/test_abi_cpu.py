@@ -27,7 +27,7 @@ def lib():
     L.ep_recv_capacity.restype = I64
     L.ep_recv_capacity.argtypes = [I, I, I, I]
     L.ep_layout_workspace_bytes.restype = SZ
-    L.ep_layout_workspace_bytes.argtypes = [I, I, I, I]
+    L.ep_layout_workspace_bytes.argtypes = [I, I, I, I, I]
     L.ep_status_string.restype = ctypes.c_char_p
     L.ep_last_error.restype = ctypes.c_char_p
     L.ep_get_layout.restype = I
@@ -63,14 +63,14 @@ def test_recv_capacity(lib):
 
 
 def test_workspace_bytes(lib):
-    n = lib.ep_layout_workspace_bytes(4096, 8, 256, 1)
+    n = lib.ep_layout_workspace_bytes(4096, 8, 256, 1, 128)
     assert n >= 4096 * 8 * 4 + 16 * 256 * 4
-    assert lib.ep_layout_workspace_bytes(0, 8, 256, 1) > 0
-    assert lib.ep_layout_workspace_bytes(4096, 8, 256, 3) == 0   # 256 % 3 != 0
-    assert lib.ep_layout_workspace_bytes(4096, 33, 256, 1) == 0  # K > 32
-    assert lib.ep_layout_workspace_bytes(4096, 8, 2048, 1) == 0  # E > 1024
-    assert lib.ep_layout_workspace_bytes(4096, 8, 256, 128) == 0 # R > 64
-    assert lib.ep_layout_workspace_bytes(4096, 8, 256, 8) > lib.ep_layout_workspace_bytes(4096, 8, 256, 1)
+    assert lib.ep_layout_workspace_bytes(0, 8, 256, 1, 128) > 0
+    assert lib.ep_layout_workspace_bytes(4096, 8, 256, 3, 128) == 0   # 256 % 3 != 0
+    assert lib.ep_layout_workspace_bytes(4096, 33, 256, 1, 128) == 0  # K > 32
+    assert lib.ep_layout_workspace_bytes(4096, 8, 2048, 1, 128) == 0  # E > 1024
+    assert lib.ep_layout_workspace_bytes(4096, 8, 256, 128, 128) == 0 # R > 64
+    assert lib.ep_layout_workspace_bytes(4096, 8, 256, 8, 128) > lib.ep_layout_workspace_bytes(4096, 8, 256, 1, 128)
 
 
 def test_status_strings(lib):
