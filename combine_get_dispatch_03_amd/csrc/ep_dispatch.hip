@@ -79,14 +79,20 @@ __device__ __forceinline__ void token_dests(const Params& p, int t, bool meta, i
 }
 
 // Padding items of wave gw are gw + j * nwaves for j < kPadItemsPerWave (the grid is sized so that no wave
-// has more).  Their row indices are fetched before the token work so the loads overlap it.
+// has more).  Their row indices are fetched before the token work so the loads overlap it.  Without zero
+// padding only the rows' metadata is written, one padding row per lane: wave gw takes rows 64 gw .. 64 gw + 63.
 struct PadWork {
     int64_t nitems;
     int row[kPadItemsPerWave];
 };
 
-__device__ __forceinline__ void pad_prefetch(const Params& p, int64_t gw, PadWork& pw) {
+__device__ __forceinline__ void pad_prefetch(const Params& p, int64_t gw, int lane, PadWork& pw) {
     pw.nitems = p.pad_sub == 0 ? 0 : (int64_t)(*p.pad_total) * p.pad_sub;
+    if (!p.zero_pad) {
+        const int64_t i = gw * kWave + lane;
+        pw.row[0] = i < pw.nitems ? p.pad_rows[i] : 0;
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < kPadItemsPerWave; ++j) {
         const int64_t i = gw + j * p.nwaves;
@@ -96,6 +102,13 @@ __device__ __forceinline__ void pad_prefetch(const Params& p, int64_t gw, PadWor
 
 template <bool FP8>
 __device__ __forceinline__ void pad_items(const Params& p, int64_t gw, int lane, const PadWork& pw) {
+    if (!p.zero_pad) {
+        if (gw * kWave + lane < pw.nitems) {
+            if (p.recv_src) p.recv_src[pw.row[0]] = -1;
+            if (p.recv_w) p.recv_w[pw.row[0]] = 0.0f;
+        }
+        return;
+    }
     const int G = p.H / 128;
     const int nchunk = FP8 ? p.H / 16 : p.H / 8;    // 16-byte chunks per row
     const int64_t row_bytes = FP8 ? p.H : 2 * (int64_t)p.H;
@@ -122,7 +135,7 @@ __global__ __launch_bounds__(kBlock) void k_dispatch_fp8(Params p) {
     const int lane = lane_id();
     const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
     PadWork pw;
-    pad_prefetch(p, gw, pw);
+    pad_prefetch(p, gw, lane, pw);
     if (gw < p.ntok_items) {
         const int t = (int)(gw / p.nstep), st = (int)(gw % p.nstep);
         int ds, js;
@@ -181,7 +194,7 @@ __global__ __launch_bounds__(kBlock) void k_dispatch_bf16(Params p) {
     const int lane = lane_id();
     const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
     PadWork pw;
-    pad_prefetch(p, gw, pw);
+    pad_prefetch(p, gw, lane, pw);
     if (gw < p.ntok_items) {
         const int t = (int)(gw / p.nstep), st = (int)(gw % p.nstep);
         int ds, js;
@@ -239,7 +252,8 @@ hipError_t launch_dispatch(const Handle& h, const DispatchArgs& a, hipStream_t s
     p.pad_sub = h.A > 1 ? (a.zero_pad ? p.nstep : (meta ? 1 : 0)) : 0;
     const int64_t max_pad_items = (int64_t)h.El * (h.A - 1) * p.pad_sub;
     int64_t nwaves = p.ntok_items;
-    const int64_t pad_waves = (max_pad_items + kPadItemsPerWave - 1) / kPadItemsPerWave;
+    const int64_t per_wave = a.zero_pad ? kPadItemsPerWave : kWave;
+    const int64_t pad_waves = (max_pad_items + per_wave - 1) / per_wave;
     if (pad_waves > nwaves) nwaves = pad_waves;
     const int64_t nblocks = (nwaves + kWavesPerBlock - 1) / kWavesPerBlock;
     p.nwaves = nblocks * kWavesPerBlock;

@@ -206,6 +206,8 @@ EDGE = [
     (257, 4, 128, 64, 63, 5, 256, True, False, "uniform"),    # 64 ranks, last rank
     (200, 5, 40, 4, 1, 1000, 1024, True, True, "invalid"),    # large alignment, -1 and invalid entries
     (4096, 8, 256, 8, 3, 128, 2048, True, True, "skew"),      # one hot expert owned by this rank
+    (256, 8, 256, 4, 1, 64, 512, True, True, "uniform"),      # exactly one tile, with send windows
+    (257, 3, 16, 2, 0, 8, 256, False, True, "invalid"),       # one token past a tile, BF16 windows
 ]
 
 
