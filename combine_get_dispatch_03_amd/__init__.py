@@ -63,6 +63,10 @@ def _load_library():
     lib.ep_combine.argtypes = [P, P, I, I64, P, P, P, P]
     lib.ep_handle_free.restype = I
     lib.ep_handle_free.argtypes = [P]
+    lib.ep_dispatch_rows.restype = I
+    lib.ep_dispatch_rows.argtypes = [P, P, I, P, I, P, I, ctypes.POINTER(_DispatchOut), P]
+    lib.ep_combine_reduce.restype = I
+    lib.ep_combine_reduce.argtypes = [P, P, I, P, P, P, P]
     return lib
 
 
@@ -258,10 +262,66 @@ def ep_combine(handle: Handle, y, topk_weights=None, bias=None, out=None, stream
     return out
 
 
+def ep_dispatch_rows(handle: Handle, rows, scales=None, topk_weights=None, do_zero_padding=False, out=None,
+                     stream=None):
+    """Place received rows (uint8 [N, row_bytes] or bf16 [N, H]) expert-major through `handle` (a layout over
+    the rows' local expert ids).  scales: fp32 [N, G] travelling with the rows.  Returns the output dict."""
+    if rows.dtype not in (torch.uint8, torch.bfloat16):
+        raise TypeError("rows must be uint8 or bfloat16")
+    _need(rows, rows.dtype, "rows")
+    if rows.dim() != 2 or rows.shape[0] != handle.num_tokens:
+        raise ValueError("rows must be [num_received_rows, row_elements]")
+    row_bytes = rows.shape[1] * rows.element_size()
+    G = 0
+    if scales is not None:
+        _need(scales, torch.float32, "scales")
+        G = scales.shape[1]
+    if topk_weights is not None:
+        _need(topk_weights, torch.float32, "topk_weights", shape=(handle.num_tokens, handle.num_topk))
+    cap = handle.recv_capacity
+    if out is None:
+        dev = rows.device
+        out = dict(recv_x=torch.empty((cap, rows.shape[1]), dtype=rows.dtype, device=dev),
+                   recv_x_scales=torch.empty((cap, G), dtype=torch.float32, device=dev) if G else None,
+                   recv_src_idx=torch.empty(cap, dtype=torch.int32, device=dev),
+                   recv_topk_weights=torch.empty(cap, dtype=torch.float32, device=dev))
+    s = _DispatchOut(
+        recv_x=out["recv_x"].data_ptr(),
+        recv_x_scales=out["recv_x_scales"].data_ptr() if out.get("recv_x_scales") is not None else None,
+        recv_src_idx=out["recv_src_idx"].data_ptr() if out.get("recv_src_idx") is not None else None,
+        recv_topk_weights=out["recv_topk_weights"].data_ptr() if out.get("recv_topk_weights") is not None else None,
+        recv_capacity=out["recv_x"].shape[0])
+    _check(_lib.ep_dispatch_rows(handle.ptr, _ptr(rows), row_bytes, _ptr(scales), G, _ptr(topk_weights),
+                                 int(bool(do_zero_padding)), ctypes.byref(s), _stream(stream)), "ep_dispatch_rows")
+    return out
+
+
+def ep_combine_reduce(handle: Handle, partials=None, local=None, bias=None, out=None, hidden=None, stream=None):
+    """Sum the combine partials returned by the other ranks (bf16 [R, T, H], window r from rank r) with this
+    rank's local combine output and the bias.  Returns out [T, H] bf16."""
+    T = handle.num_tokens
+    ref = next(t for t in (partials, local, bias, out) if t is not None)
+    H = ref.shape[-1] if hidden is None else hidden
+    if partials is not None:
+        _need(partials, torch.bfloat16, "partials", shape=(handle.num_ranks, T, H))
+    if local is not None:
+        _need(local, torch.bfloat16, "local", shape=(T, H))
+    if bias is not None:
+        _need(bias, torch.bfloat16, "bias", shape=(T, H))
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=ref.device)
+    else:
+        _need(out, torch.bfloat16, "out", shape=(T, H))
+    _check(_lib.ep_combine_reduce(handle.ptr, _ptr(partials), H, _ptr(local), _ptr(bias), _ptr(out),
+                                  _stream(stream)), "ep_combine_reduce")
+    return out
+
+
 def ep_handle_free(handle: Handle):
     handle.free()
 
 
-__all__ = ["ep_get_layout", "ep_dispatch", "ep_combine", "ep_handle_free", "ep_recv_capacity",
+__all__ = ["ep_get_layout", "ep_dispatch", "ep_combine", "ep_handle_free", "ep_recv_capacity", "ep_dispatch_rows",
+           "ep_combine_reduce",
            "ep_layout_workspace_bytes", "alloc_dispatch_outputs", "Handle", "EPError", "LIB_PATH",
            "hip_runtimes_loaded"]

@@ -186,14 +186,81 @@ ep_status_t ep_dispatch(ep_handle_t handle, const void* x, int hidden, const flo
         }
     }
     DispatchArgs a;
+    a.mode = fp8 ? DispatchArgs::kFp8 : DispatchArgs::kBf16;
     a.x = x;
+    a.x_scales = nullptr;
+    a.row_bytes = 0;
+    a.nscales = 0;
     a.topk_weights = topk_weights;
     a.hidden = hidden;
-    a.fp8 = fp8;
     a.zero_pad = do_zero_padding != 0;
     a.out = *out;
+    if (!fp8) a.out.recv_x_scales = nullptr;
     const hipError_t err = launch_dispatch(*h, a, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return hip_fail(err, "dispatch launch");
+    return EP_OK;
+}
+
+ep_status_t ep_dispatch_rows(ep_handle_t handle, const void* rows, int row_bytes, const float* row_scales,
+                             int num_scales, const float* topk_weights, int do_zero_padding,
+                             const ep_dispatch_out_t* out, void* stream) {
+    g_last_error[0] = '\0';
+    const Handle* h = check_handle(handle);
+    if (h == nullptr) return fail(EP_ERR_INVALID_ARG, "invalid handle");
+    if (row_bytes < 16 || row_bytes > kMaxRowBytes || row_bytes % 16 != 0)
+        return fail(EP_ERR_INVALID_ARG, "row_bytes must be a multiple of 16 in [16, 65536]");
+    if (num_scales < 0 || num_scales > kMaxHidden / 128)
+        return fail(EP_ERR_INVALID_ARG, "num_scales must be in [0, 256]");
+    if (out == nullptr) return fail(EP_ERR_INVALID_ARG, "out is NULL");
+    if (h->T > 0) {
+        if (rows == nullptr || !aligned16(rows)) return fail(EP_ERR_INVALID_ARG, "rows must be non-NULL and 16-byte aligned");
+        if (num_scales > 0 && row_scales == nullptr) return fail(EP_ERR_INVALID_ARG, "num_scales > 0 needs row_scales");
+        if (out->recv_x == nullptr || !aligned16(out->recv_x))
+            return fail(EP_ERR_INVALID_ARG, "recv_x must be non-NULL and 16-byte aligned");
+        if (out->recv_capacity < h->cap)
+            return fail(EP_ERR_INVALID_ARG, "recv_capacity %lld < required %lld", (long long)out->recv_capacity,
+                        (long long)h->cap);
+        if (num_scales > 0 && out->recv_x_scales == nullptr)
+            return fail(EP_ERR_INVALID_ARG, "num_scales > 0 needs recv_x_scales");
+    }
+    DispatchArgs a;
+    a.mode = DispatchArgs::kRows;
+    a.x = rows;
+    a.x_scales = num_scales > 0 ? row_scales : nullptr;
+    a.row_bytes = row_bytes;
+    a.nscales = num_scales;
+    a.topk_weights = topk_weights;
+    a.hidden = 0;
+    a.zero_pad = do_zero_padding != 0;
+    a.out = *out;
+    if (num_scales == 0) a.out.recv_x_scales = nullptr;
+    const hipError_t err = launch_dispatch(*h, a, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return hip_fail(err, "dispatch_rows launch");
+    return EP_OK;
+}
+
+ep_status_t ep_combine_reduce(ep_handle_t handle, const void* partials, int hidden, const void* local,
+                              const void* bias, void* out, void* stream) {
+    g_last_error[0] = '\0';
+    const Handle* h = check_handle(handle);
+    if (h == nullptr) return fail(EP_ERR_INVALID_ARG, "invalid handle");
+    if (hidden < 8 || hidden > kMaxHidden || hidden % 8 != 0)
+        return fail(EP_ERR_INVALID_ARG, "hidden must be a multiple of 8 in [8, 32768]");
+    if (h->T > 0) {
+        if (h->R > 1 && (partials == nullptr || !aligned16(partials)))
+            return fail(EP_ERR_INVALID_ARG, "partials must be non-NULL and 16-byte aligned");
+        if (out == nullptr || !aligned16(out)) return fail(EP_ERR_INVALID_ARG, "out must be non-NULL and 16-byte aligned");
+        if (local != nullptr && !aligned16(local)) return fail(EP_ERR_INVALID_ARG, "local must be 16-byte aligned");
+        if (bias != nullptr && !aligned16(bias)) return fail(EP_ERR_INVALID_ARG, "bias must be 16-byte aligned");
+    }
+    ReduceArgs a;
+    a.partials = partials;
+    a.local = local;
+    a.bias = bias;
+    a.out = out;
+    a.hidden = hidden;
+    const hipError_t err = launch_combine_reduce(*h, a, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return hip_fail(err, "combine_reduce launch");
     return EP_OK;
 }
 

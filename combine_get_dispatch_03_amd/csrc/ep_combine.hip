@@ -97,7 +97,84 @@ __global__ __launch_bounds__(kBlock) void k_combine(Params p) {
     st_nt(reinterpret_cast<u32x4*>(p.out + (int64_t)t * p.H) + c, pack8(acc));
 }
 
+// Source-side reduce after the combine exchange ([DeepEP->MegaMoE] §2.5: the reduce epilogue adds the rows
+// that come back from the ranks that held the token's experts; [MoE-comm] §一: plus the shared-expert bias).
+// Item (t, s) = 1 KiB segment s of token t: lanes r < R read the token's window rows, the valid ones are
+// compacted and gathered like combine's expert rows; fp32 sum of local, then ranks in ascending order, then
+// bias; one RNE rounding.
+struct ReduceParams {
+    const uint16_t* partials;   // [R, T, H]
+    const uint16_t* local;
+    const uint16_t* bias;
+    uint16_t* out;
+    const int32_t* send_slot;   // [T, R] or nullptr (R == 1)
+    int T, H, R, rank;
+    int nseg;
+    int64_t nitems;
+};
+
+__global__ __launch_bounds__(kBlock) void k_combine_reduce(ReduceParams p) {
+    __shared__ int cs_lds[kWavesPerBlock][kWave];
+    const int lane = lane_id(), wv = threadIdx.x >> 6;
+    const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + wv;
+    if (item >= p.nitems) return;
+    const int t = (int)(item / p.nseg), seg = (int)(item % p.nseg);
+    int64_t row = -1;                                      // window row of token t for rank `lane`
+    if (p.send_slot != nullptr && lane < p.R && lane != p.rank) {
+        const int j = p.send_slot[(int64_t)t * p.R + lane];
+        if (j >= 0) row = (int64_t)lane * p.T + j;
+    }
+    const uint64_t vm = ballot(row >= 0);
+    const int nv = popc64(vm);
+    if (row >= 0) cs_lds[wv][popc64(vm & lanemask_lt())] = (int)row;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int cs = lane < nv ? cs_lds[wv][lane] : 0;
+
+    const int c = seg * kWave + lane;
+    const bool active = c < p.H / 8;
+    float acc[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
+    if (active && p.local != nullptr) add8(acc, reinterpret_cast<const u32x4*>(p.local + (int64_t)t * p.H)[c]);
+    for (int kb = 0; kb < nv; kb += kBatch) {
+        u32x4 v[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            if (kb + i < nv && active)
+                v[i] = ld_nt(reinterpret_cast<const u32x4*>(p.partials + (int64_t)readlane(cs, kb + i) * p.H) + c);
+        }
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            if (kb + i < nv && active) add8(acc, v[i]);
+        }
+    }
+    if (!active) return;
+    if (p.bias != nullptr) add8(acc, reinterpret_cast<const u32x4*>(p.bias + (int64_t)t * p.H)[c]);
+    st_nt(reinterpret_cast<u32x4*>(p.out + (int64_t)t * p.H) + c, pack8(acc));
+}
+
 }  // namespace
+
+hipError_t launch_combine_reduce(const Handle& h, const ReduceArgs& a, hipStream_t stream) {
+    if (h.T == 0) return hipSuccess;
+    ReduceParams p;
+    p.partials = static_cast<const uint16_t*>(a.partials);
+    p.local = static_cast<const uint16_t*>(a.local);
+    p.bias = static_cast<const uint16_t*>(a.bias);
+    p.out = static_cast<uint16_t*>(a.out);
+    p.send_slot = h.R > 1 ? h.ws.send_slot : nullptr;
+    p.T = h.T;
+    p.H = a.hidden;
+    p.R = h.R;
+    p.rank = h.rank;
+    p.nseg = (a.hidden / 8 + kWave - 1) / kWave;
+    p.nitems = (int64_t)h.T * p.nseg;
+    const unsigned nblocks = (unsigned)((p.nitems + kWavesPerBlock - 1) / kWavesPerBlock);
+    hipLaunchKernelGGL(k_combine_reduce, dim3(nblocks), dim3(kBlock), 0, stream, p);
+    return hipGetLastError();
+}
 
 hipError_t launch_combine(const Handle& h, const CombineArgs& a, hipStream_t stream) {
     if (h.T == 0) return hipSuccess;

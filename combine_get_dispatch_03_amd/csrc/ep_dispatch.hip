@@ -8,7 +8,8 @@
 //                      three xor-shuffles, the lane casts its 16 channels to 16 e4m3 bytes and stores them as
 //                      one 16-byte vector to every destination row of the token (its local slots and its
 //                      send-window rows), together with the segment's 8 group scales.
-//                      BF16: one 512-channel (1 KiB) segment, bit copies.
+//                      BF16, and rows already in their receive format (the receiver's copy epilogue,
+//                      [DeepEP->MegaMoE] §2.4): one 1 KiB segment of 16-byte copies, plus the row's scales.
 //   padding item (p, s) segment s of padding row pad_rows[p] (zeros; its metadata on segment 0).
 // Wave w runs token item w (if any) and then padding items w, w + W, w + 2W, ... (at most kPadItemsPerWave of
 // them).  The grid is sized on the host from the number of tokens and the worst-case padding; the actual
@@ -25,7 +26,8 @@ constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kPadItemsPerWave = 2;         // worst-case padding items per wave used to size the grid
 
 struct Params {
-    const uint16_t* x;
+    const uint8_t* src;          // token rows: bf16 [T, H] (FP8 kernel) or row_bytes-byte rows (raw kernel)
+    const float* src_scales;     // raw kernel: [T, G] scales travelling with the rows, or nullptr
     const float* w;
     const int64_t* topk_idx;
     const int32_t* slot;
@@ -42,6 +44,8 @@ struct Params {
     int64_t* send_topk_idx;
     float* send_topk_w;
     int T, H, K, R, epr;
+    int row_bytes;    // bytes of one destination row
+    int G;            // fp32 scales per row (FP8: H / 128; raw: as given, 0 for none)
     int nstep;        // segments per row
     int64_t ntok_items;   // T * nstep
     int pad_sub;      // padding items per padding row (nstep with zero padding, 1 for metadata only, 0 none)
@@ -109,9 +113,9 @@ __device__ __forceinline__ void pad_items(const Params& p, int64_t gw, int lane,
         }
         return;
     }
-    const int G = p.H / 128;
-    const int nchunk = FP8 ? p.H / 16 : p.H / 8;    // 16-byte chunks per row
-    const int64_t row_bytes = FP8 ? p.H : 2 * (int64_t)p.H;
+    const int G = p.G;
+    const int nchunk = p.row_bytes / 16;            // 16-byte chunks per row
+    const int64_t row_bytes = p.row_bytes;
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int j = 0; j < kPadItemsPerWave; ++j) {
@@ -122,7 +126,11 @@ __device__ __forceinline__ void pad_items(const Params& p, int64_t gw, int lane,
         if (p.zero_pad) {
             const int c = s * kWave + lane;
             if (c < nchunk) st_nt(reinterpret_cast<u32x4*>(p.recv_x + row * row_bytes) + c, z);
-            if (FP8 && lane < 8 && s * 8 + lane < G) p.recv_scales[(int64_t)row * G + s * 8 + lane] = 0.0f;
+            if (FP8) {
+                if (lane < 8 && s * 8 + lane < G) p.recv_scales[(int64_t)row * G + s * 8 + lane] = 0.0f;
+            } else if (s == 0) {
+                for (int g = lane; g < G; g += kWave) p.recv_scales[(int64_t)row * G + g] = 0.0f;
+            }
         }
         if (s == 0 && lane == 0) {
             if (p.recv_src) p.recv_src[row] = -1;
@@ -147,7 +155,7 @@ __global__ __launch_bounds__(kBlock) void k_dispatch_fp8(Params p) {
             const bool active = ch < H;
             u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
             if (active) {
-                const u32x4* src = reinterpret_cast<const u32x4*>(p.x + (int64_t)t * H + ch);
+                const u32x4* src = reinterpret_cast<const u32x4*>(p.src + ((int64_t)t * H + ch) * 2);
                 a = ld_nt(src);
                 b = ld_nt(src + 1);
             }
@@ -190,7 +198,9 @@ __global__ __launch_bounds__(kBlock) void k_dispatch_fp8(Params p) {
     pad_items<true>(p, gw, lane, pw);
 }
 
-__global__ __launch_bounds__(kBlock) void k_dispatch_bf16(Params p) {
+// Rows that need no conversion (BF16 dispatch, and received rows that already carry their receive format):
+// 16-byte copies of one 1 KiB segment per wave; segment 0 also copies the row's scales, if any.
+__global__ __launch_bounds__(kBlock) void k_dispatch_raw(Params p) {
     const int lane = lane_id();
     const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
     PadWork pw;
@@ -201,18 +211,30 @@ __global__ __launch_bounds__(kBlock) void k_dispatch_bf16(Params p) {
         uint64_t lmask, smask;
         token_dests(p, t, st == 0, lane, ds, js, lmask, smask);
         const int c = st * kWave + lane;                  // 16-byte chunk of the row
-        const bool active = c < p.H / 8;
+        const bool active = c < p.row_bytes / 16;
         if ((lmask | smask) != 0) {
+            const int64_t rb = p.row_bytes;
             u32x4 v = {0u, 0u, 0u, 0u};
-            if (active) v = ld_nt(reinterpret_cast<const u32x4*>(p.x + (int64_t)t * p.H) + c);
+            if (active) v = ld_nt(reinterpret_cast<const u32x4*>(p.src + (int64_t)t * rb) + c);
             for (uint64_t mm = lmask; mm != 0; mm &= mm - 1) {
                 const int s = readlane(ds, __builtin_ctzll(mm));
-                if (active) st_nt(reinterpret_cast<u32x4*>(p.recv_x + (int64_t)s * p.H * 2) + c, v);
+                if (active) st_nt(reinterpret_cast<u32x4*>(p.recv_x + (int64_t)s * rb) + c, v);
             }
             for (uint64_t mm = smask; mm != 0; mm &= mm - 1) {
                 const int r = __builtin_ctzll(mm);
                 const int64_t row = (int64_t)r * p.T + readlane(js, r);
-                if (active) st_nt(reinterpret_cast<u32x4*>(p.send_x + row * p.H * 2) + c, v);
+                if (active) st_nt(reinterpret_cast<u32x4*>(p.send_x + row * rb) + c, v);
+            }
+            if (st == 0 && p.G > 0) {
+                for (int g = lane; g < p.G; g += kWave) {
+                    const float sc = p.src_scales[(int64_t)t * p.G + g];
+                    for (uint64_t mm = lmask; mm != 0; mm &= mm - 1)
+                        p.recv_scales[(int64_t)readlane(ds, __builtin_ctzll(mm)) * p.G + g] = sc;
+                    for (uint64_t mm = smask; mm != 0; mm &= mm - 1) {
+                        const int r = __builtin_ctzll(mm);
+                        p.send_scales[((int64_t)r * p.T + readlane(js, r)) * p.G + g] = sc;
+                    }
+                }
             }
         }
     }
@@ -223,8 +245,11 @@ __global__ __launch_bounds__(kBlock) void k_dispatch_bf16(Params p) {
 
 hipError_t launch_dispatch(const Handle& h, const DispatchArgs& a, hipStream_t stream) {
     if (h.T == 0) return hipSuccess;
+    const bool fp8 = a.mode == DispatchArgs::kFp8;
+    const bool raw_rows = a.mode == DispatchArgs::kRows;
     Params p;
-    p.x = static_cast<const uint16_t*>(a.x);
+    p.src = static_cast<const uint8_t*>(a.x);
+    p.src_scales = raw_rows ? a.x_scales : nullptr;
     p.w = a.topk_weights;
     p.topk_idx = h.topk_idx;
     p.slot = h.ws.slot;
@@ -232,21 +257,32 @@ hipError_t launch_dispatch(const Handle& h, const DispatchArgs& a, hipStream_t s
     p.pad_rows = h.ws.pad_rows;
     p.pad_total = h.ws.pad_total;
     p.recv_x = static_cast<uint8_t*>(a.out.recv_x);
-    p.recv_scales = a.fp8 ? a.out.recv_x_scales : nullptr;
+    p.recv_scales = a.out.recv_x_scales;
     p.recv_src = a.out.recv_src_idx;
     p.recv_w = a.out.recv_topk_weights;
-    p.send_x = h.R > 1 ? static_cast<uint8_t*>(a.out.send_x) : nullptr;
-    p.send_scales = (h.R > 1 && a.fp8) ? a.out.send_x_scales : nullptr;
-    p.send_src = h.R > 1 ? a.out.send_src_idx : nullptr;
-    p.send_topk_idx = h.R > 1 ? a.out.send_topk_idx : nullptr;
-    p.send_topk_w = h.R > 1 ? a.out.send_topk_weights : nullptr;
+    const bool windows = h.R > 1 && !raw_rows;
+    p.send_x = windows ? static_cast<uint8_t*>(a.out.send_x) : nullptr;
+    p.send_scales = windows ? a.out.send_x_scales : nullptr;
+    p.send_src = windows ? a.out.send_src_idx : nullptr;
+    p.send_topk_idx = windows ? a.out.send_topk_idx : nullptr;
+    p.send_topk_w = windows ? a.out.send_topk_weights : nullptr;
+    if (!windows) p.send_slot = nullptr;
     p.T = h.T;
     p.H = a.hidden;
     p.K = h.K;
     p.R = h.R;
     p.epr = h.El;
     p.zero_pad = a.zero_pad ? 1 : 0;
-    p.nstep = a.fp8 ? (a.hidden + 1023) / 1024 : (a.hidden / 8 + kWave - 1) / kWave;
+    if (fp8) {
+        p.row_bytes = a.hidden;
+        p.G = a.hidden / 128;
+        p.nstep = (a.hidden + 1023) / 1024;
+    } else {
+        p.row_bytes = raw_rows ? a.row_bytes : 2 * a.hidden;
+        p.G = raw_rows ? a.nscales : 0;
+        p.nstep = (p.row_bytes / 16 + kWave - 1) / kWave;
+    }
+    if (p.G == 0) p.recv_scales = nullptr;
     p.ntok_items = (int64_t)h.T * p.nstep;
     const bool meta = p.recv_src != nullptr || p.recv_w != nullptr;
     p.pad_sub = h.A > 1 ? (a.zero_pad ? p.nstep : (meta ? 1 : 0)) : 0;
@@ -257,10 +293,10 @@ hipError_t launch_dispatch(const Handle& h, const DispatchArgs& a, hipStream_t s
     if (pad_waves > nwaves) nwaves = pad_waves;
     const int64_t nblocks = (nwaves + kWavesPerBlock - 1) / kWavesPerBlock;
     p.nwaves = nblocks * kWavesPerBlock;
-    if (a.fp8)
+    if (fp8)
         hipLaunchKernelGGL(k_dispatch_fp8, dim3((unsigned)nblocks), dim3(kBlock), 0, stream, p);
     else
-        hipLaunchKernelGGL(k_dispatch_bf16, dim3((unsigned)nblocks), dim3(kBlock), 0, stream, p);
+        hipLaunchKernelGGL(k_dispatch_raw, dim3((unsigned)nblocks), dim3(kBlock), 0, stream, p);
     return hipGetLastError();
 }
 

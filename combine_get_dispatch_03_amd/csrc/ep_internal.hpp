@@ -18,6 +18,7 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxRanks = 64;
 constexpr int kMaxAlignment = 65536;
 constexpr int kMaxHidden = 32768;
+constexpr int kMaxRowBytes = 65536;
 
 // Device arrays carved out of the caller's workspace.  All int32.
 struct Workspace {
@@ -57,14 +58,27 @@ struct LayoutOutputs {
 hipError_t launch_layout(const Handle& h, const LayoutOutputs& out, hipStream_t stream);
 
 struct DispatchArgs {
-    const void* x;
+    enum Mode { kBf16, kFp8, kRows };
+    Mode mode;
+    const void* x;             // kBf16 / kFp8: bf16 [T, hidden]; kRows: [T, row_bytes] bytes
+    const float* x_scales;     // kRows: [T, nscales] or nullptr
+    int row_bytes;             // kRows only
+    int nscales;               // kRows only
     const float* topk_weights;
     int hidden;
-    bool fp8;
     bool zero_pad;
     ep_dispatch_out_t out;
 };
 hipError_t launch_dispatch(const Handle& h, const DispatchArgs& a, hipStream_t stream);
+
+struct ReduceArgs {
+    const void* partials;      // bf16 [R, T, hidden]
+    const void* local;         // bf16 [T, hidden] or nullptr
+    const void* bias;          // bf16 [T, hidden] or nullptr
+    void* out;                 // bf16 [T, hidden]
+    int hidden;
+};
+hipError_t launch_combine_reduce(const Handle& h, const ReduceArgs& a, hipStream_t stream);
 
 struct CombineArgs {
     const void* y;

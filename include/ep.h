@@ -142,6 +142,26 @@ ep_status_t ep_dispatch(ep_handle_t handle, const void* x, int hidden, const flo
                         void* stream);
 
 /*
+ * ep_dispatch_rows -- the receiver's copy epilogue ([DeepEP->MegaMoE] §2.4: rows that arrived
+ * destination-major are placed expert-major, each at its expert's rows).  Rows already carry their receive
+ * format (the bytes and scales of a sender's send window), so nothing is converted.
+ *
+ *   handle          from ep_get_layout over the received rows' expert ids: topk_idx [N, K] holding ids
+ *                   local to this rank (0..E_local-1, e.g. a window's send_topk_idx) or -1, with
+ *                   num_experts = E_local and num_ranks = 1.  Rows that were not received are all -1.
+ *   rows            device [N, row_bytes] bytes, 16-byte aligned; row_bytes % 16 == 0, <= 65536.
+ *   row_scales      device fp32 [N, num_scales] (nullable when num_scales == 0), copied with each row.
+ *   topk_weights    device fp32 [N, K], nullable (weights of 1): recv_topk_weights of the placed rows.
+ *   do_zero_padding as in ep_dispatch.
+ *   out             recv_x [recv_capacity, row_bytes], recv_x_scales [recv_capacity, num_scales] (required iff
+ *                   num_scales > 0), recv_src_idx = index of the received row (-1 on padding rows),
+ *                   recv_topk_weights; send fields are ignored.
+ */
+ep_status_t ep_dispatch_rows(ep_handle_t handle, const void* rows, int row_bytes, const float* row_scales,
+                             int num_scales, const float* topk_weights, int do_zero_padding,
+                             const ep_dispatch_out_t* out, void* stream);
+
+/*
  * ep_combine -- top-k reduction back to token order ([DeepEP->MegaMoE] §2.3 and §2.5: element-wise
  * accumulation of the top-k expert outputs of a token; [MoE-comm] §一: the shared expert's output joins
  * as bias).
@@ -157,6 +177,23 @@ ep_status_t ep_dispatch(ep_handle_t handle, const void* x, int hidden, const flo
  */
 ep_status_t ep_combine(ep_handle_t handle, const void* y, int hidden, int64_t y_rows, const float* topk_weights,
                        const void* bias, void* out, void* stream);
+
+/*
+ * ep_combine_reduce -- the source rank's reduce epilogue after the combine exchange ([DeepEP->MegaMoE] §2.5:
+ * the rows returned by the ranks holding a token's experts are added element-wise; [MoE-comm] §一: the
+ * shared-expert output joins as bias).  Rank r returns, in window r, one row per token this rank sent it
+ * (its experts' already combined outputs, e.g. ep_combine over the receiver's handle), in the same order as
+ * the send window.
+ *
+ *   handle    the source rank's handle (the one its dispatch used).
+ *   partials  device bf16 [num_ranks, num_tokens, hidden]; window rank is not read; nullable when num_ranks == 1.
+ *   local     device bf16 [num_tokens, hidden], nullable: this rank's own combine output (without bias).
+ *   bias      device bf16 [num_tokens, hidden], nullable.
+ *   out       device bf16 [num_tokens, hidden] = local + sum over ranks r != rank holding the token of
+ *             partials[r][send_slot(t, r)] + bias, fp32 in that order, one RNE rounding.  Every row is written.
+ */
+ep_status_t ep_combine_reduce(ep_handle_t handle, const void* partials, int hidden, const void* local,
+                              const void* bias, void* out, void* stream);
 
 /* Free the host object of a handle (never blocks, never touches device memory).  NULL is allowed. */
 ep_status_t ep_handle_free(ep_handle_t handle);

@@ -65,6 +65,10 @@ def _load():
     lib.oracle_dispatch.argtypes = [P, I, I, I, P, P, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P]
     lib.oracle_combine.restype = None
     lib.oracle_combine.argtypes = [P, I, P, P, I, I, P, P]
+    lib.oracle_dispatch_rows.restype = I
+    lib.oracle_dispatch_rows.argtypes = [P, I, I, P, I, I, P, I, I, I, P, P, P, P, P, P, P]
+    lib.oracle_combine_reduce.restype = None
+    lib.oracle_combine_reduce.argtypes = [P, I, I, I, I, P, P, P, P]
     _lib = lib
     return lib
 
@@ -206,4 +210,40 @@ def combine(y_bits, slot, topk_weights=None, bias_bits=None):
     b = None if bias_bits is None else _c(bias_bits, np.uint16)
     out = np.empty((T, H), np.float64)
     _load().oracle_combine(_ptr(y_bits), H, _ptr(slot), _ptr(w), T, K, _ptr(b), _ptr(out))
+    return out
+
+
+def dispatch_rows(rows, scales, topk_idx_local, topk_weights, lay, num_local_experts, expert_alignment=1,
+                  zero_pad=False, recv_fill=None):
+    """Oracle receiver-side placement.  rows: uint8 [N, row_bytes]; scales: float32 [N, G] or None;
+    topk_idx_local: int64 [N, K] (local ids or -1); lay: layout(topk_idx_local, num_local_experts, 1, 0, A)."""
+    rows = _c(rows, np.uint8)
+    N, row_bytes = rows.shape
+    K = topk_idx_local.shape[1]
+    G = 0 if scales is None else scales.shape[1]
+    sc = None if scales is None else _c(scales, np.float32)
+    cap = lay["cap"]
+    fill_b, fill_s = recv_fill if recv_fill is not None else (0, 0.0)
+    out = dict(recv_x=np.full((cap, row_bytes), fill_b, np.uint8),
+               recv_scales=np.full((cap, G), fill_s, np.float32) if G else None,
+               recv_src=np.full(cap, -7, np.int32), recv_w=np.full(cap, -7.0, np.float32))
+    w = None if topk_weights is None else _c(topk_weights, np.float32)
+    rc = _load().oracle_dispatch_rows(_ptr(rows), N, row_bytes, _ptr(sc), G, K, _ptr(w), num_local_experts,
+                                      expert_alignment, int(zero_pad), _ptr(lay["cnt"]), _ptr(lay["psum"]),
+                                      _ptr(lay["slot"]), _ptr(out["recv_x"]), _ptr(out["recv_scales"]),
+                                      _ptr(out["recv_src"]), _ptr(out["recv_w"]))
+    if rc != 0:
+        raise ValueError("oracle_dispatch_rows rejected its arguments")
+    return out
+
+
+def combine_reduce(partials_bits, send_slot, rank, local_bits=None, bias_bits=None):
+    """Oracle source-side reduce in float64.  partials_bits: uint16 [R, T, H]; send_slot: int32 [T, R]."""
+    partials_bits = _c(partials_bits, np.uint16)
+    R, T, H = partials_bits.shape
+    ss = _c(send_slot, np.int32)
+    lo = None if local_bits is None else _c(local_bits, np.uint16)
+    b = None if bias_bits is None else _c(bias_bits, np.uint16)
+    out = np.empty((T, H), np.float64)
+    _load().oracle_combine_reduce(_ptr(partials_bits), T, H, R, rank, _ptr(ss), _ptr(lo), _ptr(b), _ptr(out))
     return out

@@ -298,6 +298,39 @@ int oracle_dispatch(const uint16_t* x, int T, int H, int K, const float* topk_w,
     return 0;
 }
 
+/* The receiver's copy epilogue: rows arrive destination-major (one per token sent to this rank, already in
+ * the receive format) and are placed expert-major at their expert's rows ([DeepEP->MegaMoE] §2.4: load the
+ * received row, take the row of its expert, store).  Reading: the received rows' layout is the same stable
+ * counting sort as the sender's (oracle_layout over their local expert ids with one rank), so placement is
+ * deterministic; padding rows as in oracle_dispatch. */
+int oracle_dispatch_rows(const uint8_t* rows, int N, int row_bytes, const float* scales, int G, int K,
+                         const float* topk_w, int E_local, int A, int zero_pad, const int32_t* cnt,
+                         const int32_t* psum, const int32_t* slot, uint8_t* recv_x, float* recv_scales,
+                         int32_t* recv_src, float* recv_w) {
+    if (N < 0 || row_bytes < 1 || G < 0 || K < 1 || E_local < 1 || A < 1) return -1;
+    for (int i = 0; i < N; ++i) {
+        for (int k = 0; k < K; ++k) {
+            int32_t s = slot[(int64_t)i * K + k];
+            if (s < 0) continue;
+            memcpy(recv_x + (size_t)s * row_bytes, rows + (size_t)i * row_bytes, (size_t)row_bytes);
+            if (G > 0) memcpy(recv_scales + (size_t)s * G, scales + (size_t)i * G, sizeof(float) * (size_t)G);
+            if (recv_src) recv_src[s] = i;
+            if (recv_w) recv_w[s] = topk_w ? topk_w[(int64_t)i * K + k] : 1.0f;
+        }
+    }
+    for (int j = 0; j < E_local; ++j) {
+        for (int32_t s = psum[j] + cnt[j]; s < psum[j + 1]; ++s) {
+            if (zero_pad) {
+                memset(recv_x + (size_t)s * row_bytes, 0, (size_t)row_bytes);
+                for (int g = 0; g < G; ++g) recv_scales[(size_t)s * G + g] = 0.0f;
+            }
+            if (recv_src) recv_src[s] = -1;
+            if (recv_w) recv_w[s] = 0.0f;
+        }
+    }
+    return 0;
+}
+
 /* ======================================================================================================
  * Combine
  * ====================================================================================================== */
@@ -321,6 +354,28 @@ void oracle_combine(const uint16_t* y, int H, const int32_t* slot, const float* 
                 acc += w * (double)oracle_bf16_to_f32(y[(size_t)s * H + h]);
             }
             if (bias) acc += (double)oracle_bf16_to_f32(bias[(size_t)t * H + h]);
+            out[(size_t)t * H + h] = acc;
+        }
+    }
+}
+
+/* The source rank's reduce epilogue after the combine exchange: each rank that received token t returns one
+ * row (its experts' weighted outputs for t, already summed, [DeepEP->MegaMoE] §2.3), and the source adds
+ * them element-wise ([DeepEP->MegaMoE] §2.5: reduced[j] += source[j]) together with its own experts' part and
+ * the shared-expert bias ([MoE-comm] §一).  Row j of window r belongs to the token with send_slot[t,r] = j.
+ * In double; the order of the terms does not matter at this precision for at most R + 2 terms. */
+void oracle_combine_reduce(const uint16_t* partials, int T, int H, int R, int rank, const int32_t* send_slot,
+                           const uint16_t* local, const uint16_t* bias, double* out) {
+    for (int t = 0; t < T; ++t) {
+        for (int h = 0; h < H; ++h) {
+            double acc = 0.0;
+            if (bias) acc += (double)oracle_bf16_to_f32(bias[(size_t)t * H + h]);
+            if (local) acc += (double)oracle_bf16_to_f32(local[(size_t)t * H + h]);
+            for (int r = 0; r < R; ++r) {
+                int32_t j = send_slot[(int64_t)t * R + r];
+                if (r == rank || j < 0) continue;
+                acc += (double)oracle_bf16_to_f32(partials[((size_t)r * T + j) * H + h]);
+            }
             out[(size_t)t * H + h] = acc;
         }
     }

@@ -61,10 +61,23 @@ int oracle_dispatch(const uint16_t* x, int T, int H, int K, const float* topk_w,
                     void* send_x, float* send_scales, int32_t* send_src, int64_t* send_topk_idx,
                     float* send_topk_w);
 
+/* Expert-major placement of rows that already carry their receive format (the receiver side of the copy
+ * epilogue): row_bytes bytes per row plus G fp32 scales (G may be 0).  Layout from oracle_layout over the
+ * received rows' local expert ids.  recv_src = index of the received row; recv_w = topk_w[i,k] or 1. */
+int oracle_dispatch_rows(const uint8_t* rows, int N, int row_bytes, const float* scales, int G, int K,
+                         const float* topk_w, int E_local, int A, int zero_pad, const int32_t* cnt,
+                         const int32_t* psum, const int32_t* slot, uint8_t* recv_x, float* recv_scales,
+                         int32_t* recv_src, float* recv_w);
+
 /* ---- combine ----------------------------------------------------------------------------------------- */
 /* out[t,h] = sum_k w[t,k] * y[slot[t,k],h] (+ bias[t,h]) in double; w == NULL means all weights are 1. */
 void oracle_combine(const uint16_t* y, int H, const int32_t* slot, const float* topk_w, int T, int K,
                     const uint16_t* bias, double* out);
+
+/* Source-side sum after the combine exchange: out[t,h] = bias + local + sum over ranks r != rank with
+ * send_slot[t,r] >= 0 of partials[r, send_slot[t,r], h], in double.  local and bias may be NULL. */
+void oracle_combine_reduce(const uint16_t* partials, int T, int H, int R, int rank, const int32_t* send_slot,
+                           const uint16_t* local, const uint16_t* bias, double* out);
 
 #ifdef __cplusplus
 }

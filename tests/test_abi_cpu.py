@@ -44,7 +44,8 @@ def lib():
 def test_header_declares_the_boundary():
     names = _declared()
     for n in ("ep_get_layout", "ep_dispatch", "ep_combine", "ep_handle_free", "ep_recv_capacity",
-              "ep_layout_workspace_bytes", "ep_status_string", "ep_last_error"):
+              "ep_layout_workspace_bytes", "ep_status_string", "ep_last_error", "ep_dispatch_rows",
+              "ep_combine_reduce"):
         assert n in names
 
 
