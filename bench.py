@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before the steps (counter calibration)")
     ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--no-epilogues", dest="epilogues", action="store_false",
+                    help="skip the receiver-placement / source-reduce measurement at the EP8 shapes")
     return ap.parse_args()
 
 
@@ -122,6 +124,72 @@ def cpu_baseline(inp, y_bits, cfg):
     return dict(value=round(total / med / 1e9, 3), unit="GB/s", cores=1, kind="oracle",
                 sample="full %s workload (layout + FP8 dispatch + combine), median of %d runs, %.2f s each"
                        % (cfg.name, len(times), med))
+
+
+def measure_epilogues(ep, W, dev, n):
+    """Receiver-side placement and source-side reduce at the EP8 shapes: rank 0 (experts 0..31 of 256) receiving
+    the rows of 7 other ranks of 4096 tokens each (top-8 uniform routing, FP8 rows + 56 scales, alignment 128),
+    and the reduce of 8 returned windows of 4096 x 7168 BF16 rows with the local part and a bias."""
+    import numpy as np
+    import torch
+
+    cfg = W.CONFIGS["ep8"]
+    T, H, K, E, R, A = cfg.num_tokens, cfg.hidden, cfg.num_topk, cfg.num_experts, cfg.num_ranks, cfg.expert_alignment
+    El, G = E // R, H // 128
+    gen = torch.Generator().manual_seed(77)
+    tk = torch.full((R * T, K), -1, dtype=torch.int64)
+    tw = torch.zeros((R * T, K), dtype=torch.float32)
+    n_valid = 0
+    for s in range(1, R):
+        idx = W.route_uniform_distinct(T, E, K, gen)
+        w = W.softmax_weights(torch.randn(T, K, generator=gen))
+        mine = (idx < El).any(dim=1)
+        sel = torch.nonzero(mine).flatten()
+        n = sel.numel()
+        loc = torch.where(idx[sel] < El, idx[sel], torch.full_like(idx[sel], -1))
+        tk[s * T:s * T + n] = loc
+        tw[s * T:s * T + n] = w[sel]
+        n_valid += n
+    rows = torch.randint(0, 0x7E, (R * T, H), generator=gen, dtype=torch.uint8).to(dev)
+    sc = torch.rand(R * T, G, generator=gen).to(dev)
+    tk, tw = tk.to(dev), tw.to(dev)
+    hr, lr = ep.ep_get_layout(tk, El, 1, 0, A)
+    out = ep.ep_dispatch_rows(hr, rows, sc, tw, do_zero_padding=False)
+    torch.cuda.synchronize()
+    cnt = lr["num_tokens_per_expert"].cpu().numpy()
+    V = int(cnt.sum())
+    P = int(lr["psum_num_recv_tokens_per_expert"][-1].item()) - V
+    row_b = H + 4 * G
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(2.4e9 * 0.02))
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    t_rows = timed(lambda: ep.ep_dispatch_rows(hr, rows, sc, tw, do_zero_padding=False, out=out))
+    b_rows = n_valid * row_b + R * T * K * 12 + V * (row_b + 8) + P * 8
+
+    inp = W.make_inputs("ep8")
+    h0, l0 = ep.ep_get_layout(inp["topk_idx"].to(dev), E, R, 0, A)
+    parts = W.random_expert_outputs(R * T, H, seed=3, device=dev).view(R, T, H)
+    local = W.random_expert_outputs(T, H, seed=4, device=dev)
+    bias = W.random_expert_outputs(T, H, seed=5, device=dev)
+    red = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    t_red = timed(lambda: ep.ep_combine_reduce(h0, parts, local, bias, out=red))
+    ntr = l0["num_tokens_per_rank"].cpu().numpy()
+    n_part = int(sum(ntr[r] for r in range(1, R)))
+    b_red = n_part * 2 * H + 3 * T * 2 * H + T * R * 4
+    return dict(
+        dispatch_rows=dict(us=round(t_rows * 1e3, 2), bytes=b_rows, GBps=round(b_rows / (t_rows * 1e-3) / 1e9, 1),
+                           received_rows=n_valid, placed_rows=V),
+        combine_reduce=dict(us=round(t_red * 1e3, 2), bytes=b_red, GBps=round(b_red / (t_red * 1e-3) / 1e9, 1),
+                            partial_rows=n_part))
 
 
 def main():
@@ -282,6 +350,8 @@ def main():
                     frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=load_traffic(dom_kernel),
                     algorithmic_bytes=bm[dom], avg_launch_us=round(avg[dom] * 1e3, 2))
 
+    epi = measure_epilogues(ep, W, dev, args.steps) if args.epilogues else None
+
     cpu = None
     if not args.no_cpu_baseline:
         y_bits = y.cpu().view(torch.int16).numpy().view(np.uint16)
@@ -306,6 +376,7 @@ def main():
         kernels=kern,
         roofline=roofline,
         cpu_baseline=cpu,
+        epilogues=epi,
     )
     print(json.dumps(line), flush=True)
 
