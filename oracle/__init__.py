@@ -62,7 +62,8 @@ def _load():
     lib.oracle_quantize_row.restype = None
     lib.oracle_quantize_row.argtypes = [P, I, P, P]
     lib.oracle_dispatch.restype = I
-    lib.oracle_dispatch.argtypes = [P, I, I, I, P, P, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P]
+    lib.oracle_dispatch.argtypes = [P, I, I, I, P, P, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P,
+                                    P]
     lib.oracle_combine.restype = None
     lib.oracle_combine.argtypes = [P, I, P, P, I, I, P, P]
     lib.oracle_dispatch_rows.restype = I
@@ -152,28 +153,31 @@ def quantize_row(x_bits):
 
 
 def dispatch(x_bits, topk_idx, topk_weights, lay, num_experts, num_ranks=1, rank=0, expert_alignment=1,
-             fp8=False, zero_pad=False, recv_fill=None, want_meta=True, want_send_meta=True):
+             fp8=False, zero_pad=False, recv_fill=None, want_meta=True, want_send_meta=True, do_expand=True):
     """Oracle dispatch.  x_bits: uint16 [T,H] (BF16 bits).  lay: the dict from layout().
 
     recv_fill: optional (data_byte, scale_value) canary used to initialise the receive buffers, so that rows
-    the dispatch must leave untouched can be checked.  Returns a dict of numpy arrays."""
+    the dispatch must leave untouched can be checked.  do_expand=False gives the token-major receive layout
+    (rows = T, recv_w and recv_topk_idx [T, K]).  Returns a dict of numpy arrays."""
     x_bits = _c(x_bits, np.uint16)
     topk_idx = _c(topk_idx, np.int64)
     T, H = x_bits.shape
     K = topk_idx.shape[1]
     R = num_ranks
-    cap = lay["cap"]
+    rows = lay["cap"] if do_expand else T
     G = H // 128 if fp8 else 0
     fill_b, fill_s = recv_fill if recv_fill is not None else (0, 0.0)
     if fp8:
-        recv_x = np.full((cap, H), fill_b, np.uint8)
-        recv_scales = np.full((cap, G), fill_s, np.float32)
+        recv_x = np.full((rows, H), fill_b, np.uint8)
+        recv_scales = np.full((rows, G), fill_s, np.float32)
     else:
-        recv_x = np.full((cap, H * 2), fill_b, np.uint8)
+        recv_x = np.full((rows, H * 2), fill_b, np.uint8)
         recv_scales = None
     out = dict(recv_x=recv_x, recv_scales=recv_scales)
-    out["recv_src"] = np.full(cap, -7, np.int32) if want_meta else None
-    out["recv_w"] = np.full(cap, -7.0, np.float32) if want_meta else None
+    out["recv_src"] = np.full(rows, -7, np.int32) if want_meta else None
+    out["recv_w"] = (np.full(rows, -7.0, np.float32) if do_expand else np.full((T, K), -7.0, np.float32)) \
+        if want_meta else None
+    out["recv_topk_idx"] = np.full((T, K), -7, np.int64) if (want_meta and not do_expand) else None
     if R > 1:
         rowb = H if fp8 else 2 * H
         out["send_x"] = np.full((R, T, rowb), fill_b, np.uint8)
@@ -187,10 +191,10 @@ def dispatch(x_bits, topk_idx, topk_weights, lay, num_experts, num_ranks=1, rank
     w = None if topk_weights is None else _c(topk_weights, np.float32)
     rc = _load().oracle_dispatch(
         _ptr(x_bits), T, H, K, _ptr(w), _ptr(topk_idx), num_experts, R, rank, expert_alignment, int(fp8),
-        int(zero_pad), _ptr(lay["cnt"]), _ptr(lay["psum"]), _ptr(lay["slot"]), _ptr(lay["send_slot"]),
+        int(zero_pad), int(do_expand), _ptr(lay["cnt"]), _ptr(lay["psum"]), _ptr(lay["slot"]), _ptr(lay["send_slot"]),
         _ptr(out["recv_x"]), _ptr(out["recv_scales"]), _ptr(out["recv_src"]), _ptr(out["recv_w"]),
-        _ptr(out["send_x"]), _ptr(out["send_scales"]), _ptr(out["send_src"]), _ptr(out["send_topk_idx"]),
-        _ptr(out["send_topk_w"]))
+        _ptr(out["recv_topk_idx"]), _ptr(out["send_x"]), _ptr(out["send_scales"]), _ptr(out["send_src"]),
+        _ptr(out["send_topk_idx"]), _ptr(out["send_topk_w"]))
     if rc != 0:
         raise ValueError("oracle_dispatch rejected its arguments")
     if not fp8:
@@ -211,6 +215,13 @@ def combine(y_bits, slot, topk_weights=None, bias_bits=None):
     out = np.empty((T, H), np.float64)
     _load().oracle_combine(_ptr(y_bits), H, _ptr(slot), _ptr(w), T, K, _ptr(b), _ptr(out))
     return out
+
+
+def combine_tokens(y_bits, send_slot, rank, bias_bits=None):
+    """Oracle combine for the token-major layout: out[t] = y[send_slot[t, rank]] (+ bias), i.e. the combine
+    definition with one slot per token and unit weight.  Returns float64 [T, H]."""
+    col = np.ascontiguousarray(np.asarray(send_slot, np.int32)[:, rank:rank + 1])
+    return combine(y_bits, col, None, bias_bits)
 
 
 def dispatch_rows(rows, scales, topk_idx_local, topk_weights, lay, num_local_experts, expert_alignment=1,

@@ -126,7 +126,9 @@ int64_t oracle_recv_capacity(int num_tokens, int num_topk, int num_local_experts
  *    reading: an empty expert takes no rows;
  *  - the slot of every entry.  Reading: rows of one expert are in ascending flat index t*K+k (a stable
  *    counting sort; the atomics of the copy epilogue allow any order, this fixes one);
- *  - reading: entries equal to -1 are unused; entries < -1 or >= E are dropped and counted. */
+ *  - reading: entries equal to -1 are unused; entries < -1 or >= E are dropped and counted;
+ *  - per-rank token rows: the rank of t among the tokens with an expert on r, dense in ascending t (send
+ *    windows for other ranks; the token-major receive rows for this rank). */
 int oracle_layout(const int64_t* topk_idx, int T, int K, int E, int R, int rank, int A,
                   int32_t* cnt, int32_t* ntok_rank, uint8_t* in_rank, int32_t* psum,
                   int32_t* slot, int32_t* row_src, int64_t cap, int32_t* send_slot, int32_t* num_invalid) {
@@ -182,12 +184,13 @@ int oracle_layout(const int64_t* topk_idx, int T, int K, int E, int R, int rank,
     }
     free(cursor);
 
-    /* step 5: per-destination send slots, dense from 0 in ascending token order */
+    /* step 5: per-rank token rows, dense from 0 in ascending token order: for r != rank the row of t in the
+     * send window of rank r; for r == rank its row in the token-major receive layout (do_expand off) */
     for (int r = 0; r < R; ++r) {
         int32_t j = 0;
         for (int t = 0; t < T; ++t) {
             int32_t s = -1;
-            if (r != rank && in_rank[(int64_t)t * R + r]) s = j++;
+            if (in_rank[(int64_t)t * R + r]) s = j++;
             send_slot[(int64_t)t * R + r] = s;
         }
     }
@@ -222,21 +225,24 @@ void oracle_quantize_row(const uint16_t* x, int H, uint8_t* q, float* scales) {
     }
 }
 
-/* Expert-major dispatch of this rank's tokens (do_expand), following the dispatch and copy-epilogue
- * kernels of [DeepEP->MegaMoE] §2.2 and §2.4 and the dispatch arguments of [MoE-comm] §一:
+/* Dispatch of this rank's tokens, following the dispatch and copy-epilogue kernels of [DeepEP->MegaMoE] §2.2
+ * and §2.4 and the dispatch arguments of [MoE-comm] §一:
  *  - each token row is read once and, when FP8, quantised once ([DeepEP-hotdry] key techniques);
- *  - the row (and its scales) is written to every slot of the token;  recv_src = t and recv_w = w[t,k]
- *    per row (the source-token metadata of the received rows, [DeepEP->MegaMoE] §2.3);
- *  - padding rows [psum[j] + cnt, psum[j+1]): with do_zero_padding the data bytes and scales are zero;
- *    reading: without it they are left untouched; their recv_src is -1 and recv_w is 0 either way;
- *  - rows at or past psum[El] are never written;
+ *  - do_expand: the row (and its scales) is written to every expert-major slot of the token; recv_src = t
+ *    and recv_w = w[t,k] per row (the source-token metadata of the received rows, [DeepEP->MegaMoE] §2.3);
+ *    padding rows [psum[j] + cnt, psum[j+1]): with do_zero_padding the data bytes and scales are zero;
+ *    reading: without it they are left untouched; their recv_src is -1 and recv_w is 0 either way; rows at
+ *    or past psum[El] are never written;
+ *  - reading of do_expand off: one row per token with an expert on this rank, in ascending token order
+ *    (row send_slot[t, rank]), no padding; recv_src[j] = t, recv_topk_idx[j, k] = the local expert id of
+ *    entry k or -1, recv_w[j, k] = w[t, k];
  *  - send windows, R > 1: for r != rank, window r row send_slot[t,r] gets the same bytes and scales, the
  *    source token, the destination-local expert ids (e - r*E/R, or -1 when r does not own e) and the
  *    weights ([DeepEP->MegaMoE] §2.2: store to the send buffer before the transfer). */
 int oracle_dispatch(const uint16_t* x, int T, int H, int K, const float* topk_w, const int64_t* topk_idx,
-                    int E, int R, int rank, int A, int fp8, int zero_pad,
+                    int E, int R, int rank, int A, int fp8, int zero_pad, int do_expand,
                     const int32_t* cnt, const int32_t* psum, const int32_t* slot, const int32_t* send_slot,
-                    void* recv_x, float* recv_scales, int32_t* recv_src, float* recv_w,
+                    void* recv_x, float* recv_scales, int32_t* recv_src, float* recv_w, int64_t* recv_topk_idx,
                     void* send_x, float* send_scales, int32_t* send_src, int64_t* send_topk_idx,
                     float* send_topk_w) {
     if (T < 0 || H < 1 || K < 1 || E % R != 0 || A < 1) return -1;
@@ -255,20 +261,36 @@ int oracle_dispatch(const uint16_t* x, int T, int H, int K, const float* topk_w,
         if (fp8) oracle_quantize_row(x + (size_t)t * H, H, row, sc);
         else memcpy(row, x + (size_t)t * H, row_bytes);
 
-        /* local copies */
-        for (int k = 0; k < K; ++k) {
-            int32_t s = slot[(int64_t)t * K + k];
-            if (s < 0) continue;
-            memcpy(rx + (size_t)s * row_bytes, row, row_bytes);
-            if (fp8) memcpy(recv_scales + (size_t)s * G, sc, sizeof(float) * (size_t)G);
-            if (recv_src) recv_src[s] = t;
-            if (recv_w) recv_w[s] = topk_w ? topk_w[(int64_t)t * K + k] : 1.0f;
+        if (do_expand) {
+            /* expert-major copies */
+            for (int k = 0; k < K; ++k) {
+                int32_t s = slot[(int64_t)t * K + k];
+                if (s < 0) continue;
+                memcpy(rx + (size_t)s * row_bytes, row, row_bytes);
+                if (fp8) memcpy(recv_scales + (size_t)s * G, sc, sizeof(float) * (size_t)G);
+                if (recv_src) recv_src[s] = t;
+                if (recv_w) recv_w[s] = topk_w ? topk_w[(int64_t)t * K + k] : 1.0f;
+            }
+        } else {
+            /* token-major row */
+            int32_t j = send_slot[(int64_t)t * R + rank];
+            if (j >= 0) {
+                memcpy(rx + (size_t)j * row_bytes, row, row_bytes);
+                if (fp8) memcpy(recv_scales + (size_t)j * G, sc, sizeof(float) * (size_t)G);
+                if (recv_src) recv_src[j] = t;
+                for (int k = 0; k < K; ++k) {
+                    int64_t e = topk_idx[(int64_t)t * K + k];
+                    int owned = (e >= (int64_t)lo && e < (int64_t)lo + epr);
+                    if (recv_topk_idx) recv_topk_idx[(size_t)j * K + k] = owned ? e - lo : -1;
+                    if (recv_w) recv_w[(size_t)j * K + k] = topk_w ? topk_w[(int64_t)t * K + k] : 1.0f;
+                }
+            }
         }
 
         /* send windows */
         for (int r = 0; r < R; ++r) {
             int32_t j = send_slot[(int64_t)t * R + r];
-            if (j < 0) continue;
+            if (r == rank || j < 0) continue;
             size_t wrow = (size_t)r * T + j;
             memcpy(sx + wrow * row_bytes, row, row_bytes);
             if (fp8) memcpy(send_scales + wrow * G, sc, sizeof(float) * (size_t)G);
@@ -282,8 +304,8 @@ int oracle_dispatch(const uint16_t* x, int T, int H, int K, const float* topk_w,
         }
     }
 
-    /* padding rows of each local expert */
-    for (int j = 0; j < epr; ++j) {
+    /* padding rows of each local expert (expert-major layout only) */
+    for (int j = 0; do_expand && j < epr; ++j) {
         for (int32_t s = psum[j] + cnt[lo + j]; s < psum[j + 1]; ++s) {
             if (zero_pad) {
                 memset(rx + (size_t)s * row_bytes, 0, row_bytes);
@@ -362,7 +384,8 @@ void oracle_combine(const uint16_t* y, int H, const int32_t* slot, const float* 
 /* The source rank's reduce epilogue after the combine exchange: each rank that received token t returns one
  * row (its experts' weighted outputs for t, already summed, [DeepEP->MegaMoE] §2.3), and the source adds
  * them element-wise ([DeepEP->MegaMoE] §2.5: reduced[j] += source[j]) together with its own experts' part and
- * the shared-expert bias ([MoE-comm] §一).  Row j of window r belongs to the token with send_slot[t,r] = j.
+ * the shared-expert bias ([MoE-comm] §一).  Row j of window r belongs to the token with send_slot[t,r] = j
+ * (r != rank).
  * In double; the order of the terms does not matter at this precision for at most R + 2 terms. */
 void oracle_combine_reduce(const uint16_t* partials, int T, int H, int R, int rank, const int32_t* send_slot,
                            const uint16_t* local, const uint16_t* bias, double* out) {

@@ -41,7 +41,8 @@ int64_t oracle_recv_capacity(int num_tokens, int num_topk, int num_local_experts
  *   psum[El+1]        aligned exclusive starts of this rank's local experts; psum[El] = rows used
  *   slot[T*K]         row of entry (t,k) in the expert-major buffer, -1 when the expert is not local
  *   row_src[cap]      source token of each row, -1 for padding rows and for rows past psum[El]
- *   send_slot[T*R]    rank of t among the tokens in rank r (r != rank), else -1
+ *   send_slot[T*R]    rank of t among the tokens in rank r (send window row for r != rank; token-major
+ *                     receive row for r == rank), else -1
  *   num_invalid[1]    entries < -1 or >= E, which are dropped                                          */
 int oracle_layout(const int64_t* topk_idx, int T, int K, int E, int R, int rank, int A,
                   int32_t* cnt, int32_t* ntok_rank, uint8_t* in_rank, int32_t* psum,
@@ -51,13 +52,14 @@ int oracle_layout(const int64_t* topk_idx, int T, int K, int E, int R, int rank,
 /* Per-token per-128-channel FP8 quantisation of one BF16 row (H % 128 == 0). */
 void oracle_quantize_row(const uint16_t* x, int H, uint8_t* q, float* scales);
 
-/* fp8 != 0: recv_x is uint8 [cap,H], recv_scales float [cap,H/128]; else recv_x is uint16 (bf16) [cap,H].
- * Optional outputs may be NULL.  Send windows (R > 1): send_x [R,T,H], send_scales [R,T,H/128],
- * send_src [R,T], send_topk_idx int64 [R,T,K], send_topk_w [R,T,K].                                  */
+/* fp8 != 0: recv_x is uint8 [rows,H], recv_scales float [rows,H/128]; else recv_x is uint16 (bf16) [rows,H].
+ * do_expand: rows = cap, recv_src [cap], recv_w [cap]; else rows = T, recv_src [T], recv_w [T,K],
+ * recv_topk_idx int64 [T,K].  Optional outputs may be NULL.  Send windows (R > 1): send_x [R,T,H],
+ * send_scales [R,T,H/128], send_src [R,T], send_topk_idx int64 [R,T,K], send_topk_w [R,T,K].          */
 int oracle_dispatch(const uint16_t* x, int T, int H, int K, const float* topk_w, const int64_t* topk_idx,
-                    int E, int R, int rank, int A, int fp8, int zero_pad,
+                    int E, int R, int rank, int A, int fp8, int zero_pad, int do_expand,
                     const int32_t* cnt, const int32_t* psum, const int32_t* slot, const int32_t* send_slot,
-                    void* recv_x, float* recv_scales, int32_t* recv_src, float* recv_w,
+                    void* recv_x, float* recv_scales, int32_t* recv_src, float* recv_w, int64_t* recv_topk_idx,
                     void* send_x, float* send_scales, int32_t* send_src, int64_t* send_topk_idx,
                     float* send_topk_w);
 

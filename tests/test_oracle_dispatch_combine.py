@@ -189,3 +189,60 @@ def test_token_without_local_expert_gets_bias():
     bias = np.full((2, H), 0x4000, np.uint16)                    # 2.0
     out = O.combine(y, lay["slot"], np.array([[0.25, 0.75], [0.5, 0.5]], np.float32), bias)
     assert (out[0] == 3.0).all() and (out[1] == 2.0).all()
+
+
+@pytest.mark.parametrize("fp8,R,rank", [(False, 1, 0), (True, 4, 2), (False, 3, 0)])
+def test_token_major_dispatch(fp8, R, rank):
+    """do_expand off: one row per token with a local expert, ascending token order (a gather over the tokens
+    in this rank, brute force), local expert ids or -1 per entry, the token's weights; send windows are
+    the same bytes as under the expert-major dispatch."""
+    gen = torch.Generator().manual_seed(40 + R)
+    T, K, E, H, A = 57, 3, 12, 256, 4
+    idx = W.route_uniform_distinct(T, E, K, gen).numpy()
+    idx[7, :] = -1                                   # a token with no expert at all
+    w = W.softmax_weights(torch.randn(T, K, generator=gen)).numpy()
+    x = W.bf16_bits(W.normal_bf16((T, H), gen))
+    lay = O.layout(idx, E, R, rank, A)
+    d = O.dispatch(x, idx, w, lay, E, R, rank, A, fp8=fp8, recv_fill=(0xA5, -3.0), do_expand=False)
+    e = O.dispatch(x, idx, w, lay, E, R, rank, A, fp8=fp8, recv_fill=(0xA5, -3.0), do_expand=True)
+    epr, lo = E // R, rank * (E // R)
+    toks = [t for t in range(T) if any(lo <= v < lo + epr for v in idx[t])]
+    assert len(toks) == int(lay["ntok_rank"][rank])
+    for j, t in enumerate(toks):
+        if fp8:
+            q, s = O.quantize_row(x[t])
+            assert np.array_equal(d["recv_x"][j], q) and np.array_equal(d["recv_scales"][j], s)
+        else:
+            assert np.array_equal(d["recv_x"][j], x[t])
+        assert d["recv_src"][j] == t
+        assert d["recv_topk_idx"][j].tolist() == [int(v) - lo if lo <= v < lo + epr else -1 for v in idx[t]]
+        assert np.array_equal(d["recv_w"][j], w[t])
+        # the same bytes as every expert-major copy of the token
+        for s_ in lay["slot"][t]:
+            if s_ >= 0:
+                assert np.array_equal(e["recv_x"][s_], d["recv_x"][j])
+    n = len(toks)
+    assert (d["recv_x"][n:].view(np.uint8) == 0xA5).all()
+    assert (d["recv_src"][n:] == -7).all() and (d["recv_topk_idx"][n:] == -7).all()
+    if R > 1:
+        for k in ("send_x", "send_scales", "send_src", "send_topk_idx", "send_topk_w"):
+            if e[k] is not None:
+                assert np.array_equal(d[k], e[k]), k
+        assert (d["send_x"][rank].view(np.uint8) == 0xA5).all()      # no window towards this rank
+
+
+def test_combine_tokens_closed_form():
+    """Token-major combine: row j of y holds the value j + 1 (exact in BF16 for j < 256), so each token's
+    output names the row it gathered; tokens without a local expert get exactly the bias."""
+    idx = np.array([[0, 5], [4, 5], [1, 2], [6, 7], [3, 4]], np.int64)
+    R, rank = 2, 0
+    lay = O.layout(idx, num_experts=8, num_ranks=R, rank=rank, expert_alignment=1)
+    H = 16
+    y = O.f64_to_bf16(np.repeat(np.arange(1, 6, dtype=np.float64)[:, None], H, axis=1))
+    bias = np.full((5, H), 0x3F00, np.uint16)        # 0.5
+    out = O.combine_tokens(y, lay["send_slot"], rank, bias)
+    # tokens 0, 2, 4 hold experts of rank 0 (0..3): rows 0, 1, 2; tokens 1 and 3 none
+    assert out[:, 0].tolist() == [1.5, 0.5, 2.5, 0.5, 3.5]
+    assert (out == out[:, :1]).all()
+    out_nb = O.combine_tokens(y, lay["send_slot"], rank)
+    assert out_nb[:, 0].tolist() == [1.0, 0.0, 2.0, 0.0, 3.0]

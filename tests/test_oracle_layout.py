@@ -75,12 +75,9 @@ def _brute_layout_checks(idx, E, R, rank, A, lay):
     mask = np.ones(lay["cap"], bool)
     mask[slot[order]] = False
     assert (rs[mask] == -1).all()
-    # send slots: dense, ascending token order, only for other ranks
+    # per-rank token rows: dense, ascending token order (own rank: token-major receive rows)
     for r in range(R):
         col = lay["send_slot"][:, r]
-        if r == rank:
-            assert (col == -1).all()
-            continue
         toks = np.nonzero(lay["in_rank"][:, r])[0]
         assert np.array_equal(col[toks], np.arange(len(toks)))
         assert (np.delete(col, toks) == -1).all()
