@@ -1,8 +1,8 @@
 """Python binding of libep_mi355x.so (include/ep.h): MoE expert-parallel layout, dispatch and combine on one
 MI355X (gfx950) GPU.
 
-The functions keep the C names (ep_get_layout, ep_dispatch, ep_combine, ep_handle_free, ep_recv_capacity,
-ep_layout_workspace_bytes).  They only marshal arguments: tensors become device pointers, the stream is
+The functions keep the C names (ep_get_layout, ep_dispatch, ep_combine, ep_combine_tokens, ep_dispatch_rows,
+ep_combine_reduce, ep_handle_free, ep_recv_capacity, ep_layout_workspace_bytes).  They only marshal arguments: tensors become device pointers, the stream is
 torch's current HIP stream, and output tensors are allocated by torch when the caller does not pass them.
 Every step of the path runs in the HIP kernels of the library; there is no other implementation, and if
 the library is not built or cannot be loaded the import of this binding fails.
@@ -33,7 +33,8 @@ class EPError(RuntimeError):
 class _DispatchOut(ctypes.Structure):
     _fields_ = [
         ("recv_x", ctypes.c_void_p), ("recv_x_scales", ctypes.c_void_p), ("recv_src_idx", ctypes.c_void_p),
-        ("recv_topk_weights", ctypes.c_void_p), ("recv_capacity", ctypes.c_int64),
+        ("recv_topk_weights", ctypes.c_void_p), ("recv_topk_idx", ctypes.c_void_p),
+        ("recv_capacity", ctypes.c_int64),
         ("send_x", ctypes.c_void_p), ("send_x_scales", ctypes.c_void_p), ("send_src_idx", ctypes.c_void_p),
         ("send_topk_idx", ctypes.c_void_p), ("send_topk_weights", ctypes.c_void_p),
     ]
@@ -67,6 +68,8 @@ def _load_library():
     lib.ep_dispatch_rows.argtypes = [P, P, I, P, I, P, I, ctypes.POINTER(_DispatchOut), P]
     lib.ep_combine_reduce.restype = I
     lib.ep_combine_reduce.argtypes = [P, P, I, P, P, P, P]
+    lib.ep_combine_tokens.restype = I
+    lib.ep_combine_tokens.argtypes = [P, P, I, I64, P, P, P]
     return lib
 
 
@@ -185,11 +188,15 @@ def ep_get_layout(topk_idx, num_experts, num_ranks=1, rank=0, expert_alignment=1
 
 
 def alloc_dispatch_outputs(handle: Handle, hidden: int, fp8: bool, want_meta=True, want_send_meta=True,
-                           device=None, recv_capacity=None):
-    """Allocate (uninitialised) dispatch output tensors for `handle`."""
+                           device=None, recv_capacity=None, do_expand=True):
+    """Allocate (uninitialised) dispatch output tensors for `handle` (token-major shapes when do_expand is
+    False: num_tokens rows, recv_topk_weights and recv_topk_idx [T, K])."""
     dev = device if device is not None else handle.topk_idx.device
-    cap = handle.recv_capacity if recv_capacity is None else recv_capacity
     T, K, R = handle.num_tokens, handle.num_topk, handle.num_ranks
+    if recv_capacity is not None:
+        cap = recv_capacity
+    else:
+        cap = handle.recv_capacity if do_expand else T
     G = hidden // 128
     o = {}
     if fp8:
@@ -199,7 +206,9 @@ def alloc_dispatch_outputs(handle: Handle, hidden: int, fp8: bool, want_meta=Tru
         o["recv_x"] = torch.empty((cap, hidden), dtype=torch.bfloat16, device=dev)
         o["recv_x_scales"] = None
     o["recv_src_idx"] = torch.empty(cap, dtype=torch.int32, device=dev) if want_meta else None
-    o["recv_topk_weights"] = torch.empty(cap, dtype=torch.float32, device=dev) if want_meta else None
+    wshape = cap if do_expand else (T, K)
+    o["recv_topk_weights"] = torch.empty(wshape, dtype=torch.float32, device=dev) if want_meta else None
+    o["recv_topk_idx"] = torch.empty((T, K), dtype=torch.int64, device=dev) if (want_meta and not do_expand) else None
     if R > 1:
         o["send_x"] = torch.empty((R, T, hidden), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
         o["send_x_scales"] = torch.empty((R, T, G), dtype=torch.float32, device=dev) if fp8 else None
@@ -223,13 +232,15 @@ def ep_dispatch(handle: Handle, x, topk_weights=None, fp8=True, do_expand=True, 
     if topk_weights is not None:
         _need(topk_weights, torch.float32, "topk_weights", shape=(handle.num_tokens, handle.num_topk))
     if out is None:
-        out = alloc_dispatch_outputs(handle, H, fp8, want_meta, want_send_meta, device=x.device)
+        out = alloc_dispatch_outputs(handle, H, fp8, want_meta, want_send_meta, device=x.device,
+                                     do_expand=do_expand)
     cap = out["recv_x"].shape[0]
     s = _DispatchOut(
         recv_x=out["recv_x"].data_ptr(),
         recv_x_scales=out["recv_x_scales"].data_ptr() if out.get("recv_x_scales") is not None else None,
         recv_src_idx=out["recv_src_idx"].data_ptr() if out.get("recv_src_idx") is not None else None,
         recv_topk_weights=out["recv_topk_weights"].data_ptr() if out.get("recv_topk_weights") is not None else None,
+        recv_topk_idx=out["recv_topk_idx"].data_ptr() if out.get("recv_topk_idx") is not None else None,
         recv_capacity=cap,
         send_x=out["send_x"].data_ptr() if out.get("send_x") is not None else None,
         send_x_scales=out["send_x_scales"].data_ptr() if out.get("send_x_scales") is not None else None,
@@ -259,6 +270,25 @@ def ep_combine(handle: Handle, y, topk_weights=None, bias=None, out=None, stream
         _need(out, torch.bfloat16, "out", shape=(T, H))
     _check(_lib.ep_combine(handle.ptr, _ptr(y), H, y.shape[0], _ptr(topk_weights), _ptr(bias), _ptr(out),
                            _stream(stream)), "ep_combine")
+    return out
+
+
+def ep_combine_tokens(handle: Handle, y, bias=None, out=None, stream=None):
+    """Combine for the token-major rows (dispatch with do_expand=False): out[t] = y[row of t] + bias, where
+    y (bf16 [>= T, H]) holds one row per token of this rank in dispatch order.  Returns out [T, H] bf16."""
+    _need(y, torch.bfloat16, "y")
+    if y.dim() != 2:
+        raise ValueError("y must be [rows, hidden]")
+    H = y.shape[1]
+    T = handle.num_tokens
+    if bias is not None:
+        _need(bias, torch.bfloat16, "bias", shape=(T, H))
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    else:
+        _need(out, torch.bfloat16, "out", shape=(T, H))
+    _check(_lib.ep_combine_tokens(handle.ptr, _ptr(y), H, y.shape[0], _ptr(bias), _ptr(out), _stream(stream)),
+           "ep_combine_tokens")
     return out
 
 
@@ -321,7 +351,7 @@ def ep_handle_free(handle: Handle):
     handle.free()
 
 
-__all__ = ["ep_get_layout", "ep_dispatch", "ep_combine", "ep_handle_free", "ep_recv_capacity", "ep_dispatch_rows",
-           "ep_combine_reduce",
+__all__ = ["ep_get_layout", "ep_dispatch", "ep_combine", "ep_combine_tokens", "ep_handle_free", "ep_recv_capacity",
+           "ep_dispatch_rows", "ep_combine_reduce",
            "ep_layout_workspace_bytes", "alloc_dispatch_outputs", "Handle", "EPError", "LIB_PATH",
            "hip_runtimes_loaded"]

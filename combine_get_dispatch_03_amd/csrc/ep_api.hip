@@ -61,7 +61,7 @@ Workspace carve_workspace(void* base, int T, int K, int E, int R, int A) {
     };
     const size_t o_hist = take(sizeof(int32_t) * (size_t)ntiles * (size_t)(E + R + 1));
     const size_t o_slot = take(sizeof(int32_t) * (size_t)T * K);
-    const size_t o_send = take(R > 1 ? sizeof(int32_t) * (size_t)T * R : 0);
+    const size_t o_send = take(sizeof(int32_t) * (size_t)T * R);
     const size_t o_cnt = take(sizeof(int32_t) * (size_t)El);
     const size_t o_psum = take(sizeof(int32_t) * (size_t)(El + 1));
     const size_t o_pad = take(sizeof(int32_t) * (size_t)El * (size_t)(A - 1));
@@ -71,7 +71,7 @@ Workspace carve_workspace(void* base, int T, int K, int E, int R, int A) {
     auto at = [&](size_t o) { return b ? reinterpret_cast<int32_t*>(b + o) : nullptr; };
     w.tile_hist = at(o_hist);
     w.slot = at(o_slot);
-    w.send_slot = R > 1 ? at(o_send) : nullptr;
+    w.send_slot = at(o_send);
     w.cnt_local = at(o_cnt);
     w.psum = at(o_psum);
     w.pad_rows = A > 1 ? at(o_pad) : nullptr;
@@ -162,7 +162,6 @@ ep_status_t ep_dispatch(ep_handle_t handle, const void* x, int hidden, const flo
     g_last_error[0] = '\0';
     const Handle* h = check_handle(handle);
     if (h == nullptr) return fail(EP_ERR_INVALID_ARG, "invalid handle");
-    if (do_expand == 0) return fail(EP_ERR_UNSUPPORTED, "do_expand = 0 (token-major receive layout) is not implemented");
     if (recv_dtype != EP_DTYPE_BF16 && recv_dtype != EP_DTYPE_FP8_E4M3)
         return fail(EP_ERR_INVALID_ARG, "recv_dtype must be EP_DTYPE_BF16 or EP_DTYPE_FP8_E4M3");
     const bool fp8 = recv_dtype == EP_DTYPE_FP8_E4M3;
@@ -174,9 +173,10 @@ ep_status_t ep_dispatch(ep_handle_t handle, const void* x, int hidden, const flo
         if (x == nullptr || !aligned16(x)) return fail(EP_ERR_INVALID_ARG, "x must be non-NULL and 16-byte aligned");
         if (out->recv_x == nullptr || !aligned16(out->recv_x))
             return fail(EP_ERR_INVALID_ARG, "recv_x must be non-NULL and 16-byte aligned");
-        if (out->recv_capacity < h->cap)
+        const int64_t need = do_expand ? h->cap : (int64_t)h->T;
+        if (out->recv_capacity < need)
             return fail(EP_ERR_INVALID_ARG, "recv_capacity %lld < required %lld", (long long)out->recv_capacity,
-                        (long long)h->cap);
+                        (long long)need);
         if (fp8 && out->recv_x_scales == nullptr) return fail(EP_ERR_INVALID_ARG, "FP8 needs recv_x_scales");
         if (h->R > 1) {
             if (out->send_x == nullptr || !aligned16(out->send_x))
@@ -194,8 +194,10 @@ ep_status_t ep_dispatch(ep_handle_t handle, const void* x, int hidden, const flo
     a.topk_weights = topk_weights;
     a.hidden = hidden;
     a.zero_pad = do_zero_padding != 0;
+    a.expand = do_expand != 0;
     a.out = *out;
     if (!fp8) a.out.recv_x_scales = nullptr;
+    if (a.expand) a.out.recv_topk_idx = nullptr;
     const hipError_t err = launch_dispatch(*h, a, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return hip_fail(err, "dispatch launch");
     return EP_OK;
@@ -232,7 +234,9 @@ ep_status_t ep_dispatch_rows(ep_handle_t handle, const void* rows, int row_bytes
     a.topk_weights = topk_weights;
     a.hidden = 0;
     a.zero_pad = do_zero_padding != 0;
+    a.expand = true;
     a.out = *out;
+    a.out.recv_topk_idx = nullptr;
     if (num_scales == 0) a.out.recv_x_scales = nullptr;
     const hipError_t err = launch_dispatch(*h, a, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return hip_fail(err, "dispatch_rows launch");
@@ -284,8 +288,35 @@ ep_status_t ep_combine(ep_handle_t handle, const void* y, int hidden, int64_t y_
     a.bias = bias;
     a.out = out;
     a.hidden = hidden;
+    a.tokens = false;
     const hipError_t err = launch_combine(*h, a, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return hip_fail(err, "combine launch");
+    return EP_OK;
+}
+
+ep_status_t ep_combine_tokens(ep_handle_t handle, const void* y, int hidden, int64_t y_rows, const void* bias,
+                              void* out, void* stream) {
+    g_last_error[0] = '\0';
+    const Handle* h = check_handle(handle);
+    if (h == nullptr) return fail(EP_ERR_INVALID_ARG, "invalid handle");
+    if (hidden < 8 || hidden > kMaxHidden || hidden % 8 != 0)
+        return fail(EP_ERR_INVALID_ARG, "hidden must be a multiple of 8 in [8, 32768]");
+    if (h->T > 0) {
+        if (y == nullptr || !aligned16(y)) return fail(EP_ERR_INVALID_ARG, "y must be non-NULL and 16-byte aligned");
+        if (y_rows < h->T)
+            return fail(EP_ERR_INVALID_ARG, "y_rows %lld < num_tokens %d", (long long)y_rows, h->T);
+        if (out == nullptr || !aligned16(out)) return fail(EP_ERR_INVALID_ARG, "out must be non-NULL and 16-byte aligned");
+        if (bias != nullptr && !aligned16(bias)) return fail(EP_ERR_INVALID_ARG, "bias must be 16-byte aligned");
+    }
+    CombineArgs a;
+    a.y = y;
+    a.topk_weights = nullptr;
+    a.bias = bias;
+    a.out = out;
+    a.hidden = hidden;
+    a.tokens = true;
+    const hipError_t err = launch_combine(*h, a, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return hip_fail(err, "combine_tokens launch");
     return EP_OK;
 }
 

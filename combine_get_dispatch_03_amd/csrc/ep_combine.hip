@@ -2,6 +2,9 @@
 // token, element-wise accumulation of the top-k expert output rows; §3.2 phase 6: accumulate then store the
 // token's output row; [MoE-comm] §一: the shared-expert output enters as bias).
 //
+// The same kernel moves the token-major rows back (do_expand off): one slot per token, its row among this
+// rank's tokens, with unit weight.
+//
 // Work items are 1 KiB output segments (512 channels): item (t, s) is segment s of token t's output row, so
 // a token's row is produced by several short waves instead of one long one, which keeps more gathers in
 // flight across the chip.  The token's valid (slot, weight) pairs are compacted into lanes 0..nv-1 and read
@@ -22,8 +25,8 @@ struct Params {
     const float* w;
     const uint16_t* bias;
     uint16_t* out;
-    const int32_t* slot;
-    int T, H, K;
+    const int32_t* slot;   // row of entry k of token t at slot[t * stride + k]
+    int T, H, K, stride;
     int nseg;          // 1 KiB segments per row
     int64_t nitems;    // T * nseg
 };
@@ -60,7 +63,7 @@ __global__ __launch_bounds__(kBlock) void k_combine(Params p) {
     const int t = (int)(item / p.nseg), seg = (int)(item % p.nseg);
 
     // compact the token's valid slots (ascending k) into lanes 0..nv-1
-    const int s = lane < p.K ? p.slot[(int64_t)t * p.K + lane] : -1;
+    const int s = lane < p.K ? p.slot[(int64_t)t * p.stride + lane] : -1;
     const float wk = lane < p.K ? (p.w != nullptr ? p.w[(int64_t)t * p.K + lane] : 1.0f) : 0.0f;
     const uint64_t vm = ballot(s >= 0);
     const int nv = popc64(vm);
@@ -183,10 +186,18 @@ hipError_t launch_combine(const Handle& h, const CombineArgs& a, hipStream_t str
     p.w = a.topk_weights;
     p.bias = static_cast<const uint16_t*>(a.bias);
     p.out = static_cast<uint16_t*>(a.out);
-    p.slot = h.ws.slot;
     p.T = h.T;
     p.H = a.hidden;
-    p.K = h.K;
+    if (a.tokens) {               // one row per token: its row among this rank's tokens, unit weight
+        p.slot = h.ws.send_slot + h.rank;
+        p.stride = h.R;
+        p.K = 1;
+        p.w = nullptr;
+    } else {
+        p.slot = h.ws.slot;
+        p.stride = h.K;
+        p.K = h.K;
+    }
     p.nseg = (a.hidden / 8 + kWave - 1) / kWave;
     p.nitems = (int64_t)h.T * p.nseg;
     const unsigned nblocks = (unsigned)((p.nitems + kWavesPerBlock - 1) / kWavesPerBlock);

@@ -11,6 +11,8 @@
 //                      BF16, and rows already in their receive format (the receiver's copy epilogue,
 //                      [DeepEP->MegaMoE] §2.4): one 1 KiB segment of 16-byte copies, plus the row's scales.
 //   padding item (p, s) segment s of padding row pad_rows[p] (zeros; its metadata on segment 0).
+// Token-major mode (do_expand off, [MoE-comm] §一 dispatch arguments): the token's only local destination is
+// its row among this rank's tokens, with the token's K local expert ids and weights as metadata; no padding.
 // Wave w runs token item w (if any) and then padding items w, w + W, w + 2W, ... (at most kPadItemsPerWave of
 // them).  The grid is sized on the host from the number of tokens and the worst-case padding; the actual
 // padding count is read on the device.
@@ -31,19 +33,21 @@ struct Params {
     const float* w;
     const int64_t* topk_idx;
     const int32_t* slot;
-    const int32_t* send_slot;
+    const int32_t* send_slot;    // [T, R] send-window rows (windows only), else nullptr
+    const int32_t* own_row;      // token-major mode: [T, R] per-rank token rows (column rank), else nullptr
     const int32_t* pad_rows;
     const int32_t* pad_total;
     uint8_t* recv_x;
     float* recv_scales;
     int32_t* recv_src;
-    float* recv_w;
+    float* recv_w;               // [rows] (expert-major) or [T, K] (token-major)
+    int64_t* recv_topk_idx;      // token-major: [T, K] local expert ids or -1
     uint8_t* send_x;
     float* send_scales;
     int32_t* send_src;
     int64_t* send_topk_idx;
     float* send_topk_w;
-    int T, H, K, R, epr;
+    int T, H, K, R, rank, epr;
     int row_bytes;    // bytes of one destination row
     int G;            // fp32 scales per row (FP8: H / 128; raw: as given, 0 for none)
     int nstep;        // segments per row
@@ -53,22 +57,36 @@ struct Params {
     int64_t nwaves;   // waves in the grid
 };
 
-// Per-token destinations: the local slots (lanes < K) and send rows (lanes < R); segment 0 also writes the
-// per-row metadata.
+// Per-token destinations: the local rows (expert-major: lanes < K hold the token's slots; token-major: lane 0
+// holds its row among this rank's tokens) and the send rows (lanes r < R, r != rank); segment 0 also writes
+// the per-row metadata.
 __device__ __forceinline__ void token_dests(const Params& p, int t, bool meta, int lane, int& ds, int& js,
                                             uint64_t& lmask, uint64_t& smask) {
-    ds = lane < p.K ? p.slot[(int64_t)t * p.K + lane] : -1;
-    js = (p.send_slot != nullptr && lane < p.R) ? p.send_slot[(int64_t)t * p.R + lane] : -1;
+    if (p.own_row == nullptr) ds = lane < p.K ? p.slot[(int64_t)t * p.K + lane] : -1;
+    else ds = lane == 0 ? p.own_row[(int64_t)t * p.R + p.rank] : -1;
+    js = (p.send_slot != nullptr && lane < p.R && lane != p.rank) ? p.send_slot[(int64_t)t * p.R + lane] : -1;
     lmask = ballot(ds >= 0);
     smask = ballot(js >= 0);
     if (!meta) return;
     const float wk = (lane < p.K && p.w != nullptr) ? p.w[(int64_t)t * p.K + lane] : 1.0f;
-    if (ds >= 0) {
-        if (p.recv_src) p.recv_src[ds] = t;
-        if (p.recv_w) p.recv_w[ds] = wk;
+    const bool need_e = (smask != 0 && p.send_topk_idx != nullptr) ||
+                        (p.own_row != nullptr && lmask != 0 && p.recv_topk_idx != nullptr);
+    const int64_t e = (need_e && lane < p.K) ? p.topk_idx[(int64_t)t * p.K + lane] : -1;
+    if (p.own_row == nullptr) {
+        if (ds >= 0) {
+            if (p.recv_src) p.recv_src[ds] = t;
+            if (p.recv_w) p.recv_w[ds] = wk;
+        }
+    } else if (lmask != 0) {
+        const int64_t j = readlane(ds, 0);
+        if (lane == 0 && p.recv_src) p.recv_src[j] = t;
+        if (lane < p.K) {
+            const int64_t lo = (int64_t)p.rank * p.epr;
+            if (p.recv_topk_idx) p.recv_topk_idx[j * p.K + lane] = (e >= lo && e < lo + p.epr) ? e - lo : -1;
+            if (p.recv_w) p.recv_w[j * p.K + lane] = wk;
+        }
     }
     if (smask != 0 && (p.send_src || p.send_topk_idx || p.send_topk_w)) {
-        const int64_t e = lane < p.K ? p.topk_idx[(int64_t)t * p.K + lane] : -1;
         for (uint64_t m = smask; m != 0; m &= m - 1) {
             const int r = __builtin_ctzll(m);
             const int64_t row = (int64_t)r * p.T + readlane(js, r);
@@ -253,13 +271,15 @@ hipError_t launch_dispatch(const Handle& h, const DispatchArgs& a, hipStream_t s
     p.w = a.topk_weights;
     p.topk_idx = h.topk_idx;
     p.slot = h.ws.slot;
-    p.send_slot = h.R > 1 ? h.ws.send_slot : nullptr;
+    p.send_slot = h.ws.send_slot;
+    p.own_row = (a.expand || raw_rows) ? nullptr : h.ws.send_slot;
     p.pad_rows = h.ws.pad_rows;
     p.pad_total = h.ws.pad_total;
     p.recv_x = static_cast<uint8_t*>(a.out.recv_x);
     p.recv_scales = a.out.recv_x_scales;
     p.recv_src = a.out.recv_src_idx;
     p.recv_w = a.out.recv_topk_weights;
+    p.recv_topk_idx = p.own_row != nullptr ? a.out.recv_topk_idx : nullptr;
     const bool windows = h.R > 1 && !raw_rows;
     p.send_x = windows ? static_cast<uint8_t*>(a.out.send_x) : nullptr;
     p.send_scales = windows ? a.out.send_x_scales : nullptr;
@@ -271,6 +291,7 @@ hipError_t launch_dispatch(const Handle& h, const DispatchArgs& a, hipStream_t s
     p.H = a.hidden;
     p.K = h.K;
     p.R = h.R;
+    p.rank = h.rank;
     p.epr = h.El;
     p.zero_pad = a.zero_pad ? 1 : 0;
     if (fp8) {
@@ -285,7 +306,7 @@ hipError_t launch_dispatch(const Handle& h, const DispatchArgs& a, hipStream_t s
     if (p.G == 0) p.recv_scales = nullptr;
     p.ntok_items = (int64_t)h.T * p.nstep;
     const bool meta = p.recv_src != nullptr || p.recv_w != nullptr;
-    p.pad_sub = h.A > 1 ? (a.zero_pad ? p.nstep : (meta ? 1 : 0)) : 0;
+    p.pad_sub = (h.A > 1 && p.own_row == nullptr) ? (a.zero_pad ? p.nstep : (meta ? 1 : 0)) : 0;
     const int64_t max_pad_items = (int64_t)h.El * (h.A - 1) * p.pad_sub;
     int64_t nwaves = p.ntok_items;
     const int64_t per_wave = a.zero_pad ? kPadItemsPerWave : kWave;

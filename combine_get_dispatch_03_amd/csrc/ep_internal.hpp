@@ -24,7 +24,8 @@ constexpr int kMaxRowBytes = 65536;
 struct Workspace {
     int32_t* tile_hist;   // [ntiles, E + R + 1]  per tile: expert counts | token-in-rank counts | invalid
     int32_t* slot;        // [T, K]       expert-major row of each entry, -1 if not local
-    int32_t* send_slot;   // [T, R]       row in the send window of rank r, -1 if none (R > 1 only)
+    int32_t* send_slot;   // [T, R]       rank of t among the tokens with an expert on r, else -1: its row in the
+                          //              send window of r (r != rank) or in the token-major receive rows (r == rank)
     int32_t* cnt_local;   // [El]         routed entries of each local expert
     int32_t* psum;        // [El + 1]     aligned exclusive row starts of the local experts
     int32_t* pad_rows;    // [El * (A-1)] dense list of padding rows, expert by expert (A > 1 only)
@@ -67,6 +68,7 @@ struct DispatchArgs {
     const float* topk_weights;
     int hidden;
     bool zero_pad;
+    bool expand;               // false: token-major receive rows (kBf16 / kFp8 only)
     ep_dispatch_out_t out;
 };
 hipError_t launch_dispatch(const Handle& h, const DispatchArgs& a, hipStream_t stream);
@@ -86,6 +88,7 @@ struct CombineArgs {
     const void* bias;
     void* out;
     int hidden;
+    bool tokens;               // true: y holds the token-major rows (one per token, unit weight)
 };
 hipError_t launch_combine(const Handle& h, const CombineArgs& a, hipStream_t stream);
 

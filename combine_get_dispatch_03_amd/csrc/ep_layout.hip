@@ -161,10 +161,9 @@ __device__ uint64_t count_tile(const int64_t* __restrict__ idx, int T, int K, in
     return mask;
 }
 
-// Rows of the tile's tokens in the send windows, from the rank masks of count_tile: the rank of the token among
-// the tile's earlier tokens with an expert on r (tile-local), or -1 when it has none there or r == skip.
-__device__ void send_rows(const CountLds& L, uint64_t mask, int T, int R, int skip, int tile,
-                          int32_t* __restrict__ out) {
+// Per-rank token rows of the tile's tokens, from the rank masks of count_tile: the rank of the token among the
+// tile's earlier tokens with an expert on r (tile-local), or -1 when it has none there.
+__device__ void send_rows(const CountLds& L, uint64_t mask, int T, int R, int tile, int32_t* __restrict__ out) {
     const int tid = threadIdx.x, w = tid >> 6;
     if (w >= 4) return;
     const int t = tile * kTile + tid;
@@ -173,7 +172,7 @@ __device__ void send_rows(const CountLds& L, uint64_t mask, int T, int R, int sk
     for (int r = 0; r < R; ++r) {
         const bool bit = (mask >> r) & 1ull;
         const uint64_t b = ballot(bit);
-        if (tv) out[(int64_t)t * R + r] = (bit && r != skip) ? L.rcnt_w[w * R + r] + popc64(b & lt) : -1;
+        if (tv) out[(int64_t)t * R + r] = bit ? L.rcnt_w[w * R + r] + popc64(b & lt) : -1;
     }
 }
 
@@ -291,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void k_layout_count(
         packed_out[ent_tile0 + j] =
             p < 0 ? -1 : (((p >> kPackShift) + L.cnt_w[wv * E + (p & kPackMask)]) << kPackShift) | (p & kPackMask);
     }
-    if (send_tmp != nullptr) send_rows(L, mask, T, R, -1, tile, send_tmp);   // tile-local; finalize adds bases
+    send_rows(L, mask, T, R, tile, send_tmp);   // tile-local; finalize adds the earlier tiles' counts
 }
 
 __global__ __launch_bounds__(kThreads) void k_layout_finalize(
@@ -371,13 +370,11 @@ __global__ __launch_bounds__(kThreads) void k_layout_finalize(
             slot[ent0 + j] = s;
         }
     }
-    if (send_slot != nullptr) {
-        for (int q = tid; q < ntok * R; q += kThreads) {
-            const int r = q % R;
-            const int64_t i = (int64_t)tok_tile0 * R + q;
-            const int v = send_slot[i];
-            send_slot[i] = (r != rank && v >= 0) ? before[E + r] + v : -1;
-        }
+    for (int q = tid; q < ntok * R; q += kThreads) {
+        const int r = q % R;
+        const int64_t i = (int64_t)tok_tile0 * R + q;
+        const int v = send_slot[i];
+        send_slot[i] = v >= 0 ? before[E + r] + v : -1;
     }
 }
 
@@ -404,7 +401,7 @@ __global__ __launch_bounds__(kThreads) void k_layout_single(
         }
         slot[j] = s;
     }
-    if (send_slot != nullptr) send_rows(L, mask, T, R, rank, 0, send_slot);
+    send_rows(L, mask, T, R, 0, send_slot);
 }
 
 size_t single_lds_bytes(int E, int K, int R, int epr) {
@@ -425,7 +422,7 @@ hipError_t launch_layout(const Handle& h, const LayoutOutputs& out, hipStream_t 
     const int epr = h.El;
     int nbits = 0;
     while ((1 << nbits) < h.E) ++nbits;
-    int32_t* send = h.R > 1 ? h.ws.send_slot : nullptr;
+    int32_t* send = h.ws.send_slot;
     const Outputs o{h.ws.cnt_local, h.ws.psum, h.ws.pad_rows, h.ws.pad_total, out.num_tokens_per_rank,
                     out.num_tokens_per_expert, out.psum, out.num_invalid};
 

@@ -5,10 +5,14 @@
  * dispatch and combine:
  *   ep_get_layout  routing table -> per-expert / per-rank counts, token-in-rank membership, aligned
  *                  per-expert row starts, and the slot of every routed entry (kept in a handle);
- *   ep_dispatch    permute token rows into an expert-major, alignment-padded receive buffer, optionally
- *                  cast to FP8 e4m3 with per-128-channel fp32 scales, and pack per-destination send windows
- *                  for experts owned by other ranks;
- *   ep_combine     weighted top-k reduction of expert outputs back to token order in BF16, plus bias.
+ *   ep_dispatch    permute token rows into an expert-major, alignment-padded receive buffer (or, without
+ *                  expansion, one token-major row per token), optionally cast to FP8 e4m3 with
+ *                  per-128-channel fp32 scales, and pack per-destination send windows for experts owned by
+ *                  other ranks;
+ *   ep_combine     weighted top-k reduction of expert outputs back to token order in BF16, plus bias
+ *                  (ep_combine_tokens for the token-major rows);
+ *   ep_dispatch_rows / ep_combine_reduce  the receiver's placement of rows that arrived from other ranks and
+ *                  the source's sum of the rows those ranks return (the two ends of the exchange).
  *
  * Page names used in the citations:
  *   [DeepEP->MegaMoE]  "从 DeepEP 到 Mega MoE：MoE Runtime 演进的三向验证分析" (backyes.github.io)
@@ -45,7 +49,7 @@ extern "C" {
 typedef enum ep_status {
     EP_OK = 0,
     EP_ERR_INVALID_ARG = 1,   /* an argument is out of range, misaligned, NULL where required, or a size is short */
-    EP_ERR_UNSUPPORTED = 2,   /* a mode this version does not implement (do_expand = 0)                           */
+    EP_ERR_UNSUPPORTED = 2,   /* a mode this version does not implement (none at present; reserved)               */
     EP_ERR_HIP = 3            /* a HIP launch failed; the stream state is whatever HIP reports                    */
 } ep_status_t;
 
@@ -95,7 +99,10 @@ const char* ep_last_error(void);
  *                        [psum[j], psum[j+1]) of which the first num_tokens_per_expert[rank*El + j] are valid.
  *   num_invalid_topk     device int32 [1] out, nullable.
  *   handle_out           host out: a new handle (free with ep_handle_free).  Rows of one expert are ordered
- *                        by ascending flat entry index t * num_topk + k.
+ *                        by ascending flat entry index t * num_topk + k.  The handle also ranks, for every
+ *                        rank r, the tokens with an expert on r in ascending token order: the row of the
+ *                        token in the send window of r (r != rank), or in the token-major receive rows
+ *                        (r == rank, dispatch with do_expand = 0).
  */
 ep_status_t ep_get_layout(const int64_t* topk_idx, int num_tokens, int num_topk, int num_experts, int num_ranks,
                           int rank, int expert_alignment, void* workspace, size_t workspace_bytes,
@@ -103,13 +110,19 @@ ep_status_t ep_get_layout(const int64_t* topk_idx, int num_tokens, int num_topk,
                           int32_t* psum_num_recv_tokens_per_expert, int32_t* num_invalid_topk,
                           ep_handle_t* handle_out, void* stream);
 
-/* Outputs of ep_dispatch.  All device memory owned by the caller; NULL = not requested where allowed. */
+/* Outputs of ep_dispatch.  All device memory owned by the caller; NULL = not requested where allowed.
+ * "rows" is recv_capacity.  Expert-major (do_expand = 1) and token-major (do_expand = 0) shapes differ where
+ * noted. */
 typedef struct ep_dispatch_out {
-    void*    recv_x;            /* required: [recv_capacity, hidden] e4m3 bytes (FP8) or bf16 (BF16)            */
-    float*   recv_x_scales;     /* FP8: required, [recv_capacity, hidden / 128] fp32 scales; BF16: ignored       */
-    int32_t* recv_src_idx;      /* nullable: [recv_capacity] source token of each row; -1 on padding rows        */
-    float*   recv_topk_weights; /* nullable: [recv_capacity] routing weight of each row; 0 on padding rows      */
-    int64_t  recv_capacity;     /* rows allocated in the recv arrays; must be >= ep_recv_capacity(...)          */
+    void*    recv_x;            /* required: [rows, hidden] e4m3 bytes (FP8) or bf16 (BF16)                     */
+    float*   recv_x_scales;     /* FP8: required, [rows, hidden / 128] fp32 scales; BF16: ignored                */
+    int32_t* recv_src_idx;      /* nullable: [rows] source token of each row; -1 on padding rows                 */
+    float*   recv_topk_weights; /* nullable: expert-major [rows] routing weight of each row, 0 on padding rows;
+                                   token-major [num_tokens, num_topk] the token's weights                         */
+    int64_t* recv_topk_idx;     /* token-major only, nullable: [num_tokens, num_topk] expert id local to this
+                                   rank, -1 where another rank owns the entry's expert; ignored otherwise         */
+    int64_t  recv_capacity;     /* rows allocated in the recv arrays: >= ep_recv_capacity(...) (expert-major),
+                                   >= num_tokens (token-major)                                                    */
     void*    send_x;            /* num_ranks > 1: required, [num_ranks, num_tokens, hidden] rows (window per rank)*/
     float*   send_x_scales;     /* num_ranks > 1 and FP8: required, [num_ranks, num_tokens, hidden / 128]        */
     int32_t* send_src_idx;      /* nullable: [num_ranks, num_tokens] source token of each window row            */
@@ -129,10 +142,15 @@ typedef struct ep_dispatch_out {
  *                   recv_topk_weights and send_topk_weights only.
  *   recv_dtype      EP_DTYPE_BF16 or EP_DTYPE_FP8_E4M3.  FP8: per token and 128-channel group,
  *                   a = max(max|x|, 1e-4), scale = a / 448, q = e4m3_rne_saturating(x * (448 / a)).
- *   do_expand       must be 1 (expert-major rows, one per routed entry); 0 returns EP_ERR_UNSUPPORTED.
- *   do_zero_padding 1: padding rows [psum[j] + count_j, psum[j+1]) get zero bytes and zero scales;
- *                   0: their data bytes and scales are left untouched.  Their recv_src_idx / weights are
- *                   written (-1 / 0) either way.  Rows >= psum[El] are never written.
+ *   do_expand       1: expert-major rows, one per routed entry, at the rows of the layout.
+ *                   0: token-major rows ([MoE-comm] §一 dispatch arguments, do_expand): one row per token
+ *                   with an expert on this rank, in ascending token order (row j = the j-th such token),
+ *                   with recv_src_idx = the token, recv_topk_idx / recv_topk_weights its K entries; no
+ *                   padding; rows past num_tokens_per_rank[rank] are untouched.  The expert computation
+ *                   then returns one row per token, moved back by ep_combine_tokens.
+ *   do_zero_padding expert-major only.  1: padding rows [psum[j] + count_j, psum[j+1]) get zero bytes and
+ *                   zero scales; 0: their data bytes and scales are left untouched.  Their recv_src_idx /
+ *                   weights are written (-1 / 0) either way.  Rows >= psum[El] are never written.
  *   Send windows (num_ranks > 1): for every other rank r, row j of window r holds the j-th token (ascending)
  *   with an expert on r: the same bytes and scales as the token's local rows.  Rows past the window's count
  *   are untouched; window `rank` is untouched.
@@ -177,6 +195,20 @@ ep_status_t ep_dispatch_rows(ep_handle_t handle, const void* rows, int row_bytes
  */
 ep_status_t ep_combine(ep_handle_t handle, const void* y, int hidden, int64_t y_rows, const float* topk_weights,
                        const void* bias, void* out, void* stream);
+
+/*
+ * ep_combine_tokens -- combine for the token-major rows of a dispatch with do_expand = 0 ([MoE-comm] §一:
+ * without expansion the expert side returns one row per received token, so the combine moves that row back
+ * to its token; the shared expert's output joins as bias).
+ *
+ *   y       device bf16 [y_rows, hidden], row j = the output for the j-th token of this rank (as recv_x);
+ *           y_rows >= num_tokens.  Rows past num_tokens_per_rank[rank] are never read.
+ *   bias    device bf16 [num_tokens, hidden], nullable.
+ *   out     device bf16 [num_tokens, hidden] = y[row of t] + bias in fp32, one RNE rounding; a token with no
+ *           expert on this rank gets its bias row (or zeros).  Every row is written.
+ */
+ep_status_t ep_combine_tokens(ep_handle_t handle, const void* y, int hidden, int64_t y_rows, const void* bias,
+                              void* out, void* stream);
 
 /*
  * ep_combine_reduce -- the source rank's reduce epilogue after the combine exchange ([DeepEP->MegaMoE] §2.5:

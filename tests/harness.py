@@ -19,9 +19,9 @@ CANARY_F32 = -7.0
 ATOL, RTOL = 1e-2, 8e-3     # combine tolerance: |gpu - oracle| <= ATOL + RTOL * |oracle|
 
 
-def dispatch_outputs_with_canary(ep, h, hidden, fp8, dev):
+def dispatch_outputs_with_canary(ep, h, hidden, fp8, dev, do_expand=True):
     """Dispatch output tensors, pre-filled with canaries (the binding itself never initialises them)."""
-    o = ep.alloc_dispatch_outputs(h, hidden, fp8, device=dev)
+    o = ep.alloc_dispatch_outputs(h, hidden, fp8, device=dev, do_expand=do_expand)
     for k, t in o.items():
         if t is None:
             continue
@@ -45,24 +45,25 @@ def to_np(t):
     return t.numpy()
 
 
-def oracle_run(inp, recv_fill=True):
+def oracle_run(inp, recv_fill=True, do_expand=True):
     c = inp["cfg"]
     idx = inp["topk_idx"].numpy()
     w = inp["topk_weights"].numpy()
     x = W.bf16_bits(inp["x"])
     lay = O.layout(idx, c.num_experts, c.num_ranks, c.rank, c.expert_alignment)
     d = O.dispatch(x, idx, w, lay, c.num_experts, c.num_ranks, c.rank, c.expert_alignment, fp8=c.fp8,
-                   zero_pad=c.zero_padding, recv_fill=(CANARY_BYTE, CANARY_SCALE) if recv_fill else None)
+                   zero_pad=c.zero_padding, recv_fill=(CANARY_BYTE, CANARY_SCALE) if recv_fill else None,
+                   do_expand=do_expand)
     return lay, d
 
 
-def gpu_layout_dispatch(ep, inp, dev="cuda"):
+def gpu_layout_dispatch(ep, inp, dev="cuda", do_expand=True):
     c = inp["cfg"]
     idx = inp["topk_idx"].to(dev)
     h, lay = ep.ep_get_layout(idx, c.num_experts, c.num_ranks, c.rank, c.expert_alignment)
-    out = dispatch_outputs_with_canary(ep, h, c.hidden, c.fp8, dev)
-    ep.ep_dispatch(h, inp["x"].to(dev), inp["topk_weights"].to(dev), fp8=c.fp8, do_zero_padding=c.zero_padding,
-                   out=out)
+    out = dispatch_outputs_with_canary(ep, h, c.hidden, c.fp8, dev, do_expand=do_expand)
+    ep.ep_dispatch(h, inp["x"].to(dev), inp["topk_weights"].to(dev), fp8=c.fp8, do_expand=do_expand,
+                   do_zero_padding=c.zero_padding, out=out)
     return h, lay, out
 
 
@@ -85,6 +86,8 @@ def assert_dispatch_equal(gout, od, c):
         assert np.array_equal(gx, od["recv_x"]), _first_diff(gx, od["recv_x"])
     assert np.array_equal(to_np(gout["recv_src_idx"]), od["recv_src"])
     assert np.array_equal(to_np(gout["recv_topk_weights"]).view(np.uint32), od["recv_w"].view(np.uint32))
+    if od.get("recv_topk_idx") is not None:
+        assert np.array_equal(to_np(gout["recv_topk_idx"]), od["recv_topk_idx"])
     if od.get("send_x") is not None:
         sx = to_np(gout["send_x"])
         assert np.array_equal(sx.reshape(od["send_x"].shape).view(np.uint8), od["send_x"].view(np.uint8))

@@ -38,6 +38,8 @@ def lib():
     L.ep_combine.argtypes = [P, P, I, I64, P, P, P, P]
     L.ep_handle_free.restype = I
     L.ep_handle_free.argtypes = [P]
+    L.ep_combine_tokens.restype = I
+    L.ep_combine_tokens.argtypes = [P, P, I, I64, P, P, P]
     return L
 
 
@@ -45,7 +47,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     for n in ("ep_get_layout", "ep_dispatch", "ep_combine", "ep_handle_free", "ep_recv_capacity",
               "ep_layout_workspace_bytes", "ep_status_string", "ep_last_error", "ep_dispatch_rows",
-              "ep_combine_reduce"):
+              "ep_combine_reduce", "ep_combine_tokens"):
         assert n in names
 
 
@@ -71,7 +73,9 @@ def test_workspace_bytes(lib):
     assert lib.ep_layout_workspace_bytes(4096, 33, 256, 1, 128) == 0  # K > 32
     assert lib.ep_layout_workspace_bytes(4096, 8, 2048, 1, 128) == 0  # E > 1024
     assert lib.ep_layout_workspace_bytes(4096, 8, 256, 128, 128) == 0 # R > 64
-    assert lib.ep_layout_workspace_bytes(4096, 8, 256, 8, 128) > lib.ep_layout_workspace_bytes(4096, 8, 256, 1, 128)
+    # the per-rank token rows ([T, R] int32) grow with R (the per-local-expert arrays shrink a little)
+    assert lib.ep_layout_workspace_bytes(4096, 8, 256, 8, 1) - lib.ep_layout_workspace_bytes(4096, 8, 256, 1, 1) \
+        >= 4096 * 7 * 4 - 2 * 256 * 4 - 512
 
 
 def test_status_strings(lib):
@@ -121,3 +125,5 @@ def test_dispatch_combine_reject_bad_handles(lib):
     bogus = (ctypes.c_uint32 * 64)()                       # a host block that is not a handle
     assert lib.ep_dispatch(ctypes.cast(bogus, ctypes.c_void_p), None, 128, None, 1, 1, 0, None, None) == 1
     assert lib.ep_handle_free(None) == 0
+    assert lib.ep_combine_tokens(None, None, 128, 0, None, None, None) == 1
+    assert b"handle" in lib.ep_last_error()

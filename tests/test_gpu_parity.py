@@ -256,8 +256,12 @@ def test_validation_errors(ep):
     short = ep.alloc_dispatch_outputs(h, 7168, True, device=DEV, recv_capacity=h.recv_capacity - 1)
     with pytest.raises(ep.EPError, match="recv_capacity"):
         ep.ep_dispatch(h, x, None, fp8=True, out=short)
-    with pytest.raises(ep.EPError, match="unsupported"):
-        ep.ep_dispatch(h, x, None, fp8=True, do_expand=False)
+    short_tm = ep.alloc_dispatch_outputs(h, 7168, True, device=DEV, recv_capacity=h.num_tokens - 1,
+                                         do_expand=False)
+    with pytest.raises(ep.EPError, match="recv_capacity"):
+        ep.ep_dispatch(h, x, None, fp8=True, do_expand=False, out=short_tm)
+    with pytest.raises(ep.EPError, match="y_rows"):
+        ep.ep_combine_tokens(h, torch.zeros(h.num_tokens - 1, 7168, dtype=torch.bfloat16, device=DEV))
     y = torch.zeros(h.recv_capacity - 1, 7168, dtype=torch.bfloat16, device=DEV)
     with pytest.raises(ep.EPError, match="y_rows"):
         ep.ep_combine(h, y, None)
