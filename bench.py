@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--no-epilogues", dest="epilogues", action="store_false",
                     help="skip the receiver-placement / source-reduce measurement at the EP8 shapes")
+    ap.add_argument("--no-decode", dest="decode", action="store_false",
+                    help="skip the decode-shape comparison of the one-launch layout + dispatch")
     return ap.parse_args()
 
 
@@ -190,6 +192,76 @@ def measure_epilogues(ep, W, dev, n):
                            received_rows=n_valid, placed_rows=V),
         combine_reduce=dict(us=round(t_red * 1e3, 2), bytes=b_red, GBps=round(b_red / (t_red * 1e-3) / 1e9, 1),
                             partial_rows=n_part))
+
+
+def measure_decode(ep, W, dev, n):
+    """The decode shape (128 tokens x 7168, 256 experts, top-8, FP8, alignment 128, no zero padding): layout +
+    dispatch as two calls (ep_get_layout, ep_dispatch: two launches) and as one (ep_layout_dispatch: one
+    launch), each timed as n back-to-back calls between HIP events; and the whole step (layout, dispatch,
+    combine) captured in a HIP graph both ways, timed over n replays."""
+    import time
+
+    import torch
+
+    inp = W.make_inputs("decode")
+    c = inp["cfg"]
+    idx, w, x = inp["topk_idx"].to(dev), inp["topk_weights"].to(dev), inp["x"].to(dev)
+    T, K, E, A = c.num_tokens, c.num_topk, c.num_experts, c.expert_alignment
+    ws = torch.empty(ep.ep_layout_workspace_bytes(T, K, E, 1, A), dtype=torch.uint8, device=dev)
+    lay = dict(num_tokens_per_rank=torch.empty(1, dtype=torch.int32, device=dev),
+               num_tokens_per_expert=torch.empty(E, dtype=torch.int32, device=dev),
+               is_token_in_rank=torch.empty((T, 1), dtype=torch.uint8, device=dev),
+               psum_num_recv_tokens_per_expert=torch.empty(E + 1, dtype=torch.int32, device=dev),
+               num_invalid_topk=torch.empty(1, dtype=torch.int32, device=dev))
+    h0, _ = ep.ep_get_layout(idx, E, 1, 0, A, workspace=ws, outputs=lay)
+    dout = ep.alloc_dispatch_outputs(h0, c.hidden, True, device=dev)
+    y = W.random_expert_outputs(h0.recv_capacity, c.hidden, seed=99, device=dev)
+    out = torch.empty((T, c.hidden), dtype=torch.bfloat16, device=dev)
+
+    def two_calls():
+        h, _ = ep.ep_get_layout(idx, E, 1, 0, A, workspace=ws, outputs=lay)
+        ep.ep_dispatch(h, x, w, fp8=True, out=dout)
+        return h
+
+    def one_call():
+        h, _, _ = ep.ep_layout_dispatch(idx, x, E, 1, 0, A, w, fp8=True, out=dout, workspace=ws, outputs=lay)
+        return h
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(2.4e9 * 0.02))
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    def graph_step(first):
+        for _ in range(2):
+            ep.ep_combine(first(), y, w, out=out)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            ep.ep_combine(first(), y, w, out=out)
+        for _ in range(10):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            g.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e6 / n
+
+    res = dict(workload="decode: 128 tok x 7168, 256 experts, top-8, FP8, alignment 128, no zero padding",
+               layout_then_dispatch_us=round(timed(two_calls), 2),
+               layout_dispatch_one_launch_us=round(timed(one_call), 2),
+               combine_us=round(timed(lambda: ep.ep_combine(h0, y, w, out=out)), 2),
+               step_graph_two_launches_us=round(graph_step(two_calls), 2),
+               step_graph_one_launch_us=round(graph_step(one_call), 2))
+    h0.free()
+    return res
 
 
 def main():
@@ -351,6 +423,7 @@ def main():
                     algorithmic_bytes=bm[dom], avg_launch_us=round(avg[dom] * 1e3, 2))
 
     epi = measure_epilogues(ep, W, dev, args.steps) if args.epilogues else None
+    decode = measure_decode(ep, W, dev, args.steps) if args.decode else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -377,6 +450,7 @@ def main():
         roofline=roofline,
         cpu_baseline=cpu,
         epilogues=epi,
+        decode=decode,
     )
     print(json.dumps(line), flush=True)
 

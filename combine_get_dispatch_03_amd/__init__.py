@@ -1,8 +1,8 @@
 """Python binding of libep_mi355x.so (include/ep.h): MoE expert-parallel layout, dispatch and combine on one
 MI355X (gfx950) GPU.
 
-The functions keep the C names (ep_get_layout, ep_dispatch, ep_combine, ep_combine_tokens, ep_dispatch_rows,
-ep_combine_reduce, ep_handle_free, ep_recv_capacity, ep_layout_workspace_bytes).  They only marshal arguments: tensors become device pointers, the stream is
+The functions keep the C names (ep_get_layout, ep_dispatch, ep_layout_dispatch, ep_combine, ep_combine_tokens,
+ep_dispatch_rows, ep_combine_reduce, ep_handle_free, ep_recv_capacity, ep_layout_workspace_bytes).  They only marshal arguments: tensors become device pointers, the stream is
 torch's current HIP stream, and output tensors are allocated by torch when the caller does not pass them.
 Every step of the path runs in the HIP kernels of the library; there is no other implementation, and if
 the library is not built or cannot be loaded the import of this binding fails.
@@ -70,6 +70,9 @@ def _load_library():
     lib.ep_combine_reduce.argtypes = [P, P, I, P, P, P, P]
     lib.ep_combine_tokens.restype = I
     lib.ep_combine_tokens.argtypes = [P, P, I, I64, P, P, P]
+    lib.ep_layout_dispatch.restype = I
+    lib.ep_layout_dispatch.argtypes = [P, I, I, I, I, I, I, P, SZ, P, P, P, P, P, P, I, P, I, I, I,
+                                       ctypes.POINTER(_DispatchOut), ctypes.POINTER(P), P]
     return lib
 
 
@@ -154,11 +157,7 @@ class Handle:
             pass
 
 
-def ep_get_layout(topk_idx, num_experts, num_ranks=1, rank=0, expert_alignment=1, workspace=None, outputs=None,
-                  stream=None):
-    """Layout of `topk_idx` (int64 [T, K] on the GPU).  Returns (Handle, dict) with the device outputs
-    num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank, psum_num_recv_tokens_per_expert and
-    num_invalid_topk.  `outputs` may supply any of those tensors (or None entries to skip them)."""
+def _layout_prep(topk_idx, num_experts, num_ranks, expert_alignment, workspace, outputs):
     _need(topk_idx, torch.int64, "topk_idx")
     if topk_idx.dim() != 2:
         raise ValueError("topk_idx must be [num_tokens, num_topk]")
@@ -178,6 +177,21 @@ def ep_get_layout(topk_idx, num_experts, num_ranks=1, rank=0, expert_alignment=1
             is_token_in_rank=torch.empty((T, num_ranks), dtype=torch.uint8, device=dev),
             psum_num_recv_tokens_per_expert=torch.empty(El + 1, dtype=torch.int32, device=dev),
             num_invalid_topk=torch.empty(1, dtype=torch.int32, device=dev))
+    return T, K, workspace, outputs
+
+
+def _layout_ptrs(outputs):
+    return (_ptr(outputs.get("num_tokens_per_rank")), _ptr(outputs.get("num_tokens_per_expert")),
+            _ptr(outputs.get("is_token_in_rank")), _ptr(outputs.get("psum_num_recv_tokens_per_expert")),
+            _ptr(outputs.get("num_invalid_topk")))
+
+
+def ep_get_layout(topk_idx, num_experts, num_ranks=1, rank=0, expert_alignment=1, workspace=None, outputs=None,
+                  stream=None):
+    """Layout of `topk_idx` (int64 [T, K] on the GPU).  Returns (Handle, dict) with the device outputs
+    num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank, psum_num_recv_tokens_per_expert and
+    num_invalid_topk.  `outputs` may supply any of those tensors (or None entries to skip them)."""
+    T, K, workspace, outputs = _layout_prep(topk_idx, num_experts, num_ranks, expert_alignment, workspace, outputs)
     h = ctypes.c_void_p()
     _check(_lib.ep_get_layout(
         _ptr(topk_idx), T, K, num_experts, num_ranks, rank, expert_alignment, _ptr(workspace), workspace.numel(),
@@ -221,6 +235,17 @@ def alloc_dispatch_outputs(handle: Handle, hidden: int, fp8: bool, want_meta=Tru
     return o
 
 
+def _dispatch_struct(out):
+    def p(k):
+        t = out.get(k)
+        return t.data_ptr() if t is not None else None
+    return _DispatchOut(recv_x=p("recv_x"), recv_x_scales=p("recv_x_scales"), recv_src_idx=p("recv_src_idx"),
+                        recv_topk_weights=p("recv_topk_weights"), recv_topk_idx=p("recv_topk_idx"),
+                        recv_capacity=out["recv_x"].shape[0], send_x=p("send_x"), send_x_scales=p("send_x_scales"),
+                        send_src_idx=p("send_src_idx"), send_topk_idx=p("send_topk_idx"),
+                        send_topk_weights=p("send_topk_weights"))
+
+
 def ep_dispatch(handle: Handle, x, topk_weights=None, fp8=True, do_expand=True, do_zero_padding=False, out=None,
                 want_meta=True, want_send_meta=True, stream=None):
     """Dispatch `x` (bf16 [T, H]) through `handle`.  Returns the dict of output tensors (allocated here unless
@@ -235,22 +260,36 @@ def ep_dispatch(handle: Handle, x, topk_weights=None, fp8=True, do_expand=True, 
         out = alloc_dispatch_outputs(handle, H, fp8, want_meta, want_send_meta, device=x.device,
                                      do_expand=do_expand)
     cap = out["recv_x"].shape[0]
-    s = _DispatchOut(
-        recv_x=out["recv_x"].data_ptr(),
-        recv_x_scales=out["recv_x_scales"].data_ptr() if out.get("recv_x_scales") is not None else None,
-        recv_src_idx=out["recv_src_idx"].data_ptr() if out.get("recv_src_idx") is not None else None,
-        recv_topk_weights=out["recv_topk_weights"].data_ptr() if out.get("recv_topk_weights") is not None else None,
-        recv_topk_idx=out["recv_topk_idx"].data_ptr() if out.get("recv_topk_idx") is not None else None,
-        recv_capacity=cap,
-        send_x=out["send_x"].data_ptr() if out.get("send_x") is not None else None,
-        send_x_scales=out["send_x_scales"].data_ptr() if out.get("send_x_scales") is not None else None,
-        send_src_idx=out["send_src_idx"].data_ptr() if out.get("send_src_idx") is not None else None,
-        send_topk_idx=out["send_topk_idx"].data_ptr() if out.get("send_topk_idx") is not None else None,
-        send_topk_weights=out["send_topk_weights"].data_ptr() if out.get("send_topk_weights") is not None else None)
+    s = _dispatch_struct(out)
     _check(_lib.ep_dispatch(handle.ptr, _ptr(x), H, _ptr(topk_weights),
                             EP_DTYPE_FP8_E4M3 if fp8 else EP_DTYPE_BF16, int(bool(do_expand)),
                             int(bool(do_zero_padding)), ctypes.byref(s), _stream(stream)), "ep_dispatch")
     return out
+
+
+def ep_layout_dispatch(topk_idx, x, num_experts, num_ranks=1, rank=0, expert_alignment=1, topk_weights=None,
+                       fp8=True, do_expand=True, do_zero_padding=False, out=None, workspace=None, outputs=None,
+                       want_meta=True, want_send_meta=True, stream=None):
+    """ep_get_layout + ep_dispatch in one call (one kernel launch for <= 256 tokens).  Returns (Handle, layout
+    outputs dict, dispatch outputs dict), the same as the two calls would."""
+    T, K, workspace, outputs = _layout_prep(topk_idx, num_experts, num_ranks, expert_alignment, workspace, outputs)
+    _need(x, torch.bfloat16, "x")
+    if x.dim() != 2 or x.shape[0] != T:
+        raise ValueError("x must be [num_tokens, hidden]")
+    H = x.shape[1]
+    if topk_weights is not None:
+        _need(topk_weights, torch.float32, "topk_weights", shape=(T, K))
+    if out is None:
+        tmp = Handle(None, topk_idx, workspace, T, K, num_experts, num_ranks, rank, expert_alignment)
+        out = alloc_dispatch_outputs(tmp, H, fp8, want_meta, want_send_meta, device=x.device, do_expand=do_expand)
+    s = _dispatch_struct(out)
+    h = ctypes.c_void_p()
+    _check(_lib.ep_layout_dispatch(
+        _ptr(topk_idx), T, K, num_experts, num_ranks, rank, expert_alignment, _ptr(workspace), workspace.numel(),
+        *_layout_ptrs(outputs), _ptr(x), H, _ptr(topk_weights), EP_DTYPE_FP8_E4M3 if fp8 else EP_DTYPE_BF16,
+        int(bool(do_expand)), int(bool(do_zero_padding)), ctypes.byref(s), ctypes.byref(h), _stream(stream)),
+        "ep_layout_dispatch")
+    return Handle(h, topk_idx, workspace, T, K, num_experts, num_ranks, rank, expert_alignment), outputs, out
 
 
 def ep_combine(handle: Handle, y, topk_weights=None, bias=None, out=None, stream=None):
@@ -351,7 +390,7 @@ def ep_handle_free(handle: Handle):
     handle.free()
 
 
-__all__ = ["ep_get_layout", "ep_dispatch", "ep_combine", "ep_combine_tokens", "ep_handle_free", "ep_recv_capacity",
+__all__ = ["ep_get_layout", "ep_dispatch", "ep_layout_dispatch", "ep_combine", "ep_combine_tokens", "ep_handle_free", "ep_recv_capacity",
            "ep_dispatch_rows", "ep_combine_reduce",
            "ep_layout_workspace_bytes", "alloc_dispatch_outputs", "Handle", "EPError", "LIB_PATH",
            "hip_runtimes_loaded"]

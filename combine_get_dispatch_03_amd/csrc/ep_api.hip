@@ -111,12 +111,14 @@ const char* ep_status_string(ep_status_t s) {
 
 const char* ep_last_error(void) { return g_last_error; }
 
-ep_status_t ep_get_layout(const int64_t* topk_idx, int num_tokens, int num_topk, int num_experts, int num_ranks,
-                          int rank, int expert_alignment, void* workspace, size_t workspace_bytes,
-                          int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert, uint8_t* is_token_in_rank,
-                          int32_t* psum_num_recv_tokens_per_expert, int32_t* num_invalid_topk,
-                          ep_handle_t* handle_out, void* stream) {
-    g_last_error[0] = '\0';
+}  // extern "C"
+
+namespace {
+
+// Validation and the handle of ep_get_layout (nothing is enqueued).
+ep_status_t new_handle(const int64_t* topk_idx, int num_tokens, int num_topk, int num_experts, int num_ranks, int rank,
+                       int expert_alignment, void* workspace, size_t workspace_bytes, ep_handle_t* handle_out,
+                       Handle** h_out) {
     if (handle_out == nullptr) return fail(EP_ERR_INVALID_ARG, "handle_out is NULL");
     if (const char* why = check_shape(num_tokens, num_topk, num_experts, num_ranks, rank, expert_alignment))
         return fail(EP_ERR_INVALID_ARG, "%s", why);
@@ -143,25 +145,18 @@ ep_status_t ep_get_layout(const int64_t* topk_idx, int num_tokens, int num_topk,
     h->cap = (int64_t)num_tokens * num_topk + (int64_t)h->El * (expert_alignment - 1);
     h->topk_idx = topk_idx;
     h->ws = ws;
-
-    const LayoutOutputs out{num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank,
-                            psum_num_recv_tokens_per_expert, num_invalid_topk};
-    const hipError_t err = launch_layout(*h, out, static_cast<hipStream_t>(stream));
-    if (err != hipSuccess) {
-        h->magic = 0;
-        delete h;
-        return hip_fail(err, "layout launch");
-    }
-    *handle_out = reinterpret_cast<ep_handle_t>(h);
+    *h_out = h;
     return EP_OK;
 }
 
-ep_status_t ep_dispatch(ep_handle_t handle, const void* x, int hidden, const float* topk_weights,
-                        ep_dtype_t recv_dtype, int do_expand, int do_zero_padding, const ep_dispatch_out_t* out,
-                        void* stream) {
-    g_last_error[0] = '\0';
-    const Handle* h = check_handle(handle);
-    if (h == nullptr) return fail(EP_ERR_INVALID_ARG, "invalid handle");
+void drop_handle(Handle* h) {
+    h->magic = 0;
+    delete h;
+}
+
+// Validation of ep_dispatch's arguments against a handle, and its launch arguments (nothing is enqueued).
+ep_status_t dispatch_args(const Handle* h, const void* x, int hidden, const float* topk_weights, ep_dtype_t recv_dtype,
+                          int do_expand, int do_zero_padding, const ep_dispatch_out_t* out, DispatchArgs* a) {
     if (recv_dtype != EP_DTYPE_BF16 && recv_dtype != EP_DTYPE_FP8_E4M3)
         return fail(EP_ERR_INVALID_ARG, "recv_dtype must be EP_DTYPE_BF16 or EP_DTYPE_FP8_E4M3");
     const bool fp8 = recv_dtype == EP_DTYPE_FP8_E4M3;
@@ -185,21 +180,86 @@ ep_status_t ep_dispatch(ep_handle_t handle, const void* x, int hidden, const flo
                 return fail(EP_ERR_INVALID_ARG, "num_ranks > 1 with FP8 needs send_x_scales");
         }
     }
+    a->mode = fp8 ? DispatchArgs::kFp8 : DispatchArgs::kBf16;
+    a->x = x;
+    a->x_scales = nullptr;
+    a->row_bytes = 0;
+    a->nscales = 0;
+    a->topk_weights = topk_weights;
+    a->hidden = hidden;
+    a->zero_pad = do_zero_padding != 0;
+    a->expand = do_expand != 0;
+    a->out = *out;
+    if (!fp8) a->out.recv_x_scales = nullptr;
+    if (a->expand) a->out.recv_topk_idx = nullptr;
+    return EP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ep_status_t ep_get_layout(const int64_t* topk_idx, int num_tokens, int num_topk, int num_experts, int num_ranks,
+                          int rank, int expert_alignment, void* workspace, size_t workspace_bytes,
+                          int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert, uint8_t* is_token_in_rank,
+                          int32_t* psum_num_recv_tokens_per_expert, int32_t* num_invalid_topk,
+                          ep_handle_t* handle_out, void* stream) {
+    g_last_error[0] = '\0';
+    Handle* h = nullptr;
+    const ep_status_t st = new_handle(topk_idx, num_tokens, num_topk, num_experts, num_ranks, rank, expert_alignment,
+                                      workspace, workspace_bytes, handle_out, &h);
+    if (st != EP_OK) return st;
+    const LayoutOutputs out{num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank,
+                            psum_num_recv_tokens_per_expert, num_invalid_topk};
+    const hipError_t err = launch_layout(*h, out, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) {
+        drop_handle(h);
+        return hip_fail(err, "layout launch");
+    }
+    *handle_out = reinterpret_cast<ep_handle_t>(h);
+    return EP_OK;
+}
+
+ep_status_t ep_dispatch(ep_handle_t handle, const void* x, int hidden, const float* topk_weights,
+                        ep_dtype_t recv_dtype, int do_expand, int do_zero_padding, const ep_dispatch_out_t* out,
+                        void* stream) {
+    g_last_error[0] = '\0';
+    const Handle* h = check_handle(handle);
+    if (h == nullptr) return fail(EP_ERR_INVALID_ARG, "invalid handle");
     DispatchArgs a;
-    a.mode = fp8 ? DispatchArgs::kFp8 : DispatchArgs::kBf16;
-    a.x = x;
-    a.x_scales = nullptr;
-    a.row_bytes = 0;
-    a.nscales = 0;
-    a.topk_weights = topk_weights;
-    a.hidden = hidden;
-    a.zero_pad = do_zero_padding != 0;
-    a.expand = do_expand != 0;
-    a.out = *out;
-    if (!fp8) a.out.recv_x_scales = nullptr;
-    if (a.expand) a.out.recv_topk_idx = nullptr;
+    const ep_status_t st = dispatch_args(h, x, hidden, topk_weights, recv_dtype, do_expand, do_zero_padding, out, &a);
+    if (st != EP_OK) return st;
     const hipError_t err = launch_dispatch(*h, a, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return hip_fail(err, "dispatch launch");
+    return EP_OK;
+}
+
+ep_status_t ep_layout_dispatch(const int64_t* topk_idx, int num_tokens, int num_topk, int num_experts, int num_ranks,
+                               int rank, int expert_alignment, void* workspace, size_t workspace_bytes,
+                               int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert,
+                               uint8_t* is_token_in_rank, int32_t* psum_num_recv_tokens_per_expert,
+                               int32_t* num_invalid_topk, const void* x, int hidden, const float* topk_weights,
+                               ep_dtype_t recv_dtype, int do_expand, int do_zero_padding,
+                               const ep_dispatch_out_t* out, ep_handle_t* handle_out, void* stream) {
+    g_last_error[0] = '\0';
+    Handle* h = nullptr;
+    ep_status_t st = new_handle(topk_idx, num_tokens, num_topk, num_experts, num_ranks, rank, expert_alignment,
+                                workspace, workspace_bytes, handle_out, &h);
+    if (st != EP_OK) return st;
+    DispatchArgs a;
+    st = dispatch_args(h, x, hidden, topk_weights, recv_dtype, do_expand, do_zero_padding, out, &a);
+    if (st != EP_OK) {
+        drop_handle(h);
+        return st;
+    }
+    const LayoutOutputs lo{num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank,
+                           psum_num_recv_tokens_per_expert, num_invalid_topk};
+    const hipError_t err = launch_layout_dispatch(*h, lo, a, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) {
+        drop_handle(h);
+        return hip_fail(err, "layout_dispatch launch");
+    }
+    *handle_out = reinterpret_cast<ep_handle_t>(h);
     return EP_OK;
 }
 

@@ -38,6 +38,21 @@ __device__ __forceinline__ uint64_t match_peers(int key, bool active, int nbits)
     return peers;
 }
 
+// Inclusive prefix sum over the 64 lanes.  Within each 16-lane row: four DPP row shifts (by 1, 2, 4, 8; lanes
+// with no source read 0), each a VALU add; then rows 1..3 add the totals of the rows before them, read from
+// lanes 15, 31 and 47.  No LDS round trip.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+    const int r0 = __builtin_amdgcn_readlane(v, 15);
+    const int r1 = __builtin_amdgcn_readlane(v, 31);
+    const int r2 = __builtin_amdgcn_readlane(v, 47);
+    const int row = lane_id() >> 4;
+    return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
 // XOR-butterfly max over groups of 8 consecutive lanes (lanes 8g..8g+7).
 __device__ __forceinline__ float group8_max(float v) {
     v = fmaxf(v, __shfl_xor(v, 1));

@@ -73,6 +73,10 @@ struct DispatchArgs {
 };
 hipError_t launch_dispatch(const Handle& h, const DispatchArgs& a, hipStream_t stream);
 
+// Layout and dispatch of one routing table: one launch for <= 256 tokens (every block builds the layout in LDS),
+// else launch_layout then launch_dispatch.  The handle's workspace ends up as launch_layout leaves it.
+hipError_t launch_layout_dispatch(const Handle& h, const LayoutOutputs& lo, const DispatchArgs& a, hipStream_t stream);
+
 struct ReduceArgs {
     const void* partials;      // bf16 [R, T, hidden]
     const void* local;         // bf16 [T, hidden] or nullptr

@@ -160,6 +160,25 @@ ep_status_t ep_dispatch(ep_handle_t handle, const void* x, int hidden, const flo
                         void* stream);
 
 /*
+ * ep_layout_dispatch -- ep_get_layout and ep_dispatch in one call: the same arguments, the same outputs and the
+ * same handle, bit for bit.  For num_tokens <= 256 (the decode shape) both run in a single kernel launch: every
+ * workgroup builds the small layout in LDS and dispatches its share of the rows, so no launch waits for another
+ * ([DeepEP->MegaMoE] §4.3: at small batches launch overhead, not bytes, sets the time; [DeepEP-hotdry]
+ * 性能基准: the low-latency decode path).  Larger batches run the layout and the dispatch launches back to back.
+ *
+ *   Arguments as in ep_get_layout (topk_idx .. num_invalid_topk, handle_out) and ep_dispatch (x .. out).
+ *   Every argument of both is validated before anything is enqueued; on an error no handle is created.
+ *   The handle is reusable afterwards exactly like one from ep_get_layout.
+ */
+ep_status_t ep_layout_dispatch(const int64_t* topk_idx, int num_tokens, int num_topk, int num_experts, int num_ranks,
+                               int rank, int expert_alignment, void* workspace, size_t workspace_bytes,
+                               int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert,
+                               uint8_t* is_token_in_rank, int32_t* psum_num_recv_tokens_per_expert,
+                               int32_t* num_invalid_topk, const void* x, int hidden, const float* topk_weights,
+                               ep_dtype_t recv_dtype, int do_expand, int do_zero_padding,
+                               const ep_dispatch_out_t* out, ep_handle_t* handle_out, void* stream);
+
+/*
  * ep_dispatch_rows -- the receiver's copy epilogue ([DeepEP->MegaMoE] §2.4: rows that arrived
  * destination-major are placed expert-major, each at its expert's rows).  Rows already carry their receive
  * format (the bytes and scales of a sender's send window), so nothing is converted.

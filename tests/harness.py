@@ -21,7 +21,10 @@ ATOL, RTOL = 1e-2, 8e-3     # combine tolerance: |gpu - oracle| <= ATOL + RTOL *
 
 def dispatch_outputs_with_canary(ep, h, hidden, fp8, dev, do_expand=True):
     """Dispatch output tensors, pre-filled with canaries (the binding itself never initialises them)."""
-    o = ep.alloc_dispatch_outputs(h, hidden, fp8, device=dev, do_expand=do_expand)
+    return fill_canaries(ep.alloc_dispatch_outputs(h, hidden, fp8, device=dev, do_expand=do_expand))
+
+
+def fill_canaries(o):
     for k, t in o.items():
         if t is None:
             continue

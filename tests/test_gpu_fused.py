@@ -1,0 +1,123 @@
+"""GPU parity of ep_layout_dispatch: the layout and the dispatch of one call (one kernel launch for <= 256
+tokens, every workgroup building the layout in LDS; two launches above that).
+
+Every case compares the layout outputs and every dispatch output (canary-filled, so rows that must stay
+untouched are checked too) bit for bit with the oracle, then reuses the handle the call returned: an
+ep_dispatch in the other mode (expert-major after token-major and the reverse) and an ep_combine must match
+the oracle too, which checks that the single launch left the handle's workspace (slot map, per-rank token
+rows, padding-row list, counts) complete."""
+import numpy as np
+import pytest
+import torch
+
+import harness as Hn
+import oracle as O
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def ep():
+    import combine_get_dispatch_03_amd as ep
+    return ep
+
+
+def _canary_outputs(ep, c, do_expand):
+    """Dispatch outputs for config c, canary-filled (sized from a handle-less shape description)."""
+    tmp = ep.Handle(None, torch.empty(0, dtype=torch.int64), None, c.num_tokens, c.num_topk, c.num_experts,
+                    c.num_ranks, c.rank, c.expert_alignment)
+    return Hn.fill_canaries(ep.alloc_dispatch_outputs(tmp, c.hidden, c.fp8, device=DEV, do_expand=do_expand))
+
+
+def _check(ep, inp, do_expand=True):
+    c = inp["cfg"]
+    T, H = c.num_tokens, c.hidden
+    x, w = inp["x"].to(DEV), inp["topk_weights"].to(DEV)
+    olay, od = Hn.oracle_run(inp, do_expand=do_expand)
+    out = _canary_outputs(ep, c, do_expand)
+    h, glay, gout = ep.ep_layout_dispatch(inp["topk_idx"].to(DEV), x, c.num_experts, c.num_ranks, c.rank,
+                                          c.expert_alignment, w, fp8=c.fp8, do_expand=do_expand,
+                                          do_zero_padding=c.zero_padding, out=out)
+    torch.cuda.synchronize()
+    Hn.assert_layout_equal(glay, olay, c)
+    Hn.assert_dispatch_equal(gout, od, c)
+    # the handle is complete: dispatch in the other mode, then combine
+    _, od2 = Hn.oracle_run(inp, do_expand=not do_expand)
+    out2 = Hn.dispatch_outputs_with_canary(ep, h, H, c.fp8, DEV, do_expand=not do_expand)
+    ep.ep_dispatch(h, x, w, fp8=c.fp8, do_expand=not do_expand, do_zero_padding=c.zero_padding, out=out2)
+    Hn.assert_dispatch_equal(out2, od2, c)
+    y = W.random_expert_outputs(max(h.recv_capacity, 1), H, seed=T + 11, device=DEV)
+    got = ep.ep_combine(h, y, w)
+    torch.cuda.synchronize()
+    ref = O.combine(Hn.to_np(y), olay["slot"], inp["topk_weights"].numpy(), None)
+    ok, mabs, mrel, nbad = Hn.combine_check(Hn.to_np(got), ref)
+    assert ok, (mabs, mrel, nbad)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+@pytest.mark.parametrize("do_expand", [True, False])
+def test_fused_workloads(ep, name, do_expand):
+    print("[fused] workload %s do_expand=%d" % (name, do_expand), flush=True)
+    _check(ep, W.make_inputs(name), do_expand)
+
+
+CASES = [
+    # T, K, E, R, rank, A, H, fp8, zero_pad, kind
+    (0, 4, 8, 2, 1, 16, 256, True, True, "uniform"),
+    (1, 1, 1, 1, 0, 1, 128, True, True, "uniform"),
+    (1, 8, 256, 1, 0, 128, 7168, True, True, "uniform"),
+    (200, 6, 64, 1, 0, 16, 384, True, True, "uniform"),       # ragged tile, H not a multiple of 1024
+    (256, 8, 256, 4, 1, 64, 512, True, True, "uniform"),      # exactly one tile, with send windows
+    (255, 3, 24, 3, 2, 7, 136, False, True, "dup"),           # BF16, duplicates, H % 128 != 0
+    (256, 32, 1024, 1, 0, 1, 8, False, False, "uniform"),     # K and E at their limits, tiny rows, no padding
+    (256, 4, 128, 64, 63, 5, 256, True, False, "uniform"),    # 64 ranks, last rank
+    (200, 5, 40, 4, 1, 1000, 1024, True, True, "invalid"),    # large alignment (loops over padding), invalid ids
+    (256, 8, 256, 8, 3, 128, 2048, True, True, "skew"),       # one hot expert
+    (128, 8, 256, 1, 0, 128, 7168, True, False, "uniform"),   # decode shape without zero padding
+    (300, 4, 32, 2, 0, 8, 256, False, True, "uniform"),       # two tiles: the two-launch path
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[str(i) for i in range(len(CASES))])
+@pytest.mark.parametrize("do_expand", [True, False])
+def test_fused_edges(ep, case, do_expand):
+    T, K, E, R, rank, A, H, fp8, zp, kind = case
+    print("[fused edge] T=%d K=%d E=%d R=%d rank=%d A=%d H=%d fp8=%d zp=%d %s" % case, "expand=%d" % do_expand,
+          flush=True)
+    gen = torch.Generator().manual_seed(T + 7 * K + E)
+    if kind == "dup":
+        idx = torch.randint(0, E, (T, K), generator=gen)
+    elif kind == "skew":
+        idx = W.route_uniform_distinct(T, E, K, gen)
+        hot = 3 * (E // 8) + 1
+        idx[:, 1:] = torch.where(idx[:, 1:] == hot, 0, idx[:, 1:])
+        idx[:, 0] = hot
+    else:
+        idx = W.route_uniform_distinct(T, E, K, gen) if T > 0 else torch.zeros(0, K, dtype=torch.int64)
+    if kind == "invalid" and T > 0:
+        idx[::7, 0] = -1
+        idx[3::11, K - 1] = E + 5
+        idx[5::13, 1] = -9
+    w = W.softmax_weights(torch.randn(T, K, generator=gen))
+    x = W.normal_bf16((T, H), gen)
+    cfg = W.Config("edge", T, H, E, K, kind, A, zp, fp8, num_ranks=R, rank=rank)
+    _check(ep, dict(cfg=cfg, topk_idx=idx.contiguous(), topk_weights=w, x=x, bias=None), do_expand)
+
+
+def test_fused_validation(ep):
+    inp = W.make_inputs("decode")
+    c = inp["cfg"]
+    idx = inp["topk_idx"].to(DEV)
+    x = inp["x"].to(DEV)
+    with pytest.raises(ep.EPError, match="hidden"):
+        ep.ep_layout_dispatch(idx, x[:, :100].contiguous(), c.num_experts, expert_alignment=128)
+    nb = ep.ep_layout_workspace_bytes(c.num_tokens, c.num_topk, c.num_experts, 1, 128)
+    ws = torch.empty(nb + 256, dtype=torch.uint8, device=DEV)[16:]
+    with pytest.raises(ep.EPError, match="256-byte"):
+        ep.ep_layout_dispatch(idx, x, c.num_experts, expert_alignment=128, workspace=ws)
+    short = ep.alloc_dispatch_outputs(ep.Handle(None, idx, None, c.num_tokens, c.num_topk, c.num_experts, 1, 0, 128),
+                                      c.hidden, True, device=DEV, recv_capacity=100)
+    with pytest.raises(ep.EPError, match="recv_capacity"):
+        ep.ep_layout_dispatch(idx, x, c.num_experts, expert_alignment=128, out=short)
