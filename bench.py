@@ -147,11 +147,11 @@ def measure_epilogues(ep, W, dev, n):
         w = W.softmax_weights(torch.randn(T, K, generator=gen))
         mine = (idx < El).any(dim=1)
         sel = torch.nonzero(mine).flatten()
-        n = sel.numel()
+        ns = sel.numel()
         loc = torch.where(idx[sel] < El, idx[sel], torch.full_like(idx[sel], -1))
-        tk[s * T:s * T + n] = loc
-        tw[s * T:s * T + n] = w[sel]
-        n_valid += n
+        tk[s * T:s * T + ns] = loc
+        tw[s * T:s * T + ns] = w[sel]
+        n_valid += ns
     rows = torch.randint(0, 0x7E, (R * T, H), generator=gen, dtype=torch.uint8).to(dev)
     sc = torch.rand(R * T, G, generator=gen).to(dev)
     tk, tw = tk.to(dev), tw.to(dev)

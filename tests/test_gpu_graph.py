@@ -1,7 +1,8 @@
 """The whole path is capturable into a HIP graph: no call synchronises, allocates or copies to the host.
-The decode-shaped workload (layout -> FP8 dispatch -> combine) is captured once and replayed several times,
-with eager work between replays (canary refills of every output, a new x between replays); every replay
-must equal the eager results bit for bit."""
+The decode-shaped workload (layout -> FP8 dispatch -> combine, as three calls or as the one-launch
+ep_layout_dispatch + combine) is captured once and replayed several times, with eager work between replays
+(canary refills of every output, a new x between replays); every replay must equal the eager results bit for
+bit."""
 import numpy as np
 import pytest
 import torch
@@ -26,8 +27,8 @@ def _fill_canary(t):
         t.fill_(-7)
 
 
-@pytest.mark.parametrize("name", ["decode", "tiny"])
-def test_graph_capture_and_replay(name):
+@pytest.mark.parametrize("name,fused", [("decode", False), ("tiny", False), ("decode", True), ("tiny", True)])
+def test_graph_capture_and_replay(name, fused):
     import combine_get_dispatch_03_amd as ep
 
     inp = W.make_inputs(name)
@@ -54,8 +55,12 @@ def test_graph_capture_and_replay(name):
             _fill_canary(t)
 
     def run():
-        h, _ = ep.ep_get_layout(idx, E, R, 0, A, workspace=ws, outputs=lay)
-        ep.ep_dispatch(h, x, w, fp8=c.fp8, do_zero_padding=c.zero_padding, out=dout)
+        if fused:
+            h, _, _ = ep.ep_layout_dispatch(idx, x, E, R, 0, A, w, fp8=c.fp8, do_zero_padding=c.zero_padding,
+                                            out=dout, workspace=ws, outputs=lay)
+        else:
+            h, _ = ep.ep_get_layout(idx, E, R, 0, A, workspace=ws, outputs=lay)
+            ep.ep_dispatch(h, x, w, fp8=c.fp8, do_zero_padding=c.zero_padding, out=dout)
         ep.ep_combine(h, y, w, None, out=out)
         return h
 
