@@ -33,10 +33,11 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0        # MI355X published HBM3E peak
 WORKLOAD = "prefill"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill.json")
+# the source files each kernel is compiled from (their hash marks counter figures taken from an older kernel)
 KERNEL_SOURCES = {
-    "k_dispatch_fp8": "ep_dispatch.hip",
-    "k_combine": "ep_combine.hip",
-    "layout": "ep_layout.hip",
+    "k_dispatch_fp8": ("ep_dispatch.hip", "ep_dispatch_core.hpp", "ep_device.hpp"),
+    "k_combine": ("ep_combine.hip", "ep_device.hpp"),
+    "layout": ("ep_layout.hip", "ep_layout_core.hpp", "ep_device.hpp"),
 }
 
 
@@ -76,10 +77,12 @@ def bytes_model(cfg, counts):
     return dict(layout=layout, dispatch=dispatch, combine=combine, row_bytes=row_b)
 
 
-def source_hash(fname):
-    p = os.path.join(ROOT, "combine_get_dispatch_03_amd", "csrc", fname)
-    with open(p, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(fnames):
+    h = hashlib.sha256()
+    for fname in fnames:
+        with open(os.path.join(ROOT, "combine_get_dispatch_03_amd", "csrc", fname), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(kernel):
