@@ -53,11 +53,19 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
     return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
 
-// XOR-butterfly max over groups of 8 consecutive lanes (lanes 8g..8g+7).
+// Lane permutation within rows of 16 lanes by a DPP control (every lane has a source for the controls used here).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+// Max over groups of 8 consecutive lanes (lanes 8g..8g+7), in registers: swap neighbours (quad_perm 1,0,3,2),
+// swap pairs (quad_perm 2,3,0,1), then each lane meets the other quad of its 8 through the half-row mirror
+// (lane i <-> lane 7 - i within each 8).
 __device__ __forceinline__ float group8_max(float v) {
-    v = fmaxf(v, __shfl_xor(v, 1));
-    v = fmaxf(v, __shfl_xor(v, 2));
-    v = fmaxf(v, __shfl_xor(v, 4));
+    v = fmaxf(v, dpp_f<0xB1>(v));     // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp_f<0x4E>(v));     // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp_f<0x141>(v));    // row_half_mirror
     return v;
 }
 

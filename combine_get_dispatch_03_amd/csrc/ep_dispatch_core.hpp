@@ -104,7 +104,7 @@ __device__ __forceinline__ void token_meta(const Params& p, int t, int lane, int
 }
 
 // FP8 segment st of token t: channels [1024 st, 1024 st + 1024).  Each lane loads 32 contiguous bytes (16 bf16
-// channels); eight lanes form one 128-channel group whose max |x| comes from three xor-shuffles; the lane casts
+// channels); eight lanes form one 128-channel group whose max |x| comes from three DPP lane swaps; the lane casts
 // its 16 channels to 16 e4m3 bytes and stores them as one 16-byte vector to every destination row, together
 // with the segment's 8 group scales.
 // The segment's source bytes, loaded by fp8_load before the destinations are known (so the loads can overlap
@@ -150,10 +150,10 @@ __device__ __forceinline__ void fp8_emit(const Params& p, int st, int lane, cons
 #pragma unroll
     for (int k = 0; k < 4; ++k)
         q[k] = pack_e4m3x4(f[4 * k] * inv, f[4 * k + 1] * inv, f[4 * k + 2] * inv, f[4 * k + 3] * inv);
-    // lane g < 8 takes the scale of group 8 st + g, held by lane 8 g
-    const float sg = __shfl(scale, 8 * (lane & 7));
-    const int g = st * 8 + lane;
-    const bool sc_lane = lane < 8 && g < G;
+    // lane 8 j stores the scale of group 8 st + j: the 8 stores of a segment are contiguous (one 32-byte write)
+    const float sg = scale;
+    const int g = st * 8 + (lane >> 3);
+    const bool sc_lane = (lane & 7) == 0 && g < G;
     for (uint64_t mm = lmask; mm != 0; mm &= mm - 1) {
         const int s = readlane(ds, __builtin_ctzll(mm));
         if (active) st_nt(reinterpret_cast<u32x4*>(p.recv_x + (int64_t)s * H) + st * kWave + lane, q);
