@@ -3,7 +3,10 @@
 // allocates device memory or synchronises.
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <new>
+#include <set>
+#include <utility>
 
 #include "ep_internal.hpp"
 
@@ -49,6 +52,19 @@ const Handle* check_handle(ep_handle_t h) {
 }
 
 }  // namespace
+
+hipError_t allow_dynamic_lds(const void* kernel, int bytes) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    static std::mutex mu;
+    static std::set<std::pair<const void*, int>> done;
+    std::lock_guard<std::mutex> lock(mu);
+    if (done.count({kernel, dev}) != 0) return hipSuccess;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess) done.insert({kernel, dev});
+    return e;
+}
 
 Workspace carve_workspace(void* base, int T, int K, int E, int R, int A) {
     const int ntiles = (T + kLayoutTileTokens - 1) / kLayoutTileTokens;

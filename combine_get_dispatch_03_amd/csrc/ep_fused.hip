@@ -19,7 +19,6 @@
 //                           row's metadata;
 //   zero-padding items      (row number, segment) pairs, zeros written as in the dispatch kernels.
 #include <algorithm>
-#include <mutex>
 
 #include "ep_dispatch_core.hpp"
 #include "ep_layout_core.hpp"
@@ -125,18 +124,6 @@ __global__ __launch_bounds__(kThreads) void k_layout_dispatch_small(FusedArgs f,
     }
 }
 
-template <bool FP8>
-hipError_t allow_fused_lds() {
-    static std::once_flag once;
-    static hipError_t err = hipSuccess;
-    std::call_once(once, [] {
-        err = hipFuncSetAttribute(reinterpret_cast<const void*>(k_layout_dispatch_small<FP8>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (int)fused_lds_bytes(kMaxExperts, kMaxTopk, kMaxRanks, kMaxExperts));
-    });
-    return err;
-}
-
 }  // namespace
 
 hipError_t launch_layout_dispatch(const Handle& h, const LayoutOutputs& out, const DispatchArgs& a,
@@ -170,7 +157,9 @@ hipError_t launch_layout_dispatch(const Handle& h, const LayoutOutputs& out, con
 
     const size_t lds = fused_lds_bytes(h.E, h.K, h.R, h.El);
     if (lds > 65536) {
-        const hipError_t e = fp8 ? allow_fused_lds<true>() : allow_fused_lds<false>();
+        const void* k = fp8 ? reinterpret_cast<const void*>(k_layout_dispatch_small<true>)
+                            : reinterpret_cast<const void*>(k_layout_dispatch_small<false>);
+        const hipError_t e = allow_dynamic_lds(k, (int)fused_lds_bytes(kMaxExperts, kMaxTopk, kMaxRanks, kMaxExperts));
         if (e != hipSuccess) return e;
     }
     if (fp8)

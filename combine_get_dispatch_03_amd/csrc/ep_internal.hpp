@@ -47,6 +47,10 @@ struct Handle {
     Workspace ws;
 };
 
+// Opt `kernel` in to `bytes` of dynamic LDS (above the 64 KiB default; gfx950 has 160 KiB per CU) on the current
+// device, once per (kernel, device); thread-safe.
+hipError_t allow_dynamic_lds(const void* kernel, int bytes);
+
 // ---- launchers (each enqueues on `stream` and returns hipGetLastError()) -----------------------------
 
 struct LayoutOutputs {

@@ -15,8 +15,6 @@
 // More than one tile: k_layout_count (counting, tile rows + tile-local ranks to the workspace) then
 // k_layout_finalize (one block per tile, each re-summing the tile rows it needs).  One tile (<= 256 tokens,
 // the decode shape): k_layout_single does both phases in one block without leaving LDS, in one launch.
-#include <mutex>
-
 #include "ep_layout_core.hpp"
 
 namespace ep {
@@ -161,14 +159,6 @@ size_t single_lds_bytes(int E, int K, int R, int epr) {
     return count_lds_bytes(E, K, R) + sizeof(int) * (2 * (size_t)(epr + 1) + 2 * kWaves);
 }
 
-// Opt a kernel in to more than 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU); once per kernel.
-hipError_t allow_lds(const void* kernel, size_t max_bytes, std::once_flag& once, hipError_t& err) {
-    std::call_once(once, [&] {
-        err = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_bytes);
-    });
-    return err;
-}
-
 }  // namespace
 
 hipError_t launch_layout(const Handle& h, const LayoutOutputs& out, hipStream_t stream) {
@@ -182,11 +172,9 @@ hipError_t launch_layout(const Handle& h, const LayoutOutputs& out, hipStream_t 
     if (h.ntiles == 1) {
         const size_t lds = single_lds_bytes(h.E, h.K, h.R, epr);
         if (lds > 65536) {
-            static std::once_flag once;
-            static hipError_t err = hipSuccess;
-            if (allow_lds(reinterpret_cast<const void*>(k_layout_single),
-                          single_lds_bytes(kMaxExperts, kMaxTopk, kMaxRanks, kMaxExperts), once, err) != hipSuccess)
-                return err;
+            const hipError_t err = allow_dynamic_lds(reinterpret_cast<const void*>(k_layout_single),
+                                                     (int)single_lds_bytes(kMaxExperts, kMaxTopk, kMaxRanks, kMaxExperts));
+            if (err != hipSuccess) return err;
         }
         hipLaunchKernelGGL(k_layout_single, dim3(1), dim3(kThreads), lds, stream, h.topk_idx, h.T, h.K, h.E, h.R,
                            h.rank, epr, h.A, nbits, h.ws.slot, send, out.is_token_in_rank, o);
@@ -195,11 +183,9 @@ hipError_t launch_layout(const Handle& h, const LayoutOutputs& out, hipStream_t 
     if (h.ntiles > 1) {
         const size_t lds = count_lds_bytes(h.E, h.K, h.R);
         if (lds > 65536) {
-            static std::once_flag once;
-            static hipError_t err = hipSuccess;
-            if (allow_lds(reinterpret_cast<const void*>(k_layout_count),
-                          count_lds_bytes(kMaxExperts, kMaxTopk, kMaxRanks), once, err) != hipSuccess)
-                return err;
+            const hipError_t err = allow_dynamic_lds(reinterpret_cast<const void*>(k_layout_count),
+                                                     (int)count_lds_bytes(kMaxExperts, kMaxTopk, kMaxRanks));
+            if (err != hipSuccess) return err;
         }
         hipLaunchKernelGGL(k_layout_count, dim3(h.ntiles), dim3(kThreads), lds, stream, h.topk_idx, h.T, h.K, h.E,
                            h.R, epr, nbits, h.ws.tile_hist, h.ws.slot, send, out.is_token_in_rank);
