@@ -27,6 +27,9 @@ namespace ep {
 namespace {
 
 constexpr int kMaxPadWaves = 4096;   // padding passes loop beyond this many waves instead of growing the grid
+constexpr int kMinBlocks = 256;      // at least one workgroup per CU of an MI355X: the stores of the dispatch need
+                                     // the store paths of the whole chip, and the layout repeated per workgroup is
+                                     // latency, not throughput
 constexpr uint16_t kNoRow = 0xFFFF;  // per-rank token row "none" in LDS (rows are < 256)
 
 __device__ __forceinline__ int row_or_none(uint16_t v) { return v == kNoRow ? -1 : (int)v; }
@@ -57,7 +60,9 @@ __global__ __launch_bounds__(kThreads) void k_layout_dispatch_small(FusedArgs f,
     // the token item's source bytes do not depend on the layout: their loads are issued together with the
     // layout's entry loads and stay in flight through the layout work
     const int lane = lane_id();
-    const int64_t gw = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    // work items are strided over the workgroups (item = wave * workgroups + workgroup), so that a grid larger
+    // than the items spreads them over every CU instead of filling the first workgroups
+    const int64_t gw = (int64_t)(threadIdx.x >> 6) * gridDim.x + blockIdx.x;
     const bool tok = gw < p.ntok_items;
     const int t = tok ? (int)(gw / p.nstep) : 0, st = tok ? (int)(gw % p.nstep) : 0;
     Fp8Src v8;
@@ -140,7 +145,7 @@ hipError_t launch_layout_dispatch(const Handle& h, const LayoutOutputs& out, con
     int64_t pad_waves = (max_pad + kWave - 1) / kWave;
     if (p.zero_pad && !p.token_major) pad_waves = std::max(pad_waves, (max_pad * p.nstep + kPadItemsPerWave - 1) / kPadItemsPerWave);
     nwaves = std::max(nwaves, std::min(pad_waves, (int64_t)kMaxPadWaves));
-    const int64_t nblocks = (nwaves + kWaves - 1) / kWaves;
+    const int64_t nblocks = std::max<int64_t>((nwaves + kWaves - 1) / kWaves, kMinBlocks);
     p.nwaves = nblocks * kWaves;
 
     FusedArgs f;

@@ -14,7 +14,10 @@
 //                      prefix, global counts, the dense padding-row list, and the final row of every entry.
 // More than one tile: k_layout_count (counting, tile rows + tile-local ranks to the workspace) then
 // k_layout_finalize (one block per tile, each re-summing the tile rows it needs).  One tile (<= 256 tokens,
-// the decode shape): k_layout_single does both phases in one block without leaving LDS, in one launch.
+// the decode shape): k_layout_single does both phases without leaving LDS, in one launch; each of its
+// workgroups repeats the small layout and writes a share of the outputs.
+#include <algorithm>
+
 #include "ep_layout_core.hpp"
 
 namespace ep {
@@ -129,7 +132,11 @@ __global__ __launch_bounds__(kThreads) void k_layout_finalize(
     }
 }
 
-// ---- single-tile path (T <= 256): both phases in one block, one launch ------------------------------------
+// ---- single-tile path (T <= 256): both phases in one launch -------------------------------------------------
+// Every workgroup computes the whole (small) layout in LDS; workgroup 0 writes the counts, the membership and the
+// per-rank token rows, and the workgroups share the slot map and the padding list (finalize_core's split).
+
+constexpr int kSingleMaxBlocks = 64;
 
 __global__ __launch_bounds__(kThreads) void k_layout_single(
     const int64_t* __restrict__ idx, int T, int K, int E, int R, int rank, int epr, int A, int nbits,
@@ -138,11 +145,12 @@ __global__ __launch_bounds__(kThreads) void k_layout_single(
     int* psum = reinterpret_cast<int*>(layout_smem + count_lds_bytes(E, K, R));   // [epr + 1]
     int* padpre = psum + epr + 1;                                                 // [epr + 1]
     int* scratch = padpre + epr + 1;                                              // [2 * kWaves]
-    const int tid = threadIdx.x;
     const int lo = rank * epr;
-    const uint64_t mask = count_tile(idx, T, K, E, R, epr, nbits, 0, L, in_rank_out);
+    const bool first = blockIdx.x == 0;
+    const uint64_t mask = count_tile(idx, T, K, E, R, epr, nbits, 0, L, first ? in_rank_out : nullptr);
     finalize_core(E, R, rank, epr, A, L.row, psum, padpre, scratch, o);
-    for (int j = tid; j < T * K; j += kThreads) {
+    // this workgroup's slice of the slot map
+    for (int j = (int)blockIdx.x * kThreads + (int)threadIdx.x; j < T * K; j += (int)gridDim.x * kThreads) {
         const int p = L.ent[j];
         int s = -1;
         if (p >= 0) {
@@ -152,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void k_layout_single(
         }
         slot[j] = s;
     }
-    send_rows(L, mask, T, R, 0, send_slot);
+    if (first) send_rows(L, mask, T, R, 0, send_slot);
 }
 
 size_t single_lds_bytes(int E, int K, int R, int epr) {
@@ -176,7 +184,10 @@ hipError_t launch_layout(const Handle& h, const LayoutOutputs& out, hipStream_t 
                                                      (int)single_lds_bytes(kMaxExperts, kMaxTopk, kMaxRanks, kMaxExperts));
             if (err != hipSuccess) return err;
         }
-        hipLaunchKernelGGL(k_layout_single, dim3(1), dim3(kThreads), lds, stream, h.topk_idx, h.T, h.K, h.E, h.R,
+        // one workgroup per 16 local experts (one expert's padding rows per wave), each repeating the small layout
+        // in LDS, so that the padding list and the slot map are written by several CUs
+        const int nblk = std::min(kSingleMaxBlocks, std::max(1, (epr + kWaves - 1) / kWaves));
+        hipLaunchKernelGGL(k_layout_single, dim3(nblk), dim3(kThreads), lds, stream, h.topk_idx, h.T, h.K, h.E, h.R,
                            h.rank, epr, h.A, nbits, h.ws.slot, send, out.is_token_in_rank, o);
         return hipGetLastError();
     }
