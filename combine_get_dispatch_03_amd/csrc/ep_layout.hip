@@ -74,23 +74,22 @@ __global__ __launch_bounds__(kThreads) void k_layout_finalize(
         pk[i] = j < ntok * K ? slot[ent0 + j] : -1;
     }
 
-    // column sums of the tile rows: (part, column) per thread, all loads independent
+    // column sums of the tile rows: (part, column) per thread; its tiles are read 8 at a time, all 8 loads in
+    // flight together (one round trip per 8 tiles)
     const int P = NC <= kThreads ? kThreads / NC : 1;
     for (int q = tid; q < P * NC; q += kThreads) {
         const int col = q % NC, part = q / NC;
         const int t0 = (int)((int64_t)part * ntiles / P), t1 = (int)((int64_t)(part + 1) * ntiles / P);
         int sb = 0, st = 0;
-        int ti = t0;
-        for (; ti + 4 <= t1; ti += 4) {
-            const int v0 = tile_hist[(int64_t)ti * NC + col], v1 = tile_hist[(int64_t)(ti + 1) * NC + col];
-            const int v2 = tile_hist[(int64_t)(ti + 2) * NC + col], v3 = tile_hist[(int64_t)(ti + 3) * NC + col];
-            st += v0 + v1 + v2 + v3;
-            sb += (ti < tile ? v0 : 0) + (ti + 1 < tile ? v1 : 0) + (ti + 2 < tile ? v2 : 0) + (ti + 3 < tile ? v3 : 0);
-        }
-        for (; ti < t1; ++ti) {
-            const int v = tile_hist[(int64_t)ti * NC + col];
-            st += v;
-            if (ti < tile) sb += v;
+        for (int ti = t0; ti < t1; ti += 8) {
+            int v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = ti + u < t1 ? tile_hist[(int64_t)(ti + u) * NC + col] : 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                st += v[u];
+                sb += ti + u < tile ? v[u] : 0;
+            }
         }
         part_before[q] = sb;
         part_total[q] = st;
