@@ -372,6 +372,12 @@ def main():
         "combine": timed(lambda: ep.ep_combine(hk, y, w, bias, out=out), args.steps),
     }
 
+    def layout_then_dispatch():
+        h, _ = ep.ep_get_layout(idx, E, R, cfg.rank, cfg.expert_alignment, workspace=ws, outputs=lay_out)
+        ep.ep_dispatch(h, x, w, fp8=cfg.fp8, do_zero_padding=cfg.zero_padding, out=dout)
+
+    layout_dispatch_us = timed(layout_then_dispatch, args.steps) * 1e3
+
     # per-kernel samples with a cache flush before each (10 warm-up + N samples, the pages' method)
     flushed = None
     if args.flush_samples > 0:
@@ -388,6 +394,7 @@ def main():
                 fl["combine"].append(ev[2].elapsed_time(ev[3]))
         del junk
         flushed = {k: float(np.median(v)) for k, v in fl.items()}
+        flushed_min = {k: float(np.min(v)) for k, v in fl.items()}
 
     # device counts after the timed loop
     cnt = lay_out["num_tokens_per_expert"].cpu().numpy()
@@ -415,8 +422,11 @@ def main():
     if flushed is not None:
         for k in ("dispatch", "combine"):
             kern[k]["us_flushed_median"] = round(flushed[k] * 1e3, 2)
+            kern[k]["us_flushed_min"] = round(flushed_min[k] * 1e3, 2)
             kern[k]["GBps_flushed"] = round(gbps(bm[k], flushed[k]), 1)
         kern["layout"]["us_flushed_median"] = round(flushed["layout"] * 1e3, 2)
+        kern["layout"]["us_flushed_min"] = round(flushed_min["layout"] * 1e3, 2)
+    kern["layout_then_dispatch"] = dict(us=round(layout_dispatch_us, 2))
 
     dom = "dispatch" if avg["dispatch"] >= avg["combine"] else "combine"
     dom_kernel = {"dispatch": "k_dispatch_fp8", "combine": "k_combine"}[dom]
