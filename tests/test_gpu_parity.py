@@ -208,6 +208,9 @@ EDGE = [
     (4096, 8, 256, 8, 3, 128, 2048, True, True, "skew"),      # one hot expert owned by this rank
     (256, 8, 256, 4, 1, 64, 512, True, True, "uniform"),      # exactly one tile, with send windows
     (257, 3, 16, 2, 0, 8, 256, False, True, "invalid"),       # one token past a tile, BF16 windows
+    (40, 4, 16, 1, 0, 8, 32768, False, True, "uniform"),      # largest hidden: 64 KiB BF16 rows
+    (40, 4, 16, 2, 1, 8, 32768, True, True, "uniform"),       # largest hidden: 32 FP8 segments, windows
+    (65536, 8, 256, 1, 0, 128, 128, True, True, "uniform"),   # 256 layout tiles
 ]
 
 
