@@ -22,6 +22,10 @@ constexpr int kPackMask = (1 << kPackShift) - 1;
 constexpr int kBad = -2;                   // staged value of an entry < -1 or >= E
 constexpr int kMaxEntriesPerThread = kTile * kMaxTopk / kThreads;   // 8
 constexpr int kEntriesPerThreadMax = kMaxEntriesPerThread;
+// The token-mask work runs on the last 4 waves, so that for E <= 768 it overlaps the per-expert bases loop (which
+// runs on threads 0..E-1) instead of following it on the same threads.
+constexpr int kTokThread0 = kThreads - kTile;
+constexpr int kTokWave0 = kTokThread0 / 64;
 constexpr int kMaxCols = kMaxExperts + kMaxRanks + 1;               // columns of a tile row
 
 // ---- LDS of the counting phase ---------------------------------------------------------------------------
@@ -50,8 +54,9 @@ __device__ CountLds carve_count(unsigned char* base, int E, int K, int R) {
     return L;
 }
 
-// Counting phase for one tile.  Every thread of the block calls it; it ends with a barrier.  Returns, for
-// threads 0..255, the bit mask of ranks that token (tile start + tid) has an expert on (0 for others).
+// Counting phase for one tile.  Every thread of the block calls it; it ends with a barrier.  Returns, for the
+// token threads (the last 256 threads: token = tile start + tid - kTokThread0), the bit mask of ranks that the
+// token has an expert on (0 for the other threads).
 // `pre()` runs right after the tile's entry loads are issued and before they are used: a caller's loads that do
 // not depend on the layout go there, so that their latency overlaps the staging round trip and the rest of the
 // counting phase.
@@ -121,22 +126,23 @@ __device__ uint64_t count_tile(const int64_t* __restrict__ idx, int T, int K, in
         }
         L.row[e] = run;
     }
-    // threads 0..255 <-> tokens of the tile (waves 0..3): token-in-rank membership
-    const int t = tok_tile0 + tid;
-    const bool tv = tid < kTile && t < T;
+    // token threads (waves kTokWave0..kTokWave0+3) <-> tokens of the tile: token-in-rank membership
+    const int tt = tid - kTokThread0;
+    const int t = tok_tile0 + tt;
+    const bool tv = tt >= 0 && t < T;
     uint64_t mask = 0ull;
     if (tv) {
         for (int k = 0; k < K; ++k) {
-            const int p = L.ent[tid * K + k];
+            const int p = L.ent[tt * K + k];
             if (p >= 0) mask |= 1ull << ((p & kPackMask) / epr);
         }
     }
     if (tv && in_rank_out != nullptr)
         for (int r = 0; r < R; ++r) in_rank_out[(int64_t)t * R + r] = (uint8_t)((mask >> r) & 1ull);
-    if (w < 4) {
+    if (w >= kTokWave0) {
         for (int r = 0; r < R; ++r) {
             const uint64_t b = ballot((mask >> r) & 1ull);
-            if (lane == 0) L.rcnt_w[w * R + r] = popc64(b);
+            if (lane == 0) L.rcnt_w[(w - kTokWave0) * R + r] = popc64(b);
         }
     }
     __syncthreads();
@@ -159,18 +165,18 @@ __device__ uint64_t count_tile(const int64_t* __restrict__ idx, int T, int K, in
 
 // Per-rank token rows of the tile's tokens, from the rank masks of count_tile: the rank of the token among the
 // tile's earlier tokens with an expert on r (tile-local), or -1 when it has none there; handed to
-// put(t, r, row).  Threads 0..255 (one token each) take part.
+// put(t, r, row).  The token threads of count_tile (one token each) take part.
 template <class Put>
 __device__ __forceinline__ void token_rows(const CountLds& L, uint64_t mask, int T, int R, int tile, Put put) {
     const int tid = threadIdx.x, w = tid >> 6;
-    if (w >= 4) return;
-    const int t = tile * kTile + tid;
+    if (w < kTokWave0) return;
+    const int t = tile * kTile + tid - kTokThread0;
     const bool tv = t < T;
     const uint64_t lt = lanemask_lt();
     for (int r = 0; r < R; ++r) {
         const bool bit = (mask >> r) & 1ull;
         const uint64_t b = ballot(bit);
-        if (tv) put(t, r, bit ? L.rcnt_w[w * R + r] + popc64(b & lt) : -1);
+        if (tv) put(t, r, bit ? L.rcnt_w[(w - kTokWave0) * R + r] + popc64(b & lt) : -1);
     }
 }
 
