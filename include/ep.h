@@ -12,7 +12,8 @@
  *   ep_combine     weighted top-k reduction of expert outputs back to token order in BF16, plus bias
  *                  (ep_combine_tokens for the token-major rows);
  *   ep_dispatch_rows / ep_combine_reduce  the receiver's placement of rows that arrived from other ranks and
- *                  the source's sum of the rows those ranks return (the two ends of the exchange).
+ *                  the source's sum of the rows those ranks return (the two ends of the exchange);
+ *   ep_layout_dispatch  ep_get_layout + ep_dispatch in one call, one kernel launch for <= 256 tokens.
  *
  * Page names used in the citations:
  *   [DeepEP->MegaMoE]  "从 DeepEP 到 Mega MoE：MoE Runtime 演进的三向验证分析" (backyes.github.io)
@@ -26,8 +27,9 @@
  *   - All work is enqueued on `stream` (a hipStream_t; NULL = the default stream).  No call allocates device
  *     memory, copies to the host or synchronises: counts stay on the device, as with do_cpu_sync off
  *     ([MoE-comm] §二; [flops-record]: capacity-sized outputs and a device psum for the grouped GEMM).
- *   - Every argument is validated on the host before anything is enqueued.  On an error nothing is enqueued,
- *     no output is touched, the call returns a non-zero status and ep_last_error() describes it.
+ *   - Every argument is validated on the host before anything is enqueued.  On a validation error nothing is
+ *     enqueued, no output is touched, the call returns EP_ERR_INVALID_ARG and ep_last_error() describes it.
+ *     A failed launch returns EP_ERR_HIP; kernels of the same call enqueued before it may have run.
  *   - Memory is owned by the caller.  A buffer or handle must not be freed, resized or reused while an
  *     operation using it is still pending on its stream ([MoE-comm] §二, buffer and handle reuse).
  *   - Row-major layouts throughout.  x, y, out, bias, recv_x and send_x must be 16-byte aligned.
@@ -58,7 +60,7 @@ typedef enum ep_dtype {
     EP_DTYPE_FP8_E4M3 = 1     /* OCP e4m3fn rows + one fp32 scale per 128 channels                                 */
 } ep_dtype_t;
 
-typedef struct ep_handle* ep_handle_t;   /* opaque host object created by ep_get_layout */
+typedef struct ep_handle* ep_handle_t;   /* opaque host object created by ep_get_layout / ep_layout_dispatch */
 
 /* Rows the expert-major receive buffers (recv_x and friends, and y of ep_combine) must have:
  * num_tokens * num_topk + num_local_experts * (expert_alignment - 1), the worst case of padding every local
