@@ -78,3 +78,81 @@ def test_random_case(seed):
     torch.cuda.synchronize()
     ok, mabs, mrel, nbad = Hn.combine_check(Hn.to_np(got), ref)
     assert ok, (mabs, mrel, nbad)
+
+
+def _rows_case(seed):
+    rng = np.random.default_rng(5000 + seed)
+    El = int(rng.integers(1, 129))
+    N = int(rng.choice([0, 1, int(rng.integers(2, 256)), int(rng.integers(256, 900))]))
+    K = int(rng.integers(1, 9))
+    A = int(rng.choice([1, 4, 16, 128]))
+    rb = 16 * int(rng.integers(1, 513))
+    G = int(rng.choice([0, 0, int(rng.integers(1, 65))]))
+    idx = rng.integers(0, El, size=(N, K)).astype(np.int64)
+    if N:
+        idx[rng.random((N, K)) < 0.4] = -1                            # entries owned by other ranks
+        idx[rng.random(N) < 0.3] = -1                                 # rows not received
+    rows = rng.integers(0, 256, size=(N, rb), dtype=np.uint8)
+    sc = rng.random((N, G), dtype=np.float32) if G else None
+    w = rng.random((N, K), dtype=np.float32)
+    zp = bool(rng.random() < 0.5)
+    return idx, El, A, rows, sc, w, zp
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_random_receiver_placement(seed):
+    import combine_get_dispatch_03_amd as ep
+
+    idx, El, A, rows, sc, w, zp = _rows_case(seed)
+    N, rb = rows.shape
+    print("[random rows %d] N=%d K=%d El=%d A=%d row_bytes=%d G=%d zp=%d" % (
+        seed, N, idx.shape[1], El, A, rb, 0 if sc is None else sc.shape[1], zp), flush=True)
+    h, _ = ep.ep_get_layout(torch.from_numpy(idx).to(DEV), El, 1, 0, A)
+    cap = h.recv_capacity
+    G = 0 if sc is None else sc.shape[1]
+    out = Hn.fill_canaries(dict(
+        recv_x=torch.empty((cap, rb), dtype=torch.uint8, device=DEV),
+        recv_x_scales=torch.empty((cap, G), dtype=torch.float32, device=DEV) if G else None,
+        recv_src_idx=torch.empty(cap, dtype=torch.int32, device=DEV),
+        recv_topk_weights=torch.empty(cap, dtype=torch.float32, device=DEV)))
+    ep.ep_dispatch_rows(h, torch.from_numpy(rows).to(DEV), torch.from_numpy(sc).to(DEV) if G else None,
+                        torch.from_numpy(w).to(DEV), do_zero_padding=zp, out=out)
+    lay = O.layout(idx, El, 1, 0, A)
+    ref = O.dispatch_rows(rows, sc, idx, w, lay, El, A, zero_pad=zp, recv_fill=(Hn.CANARY_BYTE, Hn.CANARY_SCALE))
+    got = Hn.to_np(out["recv_x"])
+    assert np.array_equal(got, ref["recv_x"]), Hn._first_diff(got, ref["recv_x"])
+    if G:
+        assert np.array_equal(Hn.to_np(out["recv_x_scales"]).view(np.uint32), ref["recv_scales"].view(np.uint32))
+    assert np.array_equal(Hn.to_np(out["recv_src_idx"]), ref["recv_src"])
+    assert np.array_equal(Hn.to_np(out["recv_topk_weights"]).view(np.uint32), ref["recv_w"].view(np.uint32))
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_random_source_reduce(seed):
+    import combine_get_dispatch_03_amd as ep
+
+    rng = np.random.default_rng(7000 + seed)
+    R = int(rng.choice([1, 2, 3, 4, 8, 16]))
+    E = R * int(rng.integers(1, 33))
+    T = int(rng.choice([0, 1, int(rng.integers(2, 300)), int(rng.integers(300, 1200))]))
+    K = int(rng.integers(1, min(E, 8) + 1))
+    H = 8 * int(rng.integers(1, 257))
+    rank = int(rng.integers(0, R))
+    with_local, with_bias = bool(rng.random() < 0.7), bool(rng.random() < 0.5)
+    print("[random reduce %d] R=%d E=%d T=%d K=%d H=%d rank=%d local=%d bias=%d" % (
+        seed, R, E, T, K, H, rank, with_local, with_bias), flush=True)
+    idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int64) if T else \
+        np.zeros((0, K), np.int64)
+    gen = torch.Generator().manual_seed(seed)
+    parts = W.normal_bf16((R, T, H), gen)
+    local = W.normal_bf16((T, H), gen) if with_local else None
+    bias = W.normal_bf16((T, H), gen, 0.1) if with_bias else None
+    h, _ = ep.ep_get_layout(torch.from_numpy(idx).to(DEV), E, R, rank, 1)
+    out = ep.ep_combine_reduce(h, parts.to(DEV), local.to(DEV) if with_local else None,
+                               bias.to(DEV) if with_bias else None, hidden=H)
+    torch.cuda.synchronize()
+    lay = O.layout(idx, E, R, rank, 1)
+    ref = O.combine_reduce(W.bf16_bits(parts), lay["send_slot"], rank, W.bf16_bits(local) if with_local else None,
+                           W.bf16_bits(bias) if with_bias else None)
+    ok, mabs, mrel, nbad = Hn.combine_check(Hn.to_np(out), ref)
+    assert ok, (mabs, mrel, nbad)

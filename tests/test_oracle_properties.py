@@ -72,3 +72,84 @@ def test_dispatch_combine_places_every_entry_once(tab):
     out = O.combine(d["recv_x"], lay["slot"], None, None)
     k_local = np.array([int(((idx[t] >= lo) & (idx[t] < lo + epr)).sum()) for t in range(T)], np.float64)
     assert np.array_equal(out, (k_local * np.arange(1, T + 1))[:, None] * np.ones((1, H)))
+
+
+@st.composite
+def received(draw):
+    El = draw(st.integers(1, 8))
+    N = draw(st.integers(0, 30))
+    K = draw(st.integers(1, 5))
+    A = draw(st.sampled_from([1, 2, 4, 16]))
+    rb = 16 * draw(st.integers(1, 4))
+    G = draw(st.integers(0, 3))
+    ids = st.one_of(st.integers(0, El - 1), st.just(-1))
+    idx = np.array(draw(st.lists(ids, min_size=N * K, max_size=N * K)), np.int64).reshape(N, K)
+    seed = draw(st.integers(0, 2 ** 31 - 1))
+    return idx, El, A, rb, G, seed
+
+
+@settings(max_examples=80, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(received())
+def test_dispatch_rows_is_a_gather(rec):
+    """Receiver placement: every valid row r holds the bytes and scales of the received row that the layout maps
+    there (the row's source index, found by brute force over (i, k) with slot[i, k] == r), with that entry's
+    weight; padding rows carry -1 / 0 and zeros (zero padding); rows past psum[El] keep the canary."""
+    idx, El, A, rb, G, seed = rec
+    N, K = idx.shape
+    rng = np.random.default_rng(seed)
+    rows = rng.integers(0, 256, size=(N, rb), dtype=np.uint8)
+    sc = rng.random((N, G), dtype=np.float32) if G else None
+    w = rng.random((N, K), dtype=np.float32)
+    lay = O.layout(idx, El, 1, 0, A)
+    out = O.dispatch_rows(rows, sc, idx, w, lay, El, A, zero_pad=True, recv_fill=(0xA5, -3.0))
+    used = int(lay["psum"][-1])
+    where = {}
+    for i in range(N):
+        for k in range(K):
+            if lay["slot"][i, k] >= 0:
+                where[int(lay["slot"][i, k])] = (i, k)
+    for r in range(lay["cap"]):
+        if r in where:
+            i, k = where[r]
+            assert np.array_equal(out["recv_x"][r], rows[i]) and out["recv_src"][r] == i and out["recv_w"][r] == w[i, k]
+            if G:
+                assert np.array_equal(out["recv_scales"][r], sc[i])
+        elif r < used:
+            assert (out["recv_x"][r] == 0).all() and out["recv_src"][r] == -1 and out["recv_w"][r] == 0.0
+        else:
+            assert (out["recv_x"][r] == 0xA5).all() and out["recv_src"][r] == -7
+
+
+@settings(max_examples=80, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(st.integers(1, 8), st.integers(0, 20), st.integers(1, 4), st.integers(0, 2 ** 31 - 1), st.booleans(),
+       st.booleans())
+def test_combine_reduce_sums_what_each_rank_returned(R, T, epr, seed, with_local, with_bias):
+    """Source reduce: out[t] = local + sum over the other ranks holding t of their returned row + bias, checked
+    against a loop over ranks that locates each token's row in each window by counting the earlier tokens in
+    that rank (the send-window definition), independent of the oracle's per-rank token rows."""
+    rng = np.random.default_rng(seed)
+    E = R * epr
+    rank = int(rng.integers(0, R))
+    K = min(3, E)
+    idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int64) if T else \
+        np.zeros((0, K), np.int64)
+    H = 8
+    lay = O.layout(idx, E, R, rank, 1)
+    vals = np.arange(1, 129, dtype=np.float64) / 8.0                 # exact in BF16, small sums exact in fp64
+    parts = O.f64_to_bf16(rng.choice(vals, size=(R, T, H)))
+    local = O.f64_to_bf16(rng.choice(vals, size=(T, H))) if with_local else None
+    bias = O.f64_to_bf16(rng.choice(vals, size=(T, H))) if with_bias else None
+    got = O.combine_reduce(parts, lay["send_slot"], rank, local, bias)
+    P = O.bf16_to_f32(parts).astype(np.float64)
+    for t in range(T):
+        ref = np.zeros(H)
+        if with_local:
+            ref += O.bf16_to_f32(local[t])
+        for r in range(R):
+            if r == rank or not any(int(e) // epr == r for e in idx[t]):
+                continue
+            j = sum(1 for u in range(t) if any(int(e) // epr == r for e in idx[u]))
+            ref += P[r, j]
+        if with_bias:
+            ref += O.bf16_to_f32(bias[t])
+        assert np.array_equal(got[t], ref)
