@@ -84,15 +84,25 @@ __global__ __launch_bounds__(kBlock) void k_dispatch_fp8(Params p) {
     if (gw < p.ntok_items) {
         const int nit = (p.nstep + SPW - 1) / SPW;
         const int t = (int)(gw / nit), it = (int)(gw % nit);
+        // With send windows the source loads are issued before the destination loads, so that the two round
+        // trips overlap (5% faster at 8 ranks); without windows issuing them after measured 4% faster.
+        const bool early = p.send_slot != nullptr;
+        Fp8Src v[SPW];
+        if (early) {
+#pragma unroll
+            for (int j = 0; j < SPW; ++j)
+                if (it * SPW + j < p.nstep) v[j] = fp8_load(p, t, it * SPW + j, lane);
+        }
         int ds, js;
         uint64_t lmask, smask;
         token_dests(p, t, lane, ds, js, lmask, smask);
         if (it == 0) token_meta(p, t, lane, ds, js, lmask, smask);
         if ((lmask | smask) != 0) {
-            Fp8Src v[SPW];
+            if (!early) {
 #pragma unroll
-            for (int j = 0; j < SPW; ++j)
-                if (it * SPW + j < p.nstep) v[j] = fp8_load(p, t, it * SPW + j, lane);
+                for (int j = 0; j < SPW; ++j)
+                    if (it * SPW + j < p.nstep) v[j] = fp8_load(p, t, it * SPW + j, lane);
+            }
 #pragma unroll
             for (int j = 0; j < SPW; ++j)
                 if (it * SPW + j < p.nstep) fp8_emit(p, it * SPW + j, lane, v[j], ds, js, lmask, smask);
