@@ -8,8 +8,11 @@
 // Work items are 1 KiB output segments (512 channels): item (t, s) is segment s of token t's output row, so
 // a token's row is produced by several short waves instead of one long one, which keeps more gathers in
 // flight across the chip.  The token's valid (slot, weight) pairs are compacted into lanes 0..nv-1 and read
-// back as scalars, so every gather is a 64-lane x 16-byte row segment at a uniform base; up to kBatch gathers
-// are issued before the first FMA.  fp32 accumulation in ascending k, one RNE rounding to bf16 at the end.
+// back as scalars, so every gather is a 64-lane x 16-byte row segment at a uniform base.  The gathers are
+// straight-line code with no per-lane predicate (lanes past the row's end read chunk 0 and store nothing): a
+// predicated load whose consumer sits in another branch makes the compiler wait for every earlier load
+// before issuing it, so a batch would never have more than one gather in flight.  fp32 accumulation in
+// ascending k, one RNE rounding to bf16 at the end.
 #include "ep_device.hpp"
 #include "ep_internal.hpp"
 
@@ -18,7 +21,10 @@ namespace {
 
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
-constexpr int kBatch = 8;       // gathers issued before the first FMA
+// A wave with at least this many rows streams them (measured on the 4096 x 7168 top-8 shapes: combine is
+// fastest streaming only full top-8 tokens, the reduce, which also reads a local and a bias row, from 4).
+constexpr int kCombineStreamRows = 8;
+constexpr int kReduceStreamRows = 4;
 
 struct Params {
     const uint16_t* y;
@@ -54,6 +60,46 @@ __device__ __forceinline__ u32x4 pack8(const float* acc) {
     return r;
 }
 
+// N rows gathered from base + rows[kb + i] * stride (compacted in lanes, read back as scalars), all N issued
+// before the first use, then acc += w[kb + i] * row (WEIGHTED) or acc += row, in ascending i.
+template <int N, bool WEIGHTED>
+__device__ __forceinline__ void gather_acc(float* acc, const u32x4* base, int64_t stride, int rows, float w,
+                                           int kb) {
+    u32x4 v[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = ld_nt(base + (int64_t)readlane(rows, kb + i) * stride);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        if (WEIGHTED)
+            fma8(acc, readlane_f(w, kb + i), v[i]);
+        else
+            add8(acc, v[i]);
+    }
+}
+
+// All nv compacted rows.  A wave with few rows is latency-bound: they are issued together, as one unrolled
+// batch.  With STREAM or more the kernel is bandwidth-bound (every wave brings enough rows to keep HBM busy)
+// and a wave streams its rows one at a time, which measured about 1% faster than deeper queues.
+template <bool WEIGHTED, int STREAM>
+__device__ __forceinline__ void gather_all(float* acc, const u32x4* base, int64_t stride, int rows, float w,
+                                           int nv) {
+    static_assert(STREAM >= 1 && STREAM <= 8, "the batch switch below covers 1..7");
+    if (nv >= STREAM) {
+        for (int k = 0; k < nv; ++k) gather_acc<1, WEIGHTED>(acc, base, stride, rows, w, k);
+        return;
+    }
+    switch (nv) {
+        case 1: gather_acc<1, WEIGHTED>(acc, base, stride, rows, w, 0); break;
+        case 2: gather_acc<2, WEIGHTED>(acc, base, stride, rows, w, 0); break;
+        case 3: gather_acc<3, WEIGHTED>(acc, base, stride, rows, w, 0); break;
+        case 4: gather_acc<4, WEIGHTED>(acc, base, stride, rows, w, 0); break;
+        case 5: gather_acc<5, WEIGHTED>(acc, base, stride, rows, w, 0); break;
+        case 6: gather_acc<6, WEIGHTED>(acc, base, stride, rows, w, 0); break;
+        case 7: gather_acc<7, WEIGHTED>(acc, base, stride, rows, w, 0); break;
+        default: break;
+    }
+}
+
 __global__ __launch_bounds__(kBlock) void k_combine(Params p) {
     __shared__ int cs_lds[kWavesPerBlock][kWave];
     __shared__ float cw_lds[kWavesPerBlock][kWave];
@@ -83,18 +129,7 @@ __global__ __launch_bounds__(kBlock) void k_combine(Params p) {
     float acc[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
-    for (int kb = 0; kb < nv; kb += kBatch) {
-        u32x4 v[kBatch];
-#pragma unroll
-        for (int i = 0; i < kBatch; ++i) {
-            if (kb + i < nv && active)
-                v[i] = ld_nt(reinterpret_cast<const u32x4*>(p.y + (int64_t)readlane(cs, kb + i) * p.H) + c);
-        }
-#pragma unroll
-        for (int i = 0; i < kBatch; ++i) {
-            if (kb + i < nv && active) fma8(acc, readlane_f(cw, kb + i), v[i]);
-        }
-    }
+    gather_all<true, kCombineStreamRows>(acc, reinterpret_cast<const u32x4*>(p.y) + (active ? c : 0), p.H / 8, cs, cw, nv);
     if (!active) return;
     if (p.bias != nullptr) add8(acc, reinterpret_cast<const u32x4*>(p.bias + (int64_t)t * p.H)[c]);
     st_nt(reinterpret_cast<u32x4*>(p.out + (int64_t)t * p.H) + c, pack8(acc));
@@ -141,18 +176,7 @@ __global__ __launch_bounds__(kBlock) void k_combine_reduce(ReduceParams p) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
     if (active && p.local != nullptr) add8(acc, reinterpret_cast<const u32x4*>(p.local + (int64_t)t * p.H)[c]);
-    for (int kb = 0; kb < nv; kb += kBatch) {
-        u32x4 v[kBatch];
-#pragma unroll
-        for (int i = 0; i < kBatch; ++i) {
-            if (kb + i < nv && active)
-                v[i] = ld_nt(reinterpret_cast<const u32x4*>(p.partials + (int64_t)readlane(cs, kb + i) * p.H) + c);
-        }
-#pragma unroll
-        for (int i = 0; i < kBatch; ++i) {
-            if (kb + i < nv && active) add8(acc, v[i]);
-        }
-    }
+    gather_all<false, kReduceStreamRows>(acc, reinterpret_cast<const u32x4*>(p.partials) + (active ? c : 0), p.H / 8, cs, 0.0f, nv);
     if (!active) return;
     if (p.bias != nullptr) add8(acc, reinterpret_cast<const u32x4*>(p.bias + (int64_t)t * p.H)[c]);
     st_nt(reinterpret_cast<u32x4*>(p.out + (int64_t)t * p.H) + c, pack8(acc));
