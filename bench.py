@@ -3,10 +3,12 @@
 A step is one pass of the whole path over one batch of the prefill workload: ep_get_layout, then FP8 dispatch
 with zero padding, then the weighted BF16 combine (4096 tokens, hidden 7168, 256 experts in 8 groups with
 group-limited top-4-group / top-8 routing, alignment 128).  Inputs and expert outputs are resident in HBM
-before timing starts.  One step is captured into a HIP graph; W untimed warm-up replays, then exactly K timed
-replays bracketed by device syncs (the graph keeps host launch overhead out of the GPU's way).  Each
-call's average duration comes from HIP events on the launch stream around K back-to-back launches of that
-call, enqueued by the host ahead of the GPU.
+before timing starts.  W untimed warm-up steps, then exactly K timed steps bracketed by device syncs; the
+host enqueues the three calls of a step (~35 us of host time) far faster than the GPU runs them (~180 us),
+so no step waits on the host.  The same step captured in a HIP graph and replayed K times is reported too
+(`step_graph_replay_us`): each replay adds a few microseconds of GPU-side overhead that a graph of a whole
+model pass would spread over many more kernels.  Each call's average duration comes from HIP events on the
+launch stream around K back-to-back launches of that call, enqueued by the host ahead of the GPU.
 
 Prints one JSON line.  `value` is the step's effective HBM throughput: the algorithmic bytes of layout +
 dispatch + combine per step divided by the measured step time.  Algorithmic bytes are what the method must
@@ -327,26 +329,32 @@ def main():
             ev[3].record(stream)
         return h
 
-    # eager warm-up, then capture one step (layout -> dispatch -> combine) into a HIP graph
-    for _ in range(2):
+    # W untimed warm-up steps
+    for _ in range(max(args.warmup, 1)):
         step()
     torch.cuda.synchronize()
+
+    # timed region: exactly K steps, bracketed by device syncs
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # the same step as a HIP graph: W warm-up replays, then K timed replays
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         graph_handle = step()
     torch.cuda.synchronize()
-
-    for _ in range(args.warmup):
+    for _ in range(max(args.warmup, 1)):
         graph.replay()
     torch.cuda.synchronize()
-
-    # timed region: exactly K steps (graph replays), bracketed by device syncs
-    t0 = time.perf_counter()
+    g0 = time.perf_counter()
     for _ in range(args.steps):
         graph.replay()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    step_graph_us = (time.perf_counter() - g0) * 1e6 / args.steps
 
     # per-kernel durations: HIP events on the launch stream bracketing N back-to-back launches of one call
     # (an event marker between kernels costs several microseconds of GPU time, so each kernel is timed in a run
@@ -457,8 +465,9 @@ def main():
                     valid_rows=V, pad_rows=counts["P"], A_pad=round(int(psum[-1]) / max(V, 1), 4),
                     data_dtypes="x bf16 -> recv e4m3 + fp32 scales; y bf16 -> out bf16 (fp32 accumulate)"),
         tokens_per_s=round(T / (ms_per_step * 1e-3), 1),
-        timing="step: HIP graph replay of layout (2 kernels) + dispatch + combine; per call: events around K "
-               "back-to-back launches",
+        timing="step: K eager steps of layout (2 kernels) + dispatch + combine between device syncs; per call: "
+               "events around K back-to-back launches",
+        step_graph_replay_us=round(step_graph_us, 2),
         kernels=kern,
         roofline=roofline,
         cpu_baseline=cpu,
