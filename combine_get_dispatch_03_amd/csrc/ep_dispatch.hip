@@ -75,7 +75,12 @@ __device__ __forceinline__ void pad_items(const Params& p, int64_t gw, int lane,
 
 // FP8 token items cover SPW consecutive 1024-channel segments of a row (all loads first, then the casts and
 // stores segment by segment): longer contiguous writes per destination row than one segment per wave.
-template <int SPW>
+// EARLY (send windows present): the source loads are issued before the destination loads, so that the two
+// round trips overlap (5% faster at 8 ranks); without windows issuing them after measured faster.  It is a
+// template parameter, not a runtime flag: with both paths in one kernel the compiler cannot tell that the
+// early loads' registers are never pending on the late path, and puts a full wait (for every load and store
+// in flight, the segment-0 metadata stores included) in front of the late loads.
+template <int SPW, bool EARLY>
 __global__ __launch_bounds__(kBlock) void k_dispatch_fp8(Params p) {
     const int lane = lane_id();
     const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
@@ -84,11 +89,8 @@ __global__ __launch_bounds__(kBlock) void k_dispatch_fp8(Params p) {
     if (gw < p.ntok_items) {
         const int nit = (p.nstep + SPW - 1) / SPW;
         const int t = (int)(gw / nit), it = (int)(gw % nit);
-        // With send windows the source loads are issued before the destination loads, so that the two round
-        // trips overlap (5% faster at 8 ranks); without windows issuing them after measured 4% faster.
-        const bool early = p.send_slot != nullptr;
         Fp8Src v[SPW];
-        if (early) {
+        if (EARLY) {
 #pragma unroll
             for (int j = 0; j < SPW; ++j)
                 if (it * SPW + j < p.nstep) v[j] = fp8_load(p, t, it * SPW + j, lane);
@@ -96,13 +98,15 @@ __global__ __launch_bounds__(kBlock) void k_dispatch_fp8(Params p) {
         int ds, js;
         uint64_t lmask, smask;
         token_dests(p, t, lane, ds, js, lmask, smask);
-        if (it == 0) token_meta(p, t, lane, ds, js, lmask, smask);
-        if ((lmask | smask) != 0) {
-            if (!early) {
+        const bool any = (lmask | smask) != 0;
+        if (!EARLY && any) {
 #pragma unroll
-                for (int j = 0; j < SPW; ++j)
-                    if (it * SPW + j < p.nstep) v[j] = fp8_load(p, t, it * SPW + j, lane);
-            }
+            for (int j = 0; j < SPW; ++j)
+                if (it * SPW + j < p.nstep) v[j] = fp8_load(p, t, it * SPW + j, lane);
+        }
+        // the metadata (segment 0) follows the source loads, which then never wait behind its stores
+        if (it == 0) token_meta(p, t, lane, ds, js, lmask, smask);
+        if (any) {
 #pragma unroll
             for (int j = 0; j < SPW; ++j)
                 if (it * SPW + j < p.nstep) fp8_emit(p, it * SPW + j, lane, v[j], ds, js, lmask, smask);
@@ -141,8 +145,11 @@ hipError_t launch_dispatch(const Handle& h, const DispatchArgs& a, hipStream_t s
     if (pad_waves > nwaves) nwaves = pad_waves;
     const int64_t nblocks = (nwaves + kWavesPerBlock - 1) / kWavesPerBlock;
     p.nwaves = nblocks * kWavesPerBlock;
-    if (fp8)
-        hipLaunchKernelGGL(k_dispatch_fp8<kFp8SegsPerItem>, dim3((unsigned)nblocks), dim3(kBlock), 0, stream, p);
+    if (fp8 && p.send_slot != nullptr)
+        hipLaunchKernelGGL((k_dispatch_fp8<kFp8SegsPerItem, true>), dim3((unsigned)nblocks), dim3(kBlock), 0, stream, p);
+    else if (fp8)
+        hipLaunchKernelGGL((k_dispatch_fp8<kFp8SegsPerItem, false>), dim3((unsigned)nblocks), dim3(kBlock), 0, stream,
+                           p);
     else
         hipLaunchKernelGGL(k_dispatch_raw, dim3((unsigned)nblocks), dim3(kBlock), 0, stream, p);
     return hipGetLastError();
