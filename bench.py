@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--no-epilogues", dest="epilogues", action="store_false",
                     help="skip the receiver-placement / source-reduce measurement at the EP8 shapes")
+    ap.add_argument("--no-copy-ceiling", dest="copy_ceiling", action="store_false",
+                    help="skip the timed plain device copy reported as context")
     ap.add_argument("--no-decode", dest="decode", action="store_false",
                     help="skip the decode-shape comparison of the one-launch layout + dispatch")
     return ap.parse_args()
@@ -197,6 +199,29 @@ def measure_epilogues(ep, W, dev, n):
                            received_rows=n_valid, placed_rows=V),
         combine_reduce=dict(us=round(t_red * 1e3, 2), bytes=b_red, GBps=round(b_red / (t_red * 1e-3) / 1e9, 1),
                             partial_rows=n_part))
+
+
+def measure_copy_ceiling(dev, n, mib=1024):
+    """A plain device-to-device copy of `mib` MiB (torch's copy_, the runtime's copy kernel), timed with events
+    over n back-to-back copies: the streaming rate this machine reaches on a flat read + flat write, as context for
+    the kernels' rates (not the roofline's denominator, which is the published 8 TB/s)."""
+    import torch
+
+    a = torch.empty(mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n
+    del a, b
+    return dict(bytes_per_copy=2 * (mib << 20), us=round(us, 2), GBps=round(2 * (mib << 20) / (us * 1e-6) / 1e9, 1),
+                note="device copy of %d MiB (read + write bytes), events around %d copies" % (mib, n))
 
 
 def measure_decode(ep, W, dev, n):
@@ -445,6 +470,7 @@ def main():
 
     epi = measure_epilogues(ep, W, dev, args.steps) if args.epilogues else None
     decode = measure_decode(ep, W, dev, args.steps) if args.decode else None
+    copy_ceiling = measure_copy_ceiling(dev, 20) if args.copy_ceiling else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -473,6 +499,7 @@ def main():
         cpu_baseline=cpu,
         epilogues=epi,
         decode=decode,
+        copy_ceiling=copy_ceiling,
     )
     print(json.dumps(line), flush=True)
 
