@@ -156,3 +156,29 @@ def test_random_source_reduce(seed):
                            W.bf16_bits(bias) if with_bias else None)
     ok, mabs, mrel, nbad = Hn.combine_check(Hn.to_np(out), ref)
     assert ok, (mabs, mrel, nbad)
+
+
+@pytest.mark.parametrize("K,rank", [(32, 0), (32, 63), (12, 17)])
+def test_source_reduce_64_ranks(K, rank):
+    """The largest rank count: every lane of a wave reads a window row, and a token spread over many ranks has
+    more returned rows than one unrolled batch holds, so they are streamed.  H is not a multiple of 512, so the
+    last segment of each row has idle lanes."""
+    import combine_get_dispatch_03_amd as ep
+
+    R, E, T, H = 64, 128, 300, 8 * 77
+    rng = np.random.default_rng(9100 + K + rank)
+    idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int64)
+    gen = torch.Generator().manual_seed(K * 100 + rank)
+    parts = W.normal_bf16((R, T, H), gen)
+    local = W.normal_bf16((T, H), gen)
+    bias = W.normal_bf16((T, H), gen, 0.1)
+    print("[reduce 64 ranks] K=%d rank=%d T=%d H=%d" % (K, rank, T, H), flush=True)
+    h, _ = ep.ep_get_layout(torch.from_numpy(idx).to(DEV), E, R, rank, 1)
+    out = ep.ep_combine_reduce(h, parts.to(DEV), local.to(DEV), bias.to(DEV), hidden=H)
+    torch.cuda.synchronize()
+    lay = O.layout(idx, E, R, rank, 1)
+    nrows = (lay["send_slot"] >= 0).sum(axis=1)
+    assert nrows.max() >= 8          # the streamed path is taken
+    ref = O.combine_reduce(W.bf16_bits(parts), lay["send_slot"], rank, W.bf16_bits(local), W.bf16_bits(bias))
+    ok, mabs, mrel, nbad = Hn.combine_check(Hn.to_np(out), ref)
+    assert ok, (mabs, mrel, nbad)
