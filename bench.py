@@ -478,7 +478,7 @@ def main():
         cpu = cpu_baseline(inp, y_bits, cfg)
 
     line = dict(
-        metric="dispatch/combine effective HBM GB/s + % of peak, 4096 tok x 7168 top-8, 1 GPU",
+        metric="dispatch/combine effective HBM GB/s + % of peak, 4096 tok\u00d77168 top-8, 1 GPU",
         value=round(value, 1), unit="GB/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
         ms_per_step=round(ms_per_step, 4), higher_is_better=True, scaling="weak", vs_baseline=None,
         dtype="fp32", data="synthetic",
