@@ -102,9 +102,20 @@ def load_traffic(kernel):
     return k.get("hbm_bytes_per_launch")
 
 
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, y_bits, cfg):
-    """The oracle as it stands (single thread, plain C) on the full workload, repeated until about 10 s of
-    CPU time have been spent (at least 3 runs); the median run is reported."""
+    """The oracle as it stands (single thread, plain C) on the full workload, pinned to one host core, repeated
+    until about 10 s of CPU time have been spent (at least 3 runs); the median run is reported."""
     import numpy as np
 
     import oracle as O
@@ -114,6 +125,9 @@ def cpu_baseline(inp, y_bits, cfg):
     w = inp["topk_weights"].numpy()
     x = W.bf16_bits(inp["x"])
     bias = W.bf16_bits(inp["bias"]) if inp["bias"] is not None else None
+    allowed = sorted(os.sched_getaffinity(0))
+    core = allowed[0]
+    os.sched_setaffinity(0, {core})
     times = []
     while len(times) < 3 or sum(times) < 10.0:
         t0 = time.perf_counter()
@@ -122,6 +136,7 @@ def cpu_baseline(inp, y_bits, cfg):
                    zero_pad=cfg.zero_padding, recv_fill=None)
         O.combine(y_bits, lay["slot"], w, bias)
         times.append(time.perf_counter() - t0)
+    os.sched_setaffinity(0, set(allowed))
     El = cfg.num_experts // cfg.num_ranks
     cnt = lay["cnt"][cfg.rank * El:(cfg.rank + 1) * El]
     V = int(cnt.sum())
@@ -132,7 +147,8 @@ def cpu_baseline(inp, y_bits, cfg):
     med = float(np.median(times))
     return dict(value=round(total / med / 1e9, 3), unit="GB/s", cores=1, kind="oracle",
                 sample="full %s workload (layout + FP8 dispatch + combine), median of %d runs, %.2f s each"
-                       % (cfg.name, len(times), med))
+                       % (cfg.name, len(times), med),
+                pinned_core=core, host_cores_available=len(allowed), host_cpu=host_cpu_model())
 
 
 def measure_epilogues(ep, W, dev, n):
