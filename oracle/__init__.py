@@ -6,8 +6,9 @@ TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only ``tests/``, ``__graft_entry__.smoke
 
 The arithmetic lives in ``ep_oracle.c`` (plain C, single thread, gcc ``-O2 -ffp-contract=off``); this module
 only builds that file and marshals numpy arrays into it.  See ``ep_oracle.c`` for the definitions, their
-citations and the list of pins; the FP8 scale recipe is a reading the pages do not fix (parity unpinned for
-that choice; the e4m3 codec itself is pinned).
+citations and the list of pins; the FP8 scale recipe is a reading pinned by the properties of absmax scaling
+to +-448, except its 1e-4 floor for all-zero and tiny groups (parity unpinned for that floor; the e4m3 codec
+itself is pinned).
 """
 from __future__ import annotations
 

@@ -12,8 +12,11 @@
  * Pins (tests/test_oracle_*.py): the e4m3 and bf16 codecs against brute-force nearest-value search and
  * torch's CPU casts; the layout against the padding worked example of [MoE-comm] §三, brute-force counts
  * and numpy's stable argsort; the quantiser against hand-computed codes and its dequantisation bound; the
- * combine against a dense scatter-matrix product and its closed forms.  The FP8 scale recipe itself is a
- * reading the pages do not fix: for that choice (not for the codec) parity is unpinned.
+ * combine against a dense scatter-matrix product and its closed forms.  The pages only say that FP8 rows
+ * travel with scale factors; the per-128-channel absmax recipe is a reading, pinned by what any absmax scaling
+ * to e4m3's largest finite value must satisfy (the group maximum maps to +-448, every element dequantises to
+ * within half an e4m3 step).  The 1e-4 floor for all-zero and tiny groups is the one choice those properties
+ * leave open: parity unpinned for that floor.
  */
 #include "ep_oracle.h"
 
