@@ -42,11 +42,38 @@ def _case(seed):
     return dict(cfg=cfg, topk_idx=torch.from_numpy(idx), topk_weights=w, x=x, bias=None), expand
 
 
+def _case_many_tiles(seed):
+    """The shapes of _case(seed) with 700..6000 tokens (3 to 24 layout tiles) and hidden <= 1024."""
+    inp, expand = _case(seed)
+    c = inp["cfg"]
+    rng = np.random.default_rng(50000 + seed)
+    T = int(rng.integers(700, 6000))
+    K, E = c.num_topk, c.num_experts
+    idx = rng.integers(0, E, size=(T, K)).astype(np.int64)
+    if rng.random() < 0.5:
+        idx[rng.random((T, K)) < 0.05] = -1
+    gen = torch.Generator().manual_seed(seed)
+    w = W.softmax_weights(torch.randn(T, K, generator=gen))
+    H = min(c.hidden, 1024)
+    x = W.normal_bf16((T, H), gen)
+    cfg = W.Config("tiles%d" % seed, T, H, E, K, "uniform", c.expert_alignment, c.zero_padding, c.fp8,
+                   num_ranks=c.num_ranks, rank=c.rank)
+    return dict(cfg=cfg, topk_idx=torch.from_numpy(idx), topk_weights=w, x=x, bias=None), expand
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_case_many_tiles(seed):
+    _run_case(*_case_many_tiles(seed), seed)
+
+
 @pytest.mark.parametrize("seed", range(NCASES))
 def test_random_case(seed):
+    _run_case(*_case(seed), seed)
+
+
+def _run_case(inp, expand, seed):
     import combine_get_dispatch_03_amd as ep
 
-    inp, expand = _case(seed)
     c = inp["cfg"]
     print("[random %d] T=%d K=%d E=%d R=%d rank=%d A=%d H=%d fp8=%d zp=%d expand=%d" % (
         seed, c.num_tokens, c.num_topk, c.num_experts, c.num_ranks, c.rank, c.expert_alignment, c.hidden, c.fp8,
