@@ -130,11 +130,14 @@ __device__ uint64_t count_tile(const int64_t* __restrict__ idx, int T, int K, in
     const int tt = tid - kTokThread0;
     const int t = tok_tile0 + tt;
     const bool tv = tt >= 0 && t < T;
+    // expert -> owning rank as floor((e + 0.5) / epr) in fp32: exact here, since for e < 1024 and epr <= 1024 the
+    // quotient lies at least 0.5 / epr >= 2^-11 from an integer and the two roundings move it by < 2^-13
+    const float inv_epr = 1.0f / (float)epr;
     uint64_t mask = 0ull;
     if (tv) {
         for (int k = 0; k < K; ++k) {
             const int p = L.ent[tt * K + k];
-            if (p >= 0) mask |= 1ull << ((p & kPackMask) / epr);
+            if (p >= 0) mask |= 1ull << (int)(((float)(p & kPackMask) + 0.5f) * inv_epr);
         }
     }
     if (tv && in_rank_out != nullptr)
@@ -222,9 +225,43 @@ struct Outputs {
 };
 
 // Aligned exclusive scan of the local experts' counts (total[lo + j]) into psum[0..epr] and of their padding
-// counts into padpre[0..epr], in LDS.  Every thread of the block calls it; it ends with a barrier.
+// counts into padpre[0..epr], in LDS.  Every thread of the block calls it; it ends with a barrier.  Up to 256
+// local experts one wave does it (4 consecutive experts per lane, two DPP wave scans, one barrier); beyond
+// that the whole block scans.
 __device__ void local_scan(int epr, int lo, int A, const int* total, int* psum, int* padpre, int* scratch) {
     const int tid = threadIdx.x;
+    if (epr <= 4 * kWave) {
+        if (tid < kWave) {
+            int pad[4], gap[4], s0 = 0, s1 = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int e = 4 * tid + j;
+                const int c = e < epr ? total[lo + e] : 0;
+                pad[j] = ((c + A - 1) / A) * A;
+                gap[j] = pad[j] - c;
+                s0 += pad[j];
+                s1 += gap[j];
+            }
+            const int i0 = wave_inclusive_scan(s0), i1 = wave_inclusive_scan(s1);
+            int r0 = i0 - s0, r1 = i1 - s1;          // exclusive prefix of this lane's first expert
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int e = 4 * tid + j;
+                if (e < epr) {
+                    psum[e] = r0;
+                    padpre[e] = r1;
+                }
+                r0 += pad[j];
+                r1 += gap[j];
+            }
+            if (tid == kWave - 1) {
+                psum[epr] = i0;
+                padpre[epr] = i1;
+            }
+        }
+        __syncthreads();
+        return;
+    }
     const int c = tid < epr ? total[lo + tid] : 0;
     const int padded = ((c + A - 1) / A) * A;
     int ex, expad, all, allpad;
