@@ -90,7 +90,8 @@ __global__ __launch_bounds__(kThreads) void k_layout_dispatch_small(FusedArgs f,
             const int pk = L.ent[t * K + lane];
             if (pk >= 0) {
                 const int e = pk & kPackMask;
-                if (e >= lo && e < lo + epr) sexp = psum[e - lo] + L.cnt_w[(t / kTokPerWave) * E + e] + (pk >> kPackShift);
+                if (e >= lo && e < lo + epr)
+                    sexp = psum[e - lo] + L.cnt_w[(t / tokens_per_wave(T, 0)) * E + e] + (pk >> kPackShift);
             }
         }
         const int own = lane < R ? row_or_none(trow[t * R + lane]) : -1;

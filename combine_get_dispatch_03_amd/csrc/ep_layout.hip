@@ -38,9 +38,10 @@ __global__ __launch_bounds__(kThreads) void k_layout_count(
     for (int c = tid; c < NC; c += kThreads) tile_hist[(int64_t)tile * NC + c] = L.row[c];
     const int64_t ent_tile0 = (int64_t)tile * kTile * K;
     const int nent_tile = max(0, min(kTile, T - tile * kTile)) * K;
+    const int tpw = tokens_per_wave(T, tile);
     for (int j = tid; j < nent_tile; j += kThreads) {
         const int p = L.ent[j];
-        const int wv = (j / K) / kTokPerWave;
+        const int wv = (j / K) / tpw;
         packed_out[ent_tile0 + j] =
             p < 0 ? -1 : (((p >> kPackShift) + L.cnt_w[wv * E + (p & kPackMask)]) << kPackShift) | (p & kPackMask);
     }
@@ -149,12 +150,13 @@ __global__ __launch_bounds__(kThreads) void k_layout_single(
     const uint64_t mask = count_tile(idx, T, K, E, R, epr, nbits, 0, L, first ? in_rank_out : nullptr);
     finalize_core(E, R, rank, epr, A, L.row, psum, padpre, scratch, o);
     // this workgroup's slice of the slot map
+    const int tpw = tokens_per_wave(T, 0);
     for (int j = (int)blockIdx.x * kThreads + (int)threadIdx.x; j < T * K; j += (int)gridDim.x * kThreads) {
         const int p = L.ent[j];
         int s = -1;
         if (p >= 0) {
             const int e = p & kPackMask;
-            const int wv = (j / K) / kTokPerWave;
+            const int wv = (j / K) / tpw;
             if (e >= lo && e < lo + epr) s = psum[e - lo] + L.cnt_w[wv * E + e] + (p >> kPackShift);
         }
         slot[j] = s;

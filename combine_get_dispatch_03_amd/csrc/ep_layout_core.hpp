@@ -16,7 +16,6 @@ namespace {
 constexpr int kTile = kLayoutTileTokens;   // 256 tokens per tile
 constexpr int kThreads = 1024;             // every layout block: 16 waves
 constexpr int kWaves = kThreads / 64;
-constexpr int kTokPerWave = kTile / kWaves;   // 16 tokens ranked per wave
 constexpr int kPackShift = 11;             // packed entry: (rank << 11) | expert, or -1
 constexpr int kPackMask = (1 << kPackShift) - 1;
 constexpr int kBad = -2;                   // staged value of an entry < -1 or >= E
@@ -38,6 +37,14 @@ struct CountLds {
 };
 
 __host__ __device__ constexpr size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
+
+// Tokens ranked per wave in tile `tile`: the tile's tokens spread evenly over the 16 waves (16 for a full tile,
+// 8 for a 128-token batch, so that no wave runs two ranking rounds while others idle).  Wave w ranks tokens
+// [w * tpw, (w + 1) * tpw) of the tile; every reader of the per-wave bases uses the same split.
+__device__ __forceinline__ int tokens_per_wave(int T, int tile) {
+    const int ntok = max(0, min(kTile, T - tile * kTile));
+    return max(1, (ntok + kWaves - 1) / kWaves);
+}
 
 __host__ __device__ size_t count_lds_bytes(int E, int K, int R) {
     return align16(sizeof(uint16_t) * kWaves * (size_t)E) +
@@ -90,8 +97,9 @@ __device__ uint64_t count_tile(const int64_t* __restrict__ idx, int T, int K, in
     __syncthreads();
 
     // each wave ranks its 16 tokens' entries in flat order
-    const int nent_w = max(0, min(kTokPerWave, T - (tok_tile0 + w * kTokPerWave))) * K;
-    int32_t* went = L.ent + w * kTokPerWave * K;
+    const int tpw = tokens_per_wave(T, tile);
+    const int nent_w = max(0, min(tpw, T - (tok_tile0 + w * tpw))) * K;
+    int32_t* went = L.ent + w * tpw * K;
     const uint64_t lt = lanemask_lt();
     uint16_t* cnt = L.cnt_w + w * E;
     int inv = 0;
