@@ -167,10 +167,6 @@ __device__ __forceinline__ void fp8_emit(const Params& p, int st, int lane, cons
     }
 }
 
-__device__ __forceinline__ void fp8_segment(const Params& p, int t, int st, int lane, int ds, int js,
-                                            uint64_t lmask, uint64_t smask) {
-    fp8_emit(p, st, lane, fp8_load(p, t, st, lane), ds, js, lmask, smask);
-}
 
 // Raw segment st of row t (BF16 dispatch, and received rows that already carry their receive format): 16-byte
 // copies of one 1 KiB segment; segment 0 also copies the row's scales, if any.
@@ -208,10 +204,6 @@ __device__ __forceinline__ void raw_emit(const Params& p, int t, int st, int lan
     }
 }
 
-__device__ __forceinline__ void raw_segment(const Params& p, int t, int st, int lane, int ds, int js,
-                                            uint64_t lmask, uint64_t smask) {
-    raw_emit(p, t, st, lane, raw_load(p, t, st, lane), ds, js, lmask, smask);
-}
 
 // Zero-padding item: segment s of padding row `row` gets zero bytes (and its share of the scales); segment 0
 // also writes the row's metadata.
