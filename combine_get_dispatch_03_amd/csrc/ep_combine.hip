@@ -13,6 +13,8 @@
 // predicated load whose consumer sits in another branch makes the compiler wait for every earlier load
 // before issuing it, so a batch would never have more than one gather in flight.  fp32 accumulation in
 // ascending k, one RNE rounding to bf16 at the end.
+#include <climits>
+
 #include "ep_device.hpp"
 #include "ep_internal.hpp"
 
@@ -21,10 +23,14 @@ namespace {
 
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
-// A wave with at least this many rows streams them (measured on the 4096 x 7168 top-8 shapes: combine is
-// fastest streaming only full top-8 tokens, the reduce, which also reads a local and a bias row, from 4).
+// Streaming a wave's rows one at a time pays only when the grid keeps HBM saturated by itself: with at least
+// kStreamMinWaves waves (twice what the chip holds at once) a wave with at least kCombineStreamRows rows
+// (kReduceStreamRows for the reduce, which also reads a local and a bias row) streams them; smaller grids are
+// latency-bound and issue every row in batches of 8.  Measured: prefill combine (57,344 waves of 8 rows)
+// about 1% faster streaming; decode combine (1,792 waves of 8 rows) 23% faster batched.
 constexpr int kCombineStreamRows = 8;
 constexpr int kReduceStreamRows = 4;
+constexpr int64_t kStreamMinWaves = 16384;
 
 struct Params {
     const uint16_t* y;
@@ -35,6 +41,7 @@ struct Params {
     int T, H, K, stride;
     int nseg;          // 1 KiB segments per row
     int64_t nitems;    // T * nseg
+    int stream_min;    // a wave with at least this many rows streams them
 };
 
 __device__ __forceinline__ void fma8(float* acc, float wgt, u32x4 v) {
@@ -77,25 +84,25 @@ __device__ __forceinline__ void gather_acc(float* acc, const u32x4* base, int64_
     }
 }
 
-// All nv compacted rows.  A wave with few rows is latency-bound: they are issued together, as one unrolled
-// batch.  With STREAM or more the kernel is bandwidth-bound (every wave brings enough rows to keep HBM busy)
-// and a wave streams its rows one at a time, which measured about 1% faster than deeper queues.
-template <bool WEIGHTED, int STREAM>
+// All nv compacted rows: streamed one at a time when nv >= stream_min, else issued in unrolled batches of 8
+// (full batches, then one remainder batch of 1..7).
+template <bool WEIGHTED>
 __device__ __forceinline__ void gather_all(float* acc, const u32x4* base, int64_t stride, int rows, float w,
-                                           int nv) {
-    static_assert(STREAM >= 1 && STREAM <= 8, "the batch switch below covers 1..7");
-    if (nv >= STREAM) {
+                                           int nv, int stream_min) {
+    if (nv >= stream_min) {
         for (int k = 0; k < nv; ++k) gather_acc<1, WEIGHTED>(acc, base, stride, rows, w, k);
         return;
     }
-    switch (nv) {
-        case 1: gather_acc<1, WEIGHTED>(acc, base, stride, rows, w, 0); break;
-        case 2: gather_acc<2, WEIGHTED>(acc, base, stride, rows, w, 0); break;
-        case 3: gather_acc<3, WEIGHTED>(acc, base, stride, rows, w, 0); break;
-        case 4: gather_acc<4, WEIGHTED>(acc, base, stride, rows, w, 0); break;
-        case 5: gather_acc<5, WEIGHTED>(acc, base, stride, rows, w, 0); break;
-        case 6: gather_acc<6, WEIGHTED>(acc, base, stride, rows, w, 0); break;
-        case 7: gather_acc<7, WEIGHTED>(acc, base, stride, rows, w, 0); break;
+    int kb = 0;
+    for (; kb + 8 <= nv; kb += 8) gather_acc<8, WEIGHTED>(acc, base, stride, rows, w, kb);
+    switch (nv - kb) {
+        case 1: gather_acc<1, WEIGHTED>(acc, base, stride, rows, w, kb); break;
+        case 2: gather_acc<2, WEIGHTED>(acc, base, stride, rows, w, kb); break;
+        case 3: gather_acc<3, WEIGHTED>(acc, base, stride, rows, w, kb); break;
+        case 4: gather_acc<4, WEIGHTED>(acc, base, stride, rows, w, kb); break;
+        case 5: gather_acc<5, WEIGHTED>(acc, base, stride, rows, w, kb); break;
+        case 6: gather_acc<6, WEIGHTED>(acc, base, stride, rows, w, kb); break;
+        case 7: gather_acc<7, WEIGHTED>(acc, base, stride, rows, w, kb); break;
         default: break;
     }
 }
@@ -129,7 +136,7 @@ __global__ __launch_bounds__(kBlock) void k_combine(Params p) {
     float acc[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
-    gather_all<true, kCombineStreamRows>(acc, reinterpret_cast<const u32x4*>(p.y) + (active ? c : 0), p.H / 8, cs, cw, nv);
+    gather_all<true>(acc, reinterpret_cast<const u32x4*>(p.y) + (active ? c : 0), p.H / 8, cs, cw, nv, p.stream_min);
     if (!active) return;
     if (p.bias != nullptr) add8(acc, reinterpret_cast<const u32x4*>(p.bias + (int64_t)t * p.H)[c]);
     st_nt(reinterpret_cast<u32x4*>(p.out + (int64_t)t * p.H) + c, pack8(acc));
@@ -149,6 +156,7 @@ struct ReduceParams {
     int T, H, R, rank;
     int nseg;
     int64_t nitems;
+    int stream_min;
 };
 
 __global__ __launch_bounds__(kBlock) void k_combine_reduce(ReduceParams p) {
@@ -176,7 +184,8 @@ __global__ __launch_bounds__(kBlock) void k_combine_reduce(ReduceParams p) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
     if (active && p.local != nullptr) add8(acc, reinterpret_cast<const u32x4*>(p.local + (int64_t)t * p.H)[c]);
-    gather_all<false, kReduceStreamRows>(acc, reinterpret_cast<const u32x4*>(p.partials) + (active ? c : 0), p.H / 8, cs, 0.0f, nv);
+    gather_all<false>(acc, reinterpret_cast<const u32x4*>(p.partials) + (active ? c : 0), p.H / 8, cs, 0.0f, nv,
+                      p.stream_min);
     if (!active) return;
     if (p.bias != nullptr) add8(acc, reinterpret_cast<const u32x4*>(p.bias + (int64_t)t * p.H)[c]);
     st_nt(reinterpret_cast<u32x4*>(p.out + (int64_t)t * p.H) + c, pack8(acc));
@@ -198,6 +207,7 @@ hipError_t launch_combine_reduce(const Handle& h, const ReduceArgs& a, hipStream
     p.rank = h.rank;
     p.nseg = (a.hidden / 8 + kWave - 1) / kWave;
     p.nitems = (int64_t)h.T * p.nseg;
+    p.stream_min = p.nitems >= kStreamMinWaves ? kReduceStreamRows : INT_MAX;
     const unsigned nblocks = (unsigned)((p.nitems + kWavesPerBlock - 1) / kWavesPerBlock);
     hipLaunchKernelGGL(k_combine_reduce, dim3(nblocks), dim3(kBlock), 0, stream, p);
     return hipGetLastError();
@@ -224,6 +234,7 @@ hipError_t launch_combine(const Handle& h, const CombineArgs& a, hipStream_t str
     }
     p.nseg = (a.hidden / 8 + kWave - 1) / kWave;
     p.nitems = (int64_t)h.T * p.nseg;
+    p.stream_min = p.nitems >= kStreamMinWaves ? kCombineStreamRows : INT_MAX;
     const unsigned nblocks = (unsigned)((p.nitems + kWavesPerBlock - 1) / kWavesPerBlock);
     hipLaunchKernelGGL(k_combine, dim3(nblocks), dim3(kBlock), 0, stream, p);
     return hipGetLastError();

@@ -185,14 +185,16 @@ def test_random_source_reduce(seed):
     assert ok, (mabs, mrel, nbad)
 
 
-@pytest.mark.parametrize("K,rank", [(32, 0), (32, 63), (12, 17)])
-def test_source_reduce_64_ranks(K, rank):
+@pytest.mark.parametrize("K,rank,T,H", [(32, 0, 300, 616), (32, 63, 300, 616), (12, 17, 300, 616),
+                                          (32, 5, 8200, 520)])
+def test_source_reduce_64_ranks(K, rank, T, H):
     """The largest rank count: every lane of a wave reads a window row, and a token spread over many ranks has
-    more returned rows than one unrolled batch holds, so they are streamed.  H is not a multiple of 512, so the
-    last segment of each row has idle lanes."""
+    more returned rows than one unrolled batch holds.  With 300 tokens (a latency-bound grid) they are gathered
+    in batches of 8; with 8200 tokens the grid is large enough for the waves to stream them one at a time.  H
+    is not a multiple of 512, so the last segment of each row has idle lanes."""
     import combine_get_dispatch_03_amd as ep
 
-    R, E, T, H = 64, 128, 300, 8 * 77
+    R, E = 64, 128
     rng = np.random.default_rng(9100 + K + rank)
     idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int64)
     gen = torch.Generator().manual_seed(K * 100 + rank)
