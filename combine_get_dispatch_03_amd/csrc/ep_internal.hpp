@@ -60,7 +60,10 @@ struct LayoutOutputs {
     int32_t* psum;
     int32_t* num_invalid;
 };
-hipError_t launch_layout(const Handle& h, const LayoutOutputs& out, hipStream_t stream);
+// prefetch / prefetch_bytes (optional): a span the caller reads right after the layout (the dispatch's source
+// rows); for more than one tile, extra blocks of the layout kernels read it while the layout runs.
+hipError_t launch_layout(const Handle& h, const LayoutOutputs& out, hipStream_t stream, const void* prefetch = nullptr,
+                         size_t prefetch_bytes = 0);
 
 struct DispatchArgs {
     enum Mode { kBf16, kFp8, kRows };

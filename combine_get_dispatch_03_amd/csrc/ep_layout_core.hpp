@@ -305,20 +305,20 @@ __device__ void write_counts(int E, int R, int lo, int epr, const int* total, co
 }
 
 // Finalizing phase shared by both layout paths.  `total` holds the column totals over all tiles (experts |
-// ranks | invalid).  Computes psum / padpre (LDS), block 0 writes the global outputs, and every block writes
-// its share (experts blockIdx.x + i * gridDim.x) of the dense padding-row list.
+// ranks | invalid).  Computes psum / padpre (LDS), block 0 writes the global outputs, and each of the nblk
+// layout blocks writes its share (experts blockIdx.x + i * nblk) of the dense padding-row list.
 __device__ void finalize_core(int E, int R, int rank, int epr, int A, const int* total, int* psum, int* padpre,
-                              int* scratch, const Outputs& o) {
+                              int* scratch, const Outputs& o, int nblk) {
     const int tid = threadIdx.x;
     const int lo = rank * epr;
     local_scan(epr, lo, A, total, psum, padpre, scratch);
     if (blockIdx.x == 0) write_counts(E, R, lo, epr, total, psum, padpre, o);
     if (o.pad_rows != nullptr) {
-        // this block's share: local experts blockIdx.x + i * gridDim.x, one expert per wave, lanes over its rows
-        const int nexp = (epr - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+        // this block's share: local experts blockIdx.x + i * nblk, one expert per wave, lanes over its rows
+        const int nexp = (epr - (int)blockIdx.x + nblk - 1) / nblk;
         const int w = tid >> 6, lane = tid & 63;
         for (int i = w; i < nexp; i += kWaves) {
-            const int j = blockIdx.x + i * gridDim.x;
+            const int j = blockIdx.x + i * nblk;
             const int first = psum[j] + total[lo + j];
             const int n = psum[j + 1] - first;
             int32_t* dst = o.pad_rows + padpre[j];
