@@ -1,11 +1,12 @@
 """Benchmark of the MoE expert-parallel layout / dispatch / combine path on one MI355X.
 
-A step is one pass of the whole path over one batch of the prefill workload: ep_get_layout, then FP8 dispatch
-with zero padding, then the weighted BF16 combine (4096 tokens, hidden 7168, 256 experts in 8 groups with
-group-limited top-4-group / top-8 routing, alignment 128).  Inputs and expert outputs are resident in HBM
-before timing starts.  W untimed warm-up steps, then exactly K timed steps bracketed by device syncs; the
-host enqueues the three calls of a step (~35 us of host time) far faster than the GPU runs them (~180 us),
-so no step waits on the host.  The same step captured in a HIP graph and replayed K times is reported too
+A step is one pass of the whole path over one batch of the prefill workload: the layout and the FP8 dispatch
+with zero padding (one ep_layout_dispatch call, whose layout kernels also read the token rows ahead of the
+dispatch), then the weighted BF16 combine (4096 tokens, hidden 7168, 256 experts in 8 groups with group-limited
+top-4-group / top-8 routing, alignment 128).  Inputs and expert outputs are resident in HBM before timing
+starts.  W untimed warm-up steps, then exactly K timed steps bracketed by device syncs; the host enqueues the
+calls of a step (~35 us of host time) far faster than the GPU runs them (~175 us), so no step waits on the
+host.  The same step captured in a HIP graph and replayed K times is reported too
 (`step_graph_replay_us`): each replay adds a few microseconds of GPU-side overhead that a graph of a whole
 model pass would spread over many more kernels.  Each call's average duration comes from HIP events on the
 launch stream around K back-to-back launches of that call, enqueued by the host ahead of the GPU.
@@ -356,18 +357,23 @@ def main():
         del a, b
 
     def step(ev=None):
+        """One pass of the path.  Timed steps (ev None) make the one-call layout + dispatch, which reads the token
+        rows into the memory-side cache while the layout runs; the flushed per-call samples (ev given) make the
+        two calls separately so that each can be bracketed by its own events."""
         stream = torch.cuda.current_stream()
-        if ev is not None:
-            ev[0].record(stream)
+        if ev is None:
+            h, _, _ = ep.ep_layout_dispatch(idx, x, E, R, cfg.rank, cfg.expert_alignment, w, fp8=cfg.fp8,
+                                            do_zero_padding=cfg.zero_padding, out=dout, workspace=ws,
+                                            outputs=lay_out)
+            ep.ep_combine(h, y, w, bias, out=out)
+            return h
+        ev[0].record(stream)
         h, _ = ep.ep_get_layout(idx, E, R, cfg.rank, cfg.expert_alignment, workspace=ws, outputs=lay_out)
-        if ev is not None:
-            ev[1].record(stream)
+        ev[1].record(stream)
         ep.ep_dispatch(h, x, w, fp8=cfg.fp8, do_zero_padding=cfg.zero_padding, out=dout)
-        if ev is not None:
-            ev[2].record(stream)
+        ev[2].record(stream)
         ep.ep_combine(h, y, w, bias, out=out)
-        if ev is not None:
-            ev[3].record(stream)
+        ev[3].record(stream)
         return h
 
     # W untimed warm-up steps
@@ -427,6 +433,12 @@ def main():
 
     layout_dispatch_us = timed(layout_then_dispatch, args.steps) * 1e3
 
+    def layout_dispatch_one_call():
+        ep.ep_layout_dispatch(idx, x, E, R, cfg.rank, cfg.expert_alignment, w, fp8=cfg.fp8,
+                              do_zero_padding=cfg.zero_padding, out=dout, workspace=ws, outputs=lay_out)
+
+    layout_dispatch_one_us = timed(layout_dispatch_one_call, args.steps) * 1e3
+
     # per-kernel samples with a cache flush before each (10 warm-up + N samples, the pages' method)
     flushed = None
     if args.flush_samples > 0:
@@ -476,6 +488,9 @@ def main():
         kern["layout"]["us_flushed_median"] = round(flushed["layout"] * 1e3, 2)
         kern["layout"]["us_flushed_min"] = round(flushed_min["layout"] * 1e3, 2)
     kern["layout_then_dispatch"] = dict(us=round(layout_dispatch_us, 2))
+    kern["layout_dispatch_one_call"] = dict(us=round(layout_dispatch_one_us, 2),
+                                            note="ep_layout_dispatch: the layout kernels also read x ahead of "
+                                                 "the dispatch")
 
     dom = "dispatch" if avg["dispatch"] >= avg["combine"] else "combine"
     dom_kernel = {"dispatch": "k_dispatch_fp8", "combine": "k_combine"}[dom]
@@ -507,7 +522,8 @@ def main():
                     valid_rows=V, pad_rows=counts["P"], A_pad=round(int(psum[-1]) / max(V, 1), 4),
                     data_dtypes="x bf16 -> recv e4m3 + fp32 scales; y bf16 -> out bf16 (fp32 accumulate)"),
         tokens_per_s=round(T / (ms_per_step * 1e-3), 1),
-        timing="step: K eager steps of layout (2 kernels) + dispatch + combine between device syncs; per call: "
+        timing="step: K eager steps of ep_layout_dispatch (layout kernels reading x ahead, then the dispatch) + "
+               "ep_combine between device syncs; per call: "
                "events around K back-to-back launches",
         step_graph_replay_us=round(step_graph_us, 2),
         kernels=kern,
