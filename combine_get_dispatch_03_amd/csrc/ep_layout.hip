@@ -42,6 +42,11 @@ struct Prefetch {
 // 87-89 us; 448 or 896 blocks no better).
 constexpr int kPrefetchBlocks = 224;
 constexpr int64_t kPrefetchCountPct = 60;
+// The span is read only if it is at most this long: about what HBM moves in the ~11 us the layout takes.  All
+// or nothing, as measured: prefill (58.7 MB of rows) step 2.2% faster reading all of it, but 32 MiB of it made
+// the step slower than none; for a 235 MB span (16,384 tokens) reading all of it made the step 8% slower and
+// reading the first 32 or 64 MiB 1% slower than none.
+constexpr int64_t kPrefetchMaxBytes = 64ll << 20;
 
 __device__ void prefetch_share(const Prefetch& pf, int b) {
     const int64_t stride = (int64_t)pf.nblk * kThreads;
@@ -233,7 +238,8 @@ hipError_t launch_layout(const Handle& h, const LayoutOutputs& out, hipStream_t 
     }
     // the span the caller reads next, in 16-byte units: the count kernel's extra blocks read the first
     // kPrefetchCountPct percent of it, the finalize kernel's the rest
-    const int64_t n16 = prefetch != nullptr ? (int64_t)(prefetch_bytes / 16) : 0;
+    const int64_t n16 =
+        prefetch != nullptr && (int64_t)prefetch_bytes <= kPrefetchMaxBytes ? (int64_t)prefetch_bytes / 16 : 0;
     const int64_t split = n16 * kPrefetchCountPct / 100;
     const Prefetch pf_count{static_cast<const u32x4*>(prefetch), 0, split, kPrefetchBlocks};
     const Prefetch pf_final{static_cast<const u32x4*>(prefetch), split, n16, kPrefetchBlocks};
