@@ -56,9 +56,11 @@ def _check(ep, inp, do_expand=True):
     assert ok, (mabs, mrel, nbad)
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode"])
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "ep8", "skewed"])
 @pytest.mark.parametrize("do_expand", [True, False])
 def test_fused_workloads(ep, name, do_expand):
+    """Two launches above 256 tokens: prefill and ep8 (58.7 MB of token rows) have the layout kernels read the rows
+    ahead of the dispatch; skewed (235 MB, over the 64 MiB limit) does not."""
     print("[fused] workload %s do_expand=%d" % (name, do_expand), flush=True)
     _check(ep, W.make_inputs(name), do_expand)
 
