@@ -47,6 +47,9 @@ constexpr int64_t kPrefetchCountPct = 60;
 // the step slower than none; for a 235 MB span (16,384 tokens) reading all of it made the step 8% slower and
 // reading the first 32 or 64 MiB 1% slower than none.
 constexpr int64_t kPrefetchMaxBytes = 64ll << 20;
+// ... and at least this long: below it the extra blocks cost more than the reads save (1024 tokens, 14.7 MB of
+// rows: layout + dispatch 1-2 us slower; 2048 tokens: no change).
+constexpr int64_t kPrefetchMinBytes = 16ll << 20;
 
 __device__ void prefetch_share(const Prefetch& pf, int b) {
     const int64_t stride = (int64_t)pf.nblk * kThreads;
@@ -238,8 +241,9 @@ hipError_t launch_layout(const Handle& h, const LayoutOutputs& out, hipStream_t 
     }
     // the span the caller reads next, in 16-byte units: the count kernel's extra blocks read the first
     // kPrefetchCountPct percent of it, the finalize kernel's the rest
-    const int64_t n16 =
-        prefetch != nullptr && (int64_t)prefetch_bytes <= kPrefetchMaxBytes ? (int64_t)prefetch_bytes / 16 : 0;
+    const bool read_ahead = prefetch != nullptr && (int64_t)prefetch_bytes >= kPrefetchMinBytes &&
+                            (int64_t)prefetch_bytes <= kPrefetchMaxBytes;
+    const int64_t n16 = read_ahead ? (int64_t)prefetch_bytes / 16 : 0;
     const int64_t split = n16 * kPrefetchCountPct / 100;
     const Prefetch pf_count{static_cast<const u32x4*>(prefetch), 0, split, kPrefetchBlocks};
     const Prefetch pf_final{static_cast<const u32x4*>(prefetch), split, n16, kPrefetchBlocks};

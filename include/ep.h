@@ -167,7 +167,7 @@ ep_status_t ep_dispatch(ep_handle_t handle, const void* x, int hidden, const flo
  * workgroup builds the small layout in LDS and dispatches its share of the rows, so no launch waits for another
  * ([DeepEP->MegaMoE] §4.3: at small batches launch overhead, not bytes, sets the time; [DeepEP-hotdry]
  * 性能基准: the low-latency decode path).  Larger batches run the layout and the dispatch launches back to back;
- * when x is at most 64 MiB the layout launches also read it (and store nothing) while the layout runs, so that
+ * when x is 16 to 64 MiB the layout launches also read it (and store nothing) while the layout runs, so that
  * the dispatch finds its rows in the memory-side cache.  x is only read, as by ep_dispatch.
  *
  *   Arguments as in ep_get_layout (topk_idx .. num_invalid_topk, handle_out) and ep_dispatch (x .. out).
