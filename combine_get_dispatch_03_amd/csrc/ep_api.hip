@@ -3,9 +3,9 @@
 // allocates device memory or synchronises.
 #include <cstdarg>
 #include <cstdio>
+#include <map>
 #include <mutex>
 #include <new>
-#include <set>
 #include <utility>
 
 #include "ep_internal.hpp"
@@ -58,11 +58,12 @@ hipError_t allow_dynamic_lds(const void* kernel, int bytes) {
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     static std::mutex mu;
-    static std::set<std::pair<const void*, int>> done;
+    static std::map<std::pair<const void*, int>, int> allowed;   // (kernel, device) -> largest size set
     std::lock_guard<std::mutex> lock(mu);
-    if (done.count({kernel, dev}) != 0) return hipSuccess;
+    const auto it = allowed.find({kernel, dev});
+    if (it != allowed.end() && it->second >= bytes) return hipSuccess;
     e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e == hipSuccess) done.insert({kernel, dev});
+    if (e == hipSuccess) allowed[{kernel, dev}] = bytes;
     return e;
 }
 

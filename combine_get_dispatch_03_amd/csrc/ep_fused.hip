@@ -167,7 +167,7 @@ hipError_t launch_layout_dispatch(const Handle& h, const LayoutOutputs& out, con
     if (lds > 65536) {
         const void* k = fp8 ? reinterpret_cast<const void*>(k_layout_dispatch_small<true>)
                             : reinterpret_cast<const void*>(k_layout_dispatch_small<false>);
-        const hipError_t e = allow_dynamic_lds(k, (int)fused_lds_bytes(kMaxExperts, kMaxTopk, kMaxRanks, kMaxExperts));
+        const hipError_t e = allow_dynamic_lds(k, (int)lds);
         if (e != hipSuccess) return e;
     }
     if (fp8)

@@ -48,7 +48,7 @@ struct Handle {
 };
 
 // Opt `kernel` in to `bytes` of dynamic LDS (above the 64 KiB default; gfx950 has 160 KiB per CU) on the current
-// device, once per (kernel, device); thread-safe.
+// device; the attribute is only ever raised, to the largest size asked for per (kernel, device); thread-safe.
 hipError_t allow_dynamic_lds(const void* kernel, int bytes);
 
 // ---- launchers (each enqueues on `stream` and returns hipGetLastError()) -----------------------------

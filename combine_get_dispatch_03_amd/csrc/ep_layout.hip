@@ -228,8 +228,7 @@ hipError_t launch_layout(const Handle& h, const LayoutOutputs& out, hipStream_t 
     if (h.ntiles == 1) {
         const size_t lds = single_lds_bytes(h.E, h.K, h.R, epr);
         if (lds > 65536) {
-            const hipError_t err = allow_dynamic_lds(reinterpret_cast<const void*>(k_layout_single),
-                                                     (int)single_lds_bytes(kMaxExperts, kMaxTopk, kMaxRanks, kMaxExperts));
+            const hipError_t err = allow_dynamic_lds(reinterpret_cast<const void*>(k_layout_single), (int)lds);
             if (err != hipSuccess) return err;
         }
         // one workgroup per 16 local experts (one expert's padding rows per wave), each repeating the small layout
@@ -253,8 +252,7 @@ hipError_t launch_layout(const Handle& h, const LayoutOutputs& out, hipStream_t 
     if (h.ntiles > 1) {
         const size_t lds = count_lds_bytes(h.E, h.K, h.R);
         if (lds > 65536) {
-            const hipError_t err = allow_dynamic_lds(reinterpret_cast<const void*>(k_layout_count),
-                                                     (int)count_lds_bytes(kMaxExperts, kMaxTopk, kMaxRanks));
+            const hipError_t err = allow_dynamic_lds(reinterpret_cast<const void*>(k_layout_count), (int)lds);
             if (err != hipSuccess) return err;
         }
         hipLaunchKernelGGL(k_layout_count, dim3(nb_count), dim3(kThreads), lds, stream, h.topk_idx, h.T, h.K, h.E,
