@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--no-epilogues", dest="epilogues", action="store_false",
                     help="skip the receiver-placement / source-reduce measurement at the EP8 shapes")
+    ap.add_argument("--no-workloads", dest="workloads", action="store_false",
+                    help="skip the per-call summary of the other workloads (tiny, decode, ep8, skewed)")
     ap.add_argument("--no-copy-ceiling", dest="copy_ceiling", action="store_false",
                     help="skip the timed plain device copy reported as context")
     ap.add_argument("--no-decode", dest="decode", action="store_false",
@@ -239,6 +241,84 @@ def measure_copy_ceiling(dev, n, mib=1024):
     del a, b
     return dict(bytes_per_copy=2 * (mib << 20), us=round(us, 2), GBps=round(2 * (mib << 20) / (us * 1e-6) / 1e9, 1),
                 note="device copy of %d MiB (read + write bytes), events around %d copies" % (mib, n))
+
+
+def measure_workloads(ep, W, dev, names, n):
+    """The other workloads at a glance, measured like the headline one: per call, HIP events around n back-to-back
+    launches; the step (one-call layout + dispatch, then combine), n eager steps between device syncs, host
+    clock; algorithmic bytes from the byte model with the device counts.  Parity for each is in the test suite."""
+    import time
+
+    import torch
+
+    out = {}
+    for name in names:
+        inp = W.make_inputs(name)
+        cfg = inp["cfg"]
+        T, K, E, R, A = cfg.num_tokens, cfg.num_topk, cfg.num_experts, cfg.num_ranks, cfg.expert_alignment
+        idx = inp["topk_idx"].to(dev)
+        w = inp["topk_weights"].to(dev)
+        x = inp["x"].to(dev)
+        bias = inp["bias"].to(dev) if inp["bias"] is not None else None
+        ws = torch.empty(ep.ep_layout_workspace_bytes(T, K, E, R, A), dtype=torch.uint8, device=dev)
+        lay = dict(num_tokens_per_rank=torch.empty(R, dtype=torch.int32, device=dev),
+                   num_tokens_per_expert=torch.empty(E, dtype=torch.int32, device=dev),
+                   is_token_in_rank=torch.empty((T, R), dtype=torch.uint8, device=dev),
+                   psum_num_recv_tokens_per_expert=torch.empty(E // R + 1, dtype=torch.int32, device=dev),
+                   num_invalid_topk=torch.empty(1, dtype=torch.int32, device=dev))
+        h, _ = ep.ep_get_layout(idx, E, R, cfg.rank, A, workspace=ws, outputs=lay)
+        dout = ep.alloc_dispatch_outputs(h, cfg.hidden, cfg.fp8, device=dev)
+        y = W.random_expert_outputs(h.recv_capacity, cfg.hidden, seed=1234, device=dev)
+        res = torch.empty((T, cfg.hidden), dtype=torch.bfloat16, device=dev)
+
+        def timed(fn):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            torch.cuda._sleep(int(2.4e9 * 0.02))
+            e0.record()
+            for _ in range(n):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / n
+
+        def step():
+            hs, _, _ = ep.ep_layout_dispatch(idx, x, E, R, cfg.rank, A, w, fp8=cfg.fp8,
+                                             do_zero_padding=cfg.zero_padding, out=dout, workspace=ws, outputs=lay)
+            ep.ep_combine(hs, y, w, bias, out=res)
+
+        us = dict(layout=timed(lambda: ep.ep_get_layout(idx, E, R, cfg.rank, A, workspace=ws, outputs=lay)),
+                  dispatch=timed(lambda: ep.ep_dispatch(h, x, w, fp8=cfg.fp8, do_zero_padding=cfg.zero_padding,
+                                                        out=dout)),
+                  combine=timed(lambda: ep.ep_combine(h, y, w, bias, out=res)))
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            step()
+        torch.cuda.synchronize()
+        step_us = (time.perf_counter() - t0) * 1e6 / n
+        cnt = lay["num_tokens_per_expert"].cpu().numpy()
+        psum = lay["psum_num_recv_tokens_per_expert"].cpu().numpy()
+        ntr = lay["num_tokens_per_rank"].cpu().numpy()
+        El = E // R
+        V = int(cnt[cfg.rank * El:(cfg.rank + 1) * El].sum())
+        bm = bytes_model(cfg, dict(V=V, P=int(psum[-1]) - V,
+                                   N_send=int(sum(ntr[r] for r in range(R) if r != cfg.rank))))
+        rate = lambda b, u: b / (u * 1e-6) / 1e9
+        out[name] = dict(
+            layout_us=round(us["layout"], 2), dispatch_us=round(us["dispatch"], 2),
+            dispatch_GBps=round(rate(bm["dispatch"], us["dispatch"]), 1),
+            dispatch_pct_peak=round(100 * rate(bm["dispatch"], us["dispatch"]) / HBM_PEAK_GBPS, 1),
+            combine_us=round(us["combine"], 2), combine_GBps=round(rate(bm["combine"], us["combine"]), 1),
+            combine_pct_peak=round(100 * rate(bm["combine"], us["combine"]) / HBM_PEAK_GBPS, 1),
+            step_us=round(step_us, 2),
+            step_GBps=round(rate(bm["layout"] + bm["dispatch"] + bm["combine"], step_us), 1))
+        h.free()
+        del ws, lay, dout, y, res, idx, w, x, bias
+        torch.cuda.empty_cache()
+    return out
 
 
 def measure_decode(ep, W, dev, n):
@@ -502,6 +582,12 @@ def main():
     epi = measure_epilogues(ep, W, dev, args.steps) if args.epilogues else None
     decode = measure_decode(ep, W, dev, args.steps) if args.decode else None
     copy_ceiling = measure_copy_ceiling(dev, 20) if args.copy_ceiling else None
+    others = ([n for n in ("tiny", "decode", "ep8", "skewed") if n != args.workload] if args.workloads else [])
+    workloads = measure_workloads(ep, W, dev, others, 20) if others else None
+    if workloads:
+        workloads["note"] = ("per call: events around back-to-back launches; step: eager one-call layout + dispatch "
+                             "then combine, host clock -- for tiny and decode that is bounded by the host's enqueue "
+                             "of the calls, see decode.step_graph_* for the GPU-side decode step")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -532,6 +618,7 @@ def main():
         epilogues=epi,
         decode=decode,
         copy_ceiling=copy_ceiling,
+        workloads=workloads,
     )
     print(json.dumps(line), flush=True)
 
