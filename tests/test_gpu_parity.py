@@ -211,6 +211,8 @@ EDGE = [
     (40, 4, 16, 1, 0, 8, 32768, False, True, "uniform"),      # largest hidden: 64 KiB BF16 rows
     (40, 4, 16, 2, 1, 8, 32768, True, True, "uniform"),       # largest hidden: 32 FP8 segments, windows
     (65536, 8, 256, 1, 0, 128, 128, True, True, "uniform"),   # 256 layout tiles
+    (5, 1, 1, 1, 0, 65536, 8, False, True, "uniform"),        # largest alignment: 65,531 zero-padded rows
+    (300, 2, 2, 2, 1, 65536, 128, True, True, "uniform"),     # largest alignment, FP8, two ranks
 ]
 
 
