@@ -2,18 +2,21 @@
 // on gfx950 ([DeepEP->MegaMoE] §4.3: at small batches the launches, not the bytes, set the time; [DeepEP-hotdry]
 // 性能基准 and [MoE-comm] §一: the low-latency decode path dispatches with the layout of the same call).
 //
-// Every block computes the whole layout of the routing table in LDS -- the counting sort of k_layout_single:
-// stage the entries, rank them per wave with key-bit ballots, per-wave bases, the aligned scans of counts and
-// padding -- and then runs its share of the dispatch work items with the rows taken from LDS.  No block waits
-// for another, so one launch replaces the layout launch and the dispatch launch; the price is that each block
-// repeats the (small, latency-bound) layout work.
+// Workgroup t < T owns token t.  A token's rows need only counts, not a sort: its expert-major row for entry k is
+// the aligned start of the expert, plus the expert's entries in the tokens before t, plus the copies of the
+// expert among entries 0..k-1 of t; its row in rank r's window is the number of tokens before t that have an
+// expert on r.  So every workgroup stages the routing table in LDS and builds, with LDS atomic adds, the column
+// totals (experts | ranks | invalid) and the counts before its own token, runs the aligned scan of the local
+// experts, and writes its token; no workgroup waits for another, and the per-workgroup layout work is two
+// atomic adds per entry instead of a ranking of the whole table.
 //
 // The handle's workspace and the layout outputs are written along the way, so the handle is complete
 // afterwards (ep_dispatch and ep_combine can reuse it as if ep_get_layout had built it): block 0 writes the
-// counts and the psum; the wave of a token's segment 0 writes its slots, its per-rank token rows and its
+// counts and the psum; wave 0 of token t's workgroup writes its slots, its per-rank token rows and its
 // membership; the padding waves write the padding-row list.
-//   token item (t, s)       as in the dispatch kernels (FP8 cast, or 16-byte copies), destinations from LDS;
-//                           its source loads are issued before the layout work, so they overlap it;
+//   token segments          segment s of token t on wave s % 16 of workgroup t, as in the dispatch kernels (FP8
+//                           cast, or 16-byte copies); the first segment's loads are issued before the layout
+//                           work, so they overlap it;
 //   padding-list lanes      lane q of the pass over padding row numbers finds its row by a binary search of
 //                           the padding prefix in LDS, writes the list entry and (without zero padding) the
 //                           row's metadata;
@@ -27,21 +30,18 @@ namespace ep {
 namespace {
 
 constexpr int kMaxPadWaves = 4096;   // padding passes loop beyond this many waves instead of growing the grid
-constexpr int kMinBlocks = 256;      // at least one workgroup per CU of an MI355X: the stores of the dispatch need
-                                     // the store paths of the whole chip, and the layout repeated per workgroup is
-                                     // latency, not throughput
-constexpr uint16_t kNoRow = 0xFFFF;  // per-rank token row "none" in LDS (rows are < 256)
-
-__device__ __forceinline__ int row_or_none(uint16_t v) { return v == kNoRow ? -1 : (int)v; }
+constexpr int kMinBlocks = 256;      // at least one workgroup per CU of an MI355X, and at least one per token (a
+                                     // batch has at most 256 tokens): the padding passes spread over the chip, and
+                                     // the layout repeated per workgroup is latency, not throughput
 
 __host__ __device__ size_t fused_lds_bytes(int E, int K, int R, int epr) {
-    return count_lds_bytes(E, K, R) + sizeof(int) * (2 * (size_t)(epr + 1) + 2 * kWaves) +
-           sizeof(uint16_t) * (size_t)kTile * R;
+    return sizeof(int) * ((size_t)kTile * K + (size_t)(E + R + 1) + (size_t)E + (size_t)R + 2 * (size_t)(epr + 1) +
+                          2 * (size_t)kWaves);
 }
 
 struct FusedArgs {
     const int64_t* idx;
-    int E, A, nbits;
+    int E, A;
     Outputs o;               // counts, psum, padding list and total
     int32_t* slot_ws;        // [T, K] workspace slot map
     int32_t* rows_ws;        // [T, R] workspace per-rank token rows
@@ -51,54 +51,106 @@ struct FusedArgs {
 template <bool FP8>
 __global__ __launch_bounds__(kThreads) void k_layout_dispatch_small(FusedArgs f, Params p) {
     const int T = p.T, K = p.K, R = p.R, E = f.E, epr = p.epr, lo = p.rank * epr;
-    const CountLds L = carve_count(layout_smem, E, K, R);
-    int* psum = reinterpret_cast<int*>(layout_smem + count_lds_bytes(E, K, R));   // [epr + 1]
-    int* padpre = psum + epr + 1;                                                 // [epr + 1]
-    int* scratch = padpre + epr + 1;                                              // [2 * kWaves]
-    uint16_t* trow = reinterpret_cast<uint16_t*>(scratch + 2 * kWaves);           // [256 * R], kNoRow = none
+    int* ent = reinterpret_cast<int*>(layout_smem);   // [256 * K] staged expert ids (-1 none, kBad invalid)
+    int* tot = ent + kTile * K;                       // [E + R + 1] entries per expert | tokens per rank | invalid
+    int* bef = tot + E + R + 1;                       // [E] entries per expert in the tokens before token t
+    int* rbef = bef + E;                              // [R] tokens before token t with an expert on rank r
+    int* psum = rbef + R;                             // [epr + 1]
+    int* padpre = psum + epr + 1;                     // [epr + 1]
+    int* scratch = padpre + epr + 1;                  // [2 * kWaves]
+    const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
+    const int t = blockIdx.x;                         // this workgroup's token (the grid has >= T workgroups)
+    const bool tok = t < T;
+    const int nent = T * K;
 
-    // the token item's source bytes do not depend on the layout: their loads are issued together with the
-    // layout's entry loads and stay in flight through the layout work
-    const int lane = lane_id();
-    // work items are strided over the workgroups (item = wave * workgroups + workgroup), so that a grid larger
-    // than the items spreads them over every CU instead of filling the first workgroups
-    const int64_t gw = (int64_t)(threadIdx.x >> 6) * gridDim.x + blockIdx.x;
-    const bool tok = gw < p.ntok_items;
-    const int t = tok ? (int)(gw / p.nstep) : 0, st = tok ? (int)(gw % p.nstep) : 0;
+    // stage the routing table; the token's first segments (segment s on wave s % 16) and its metadata are loaded
+    // with it, as they do not depend on the layout
+    int64_t v[kEntriesPerThreadMax];
+#pragma unroll
+    for (int u = 0; u < kEntriesPerThreadMax; ++u) {
+        const int j = u * kThreads + tid;
+        v[u] = j < nent ? f.idx[j] : -1;
+    }
+    const bool seg_first = tok && w < p.nstep;
     Fp8Src v8;
     u32x4 vr;
     TokenEntry te;
-    auto prefetch = [&] {
-        if (tok) {
-            if (FP8) v8 = fp8_load(p, t, st, lane);
-            else vr = raw_load(p, t, st, lane);
-            if (st == 0) te = token_entry(p, t, lane);
-        }
-    };
-
-    // the layout, in LDS
-    const uint64_t mask = count_tile(f.idx, T, K, E, R, epr, f.nbits, 0, L, nullptr, prefetch);
-    local_scan(epr, lo, f.A, L.row, psum, padpre, scratch);
-    token_rows(L, mask, T, R, 0, [&](int t, int r, int v) { trow[t * R + r] = v < 0 ? kNoRow : (uint16_t)v; });
+    if (seg_first) {
+        if (FP8) v8 = fp8_load(p, t, w, lane);
+        else vr = raw_load(p, t, w, lane);
+        if (w == 0) te = token_entry(p, t, lane);
+    }
+    for (int i = tid; i < E + R + 1; i += kThreads) tot[i] = 0;
+    for (int i = tid; i < E; i += kThreads) bef[i] = 0;
+    if (tid < R) rbef[tid] = 0;
+    int st[kEntriesPerThreadMax];
+#pragma unroll
+    for (int u = 0; u < kEntriesPerThreadMax; ++u) {
+        const int j = u * kThreads + tid;
+        st[u] = (v[u] >= 0 && v[u] < E) ? (int)v[u] : (v[u] == -1 ? -1 : kBad);
+        if (j < nent) ent[j] = st[u];
+    }
     __syncthreads();
-    if (blockIdx.x == 0) write_counts(E, R, lo, epr, L.row, psum, padpre, f.o);
 
-    // token item
-    if (tok) {
-        int sexp = -1;                                 // expert-major row of entry (t, lane)
+    // Counts by LDS atomic adds (the order of the adds does not change a count): entries per expert, in all tokens
+    // and in the tokens before t; invalid entries; tokens per rank, in all tokens and before t.  The token's rows
+    // follow from these alone -- expert-major row = aligned start of the expert + its entries before t + its
+    // earlier copies in t, window row = tokens before t with an expert on that rank -- so no workgroup ranks
+    // the whole table.
+    int inv = 0;
+#pragma unroll
+    for (int u = 0; u < kEntriesPerThreadMax; ++u) {
+        const int j = u * kThreads + tid;
+        const int e = j < nent ? st[u] : -1;
+        if (e >= 0) {
+            atomicAdd(&tot[e], 1);
+            if (j < t * K) atomicAdd(&bef[e], 1);
+        }
+        inv += popc64(ballot(e == kBad));
+    }
+    if (lane == 0 && inv != 0) atomicAdd(&tot[E + R], inv);
+    // expert -> owning rank as floor((e + 0.5) / epr) in fp32: exact for e < 1024, epr <= 1024
+    const float inv_epr = 1.0f / (float)epr;
+    if (tid < T) {
+        uint64_t m = 0ull;
+        for (int k = 0; k < K; ++k) {
+            const int e = ent[tid * K + k];
+            if (e >= 0) m |= 1ull << (int)(((float)e + 0.5f) * inv_epr);
+        }
+        for (uint64_t mm = m; mm != 0; mm &= mm - 1) {
+            const int r = __builtin_ctzll(mm);
+            atomicAdd(&tot[E + r], 1);
+            if (tid < t) atomicAdd(&rbef[r], 1);
+        }
+    }
+    __syncthreads();
+    local_scan(epr, lo, f.A, tot, psum, padpre, scratch);
+    if (blockIdx.x == 0) write_counts(E, R, lo, epr, tot, psum, padpre, f.o);
+
+    // token t: its rows (lane k < K: expert-major row of entry k; lane r < R: row in rank r's window), then its
+    // segments, segment s on wave s % 16
+    if (tok && w < p.nstep) {
+        int sexp = -1;
         if (lane < K) {
-            const int pk = L.ent[t * K + lane];
-            if (pk >= 0) {
-                const int e = pk & kPackMask;
-                if (e >= lo && e < lo + epr)
-                    sexp = psum[e - lo] + L.cnt_w[(t / tokens_per_wave(T, 0)) * E + e] + (pk >> kPackShift);
+            const int e = ent[t * K + lane];
+            if (e >= lo && e < lo + epr) {
+                int dup = 0;                                   // earlier copies of e in this token
+                for (int k = 0; k < lane; ++k) dup += ent[t * K + k] == e ? 1 : 0;
+                sexp = psum[e - lo] + bef[e] + dup;
             }
         }
-        const int own = lane < R ? row_or_none(trow[t * R + lane]) : -1;
-        const int ds = p.token_major ? (lane == 0 ? row_or_none(trow[t * R + p.rank]) : -1) : sexp;
-        const int js = (p.send_slot != nullptr && lane != p.rank) ? own : -1;
+        bool has = false;
+        if (lane < R)
+            for (int k = 0; k < K; ++k) {
+                const int e = ent[t * K + k];
+                if (e >= 0 && (int)(((float)e + 0.5f) * inv_epr) == lane) has = true;
+            }
+        const int own = has ? rbef[lane] : -1;
+        const int own_here = readlane(own, p.rank);        // the token's row among this rank's tokens
+        const int ds = p.token_major ? (lane == 0 ? own_here : -1) : sexp;
+        const int js = (p.send_slot != nullptr && lane < R && lane != p.rank) ? own : -1;
         const uint64_t lmask = ballot(ds >= 0), smask = ballot(js >= 0);
-        if (st == 0) {
+        if (w == 0) {
             if (lane < K) f.slot_ws[(int64_t)t * K + lane] = sexp;
             if (lane < R) {
                 f.rows_ws[(int64_t)t * R + lane] = own;
@@ -107,12 +159,15 @@ __global__ __launch_bounds__(kThreads) void k_layout_dispatch_small(FusedArgs f,
             token_meta(p, t, lane, ds, js, lmask, smask, &te);
         }
         if ((lmask | smask) != 0) {
-            if (FP8) fp8_emit(p, st, lane, v8, ds, js, lmask, smask);
-            else raw_emit(p, t, st, lane, vr, ds, js, lmask, smask);
+            for (int s = w; s < p.nstep; s += kWaves) {
+                if (FP8) fp8_emit(p, s, lane, s == w ? v8 : fp8_load(p, t, s, lane), ds, js, lmask, smask);
+                else raw_emit(p, t, s, lane, s == w ? vr : raw_load(p, t, s, lane), ds, js, lmask, smask);
+            }
         }
     }
 
     // padding: the row list (and, without zero padding, the rows' metadata), one row number per lane
+    const int64_t gw = (int64_t)w * gridDim.x + blockIdx.x;
     const int npad = padpre[epr];
     const bool meta_only = !p.token_major && !p.zero_pad && (p.recv_src != nullptr || p.recv_w != nullptr);
     for (int64_t q = gw * kWave + lane; q < npad; q += p.nwaves * kWave) {
@@ -144,10 +199,10 @@ hipError_t launch_layout_dispatch(const Handle& h, const LayoutOutputs& out, con
     const bool fp8 = a.mode == DispatchArgs::kFp8;
     Params p = dispatch_params(h, a);
     const int64_t max_pad = (int64_t)h.El * (h.A - 1);
-    int64_t nwaves = p.ntok_items;
     int64_t pad_waves = (max_pad + kWave - 1) / kWave;
     if (p.zero_pad && !p.token_major) pad_waves = std::max(pad_waves, (max_pad * p.nstep + kPadItemsPerWave - 1) / kPadItemsPerWave);
-    nwaves = std::max(nwaves, std::min(pad_waves, (int64_t)kMaxPadWaves));
+    const int64_t nwaves = std::min(pad_waves, (int64_t)kMaxPadWaves);
+    static_assert(kMinBlocks >= kTile, "workgroup t owns token t of a one-tile batch");
     const int64_t nblocks = std::max<int64_t>((nwaves + kWaves - 1) / kWaves, kMinBlocks);
     p.nwaves = nblocks * kWaves;
 
@@ -155,8 +210,6 @@ hipError_t launch_layout_dispatch(const Handle& h, const LayoutOutputs& out, con
     f.idx = h.topk_idx;
     f.E = h.E;
     f.A = h.A;
-    f.nbits = 0;
-    while ((1 << f.nbits) < h.E) ++f.nbits;
     f.o = Outputs{h.ws.cnt_local, h.ws.psum, h.ws.pad_rows, h.ws.pad_total, out.num_tokens_per_rank,
                   out.num_tokens_per_expert, out.psum, out.num_invalid};
     f.slot_ws = h.ws.slot;

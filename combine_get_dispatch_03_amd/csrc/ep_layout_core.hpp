@@ -46,12 +46,12 @@ __device__ __forceinline__ int tokens_per_wave(int T, int tile) {
     return max(1, (ntok + kWaves - 1) / kWaves);
 }
 
-__host__ __device__ size_t count_lds_bytes(int E, int K, int R) {
+__host__ __device__ inline size_t count_lds_bytes(int E, int K, int R) {
     return align16(sizeof(uint16_t) * kWaves * (size_t)E) +
            sizeof(int32_t) * ((size_t)kTile * K + 4 * (size_t)R + kWaves + (size_t)(E + R + 1));
 }
 
-__device__ CountLds carve_count(unsigned char* base, int E, int K, int R) {
+__device__ inline CountLds carve_count(unsigned char* base, int E, int K, int R) {
     CountLds L;
     L.cnt_w = reinterpret_cast<uint16_t*>(base);
     L.ent = reinterpret_cast<int32_t*>(base + align16(sizeof(uint16_t) * kWaves * (size_t)E));
@@ -191,7 +191,7 @@ __device__ __forceinline__ void token_rows(const CountLds& L, uint64_t mask, int
     }
 }
 
-__device__ void send_rows(const CountLds& L, uint64_t mask, int T, int R, int tile, int32_t* __restrict__ out) {
+__device__ inline void send_rows(const CountLds& L, uint64_t mask, int T, int R, int tile, int32_t* __restrict__ out) {
     token_rows(L, mask, T, R, tile, [&](int t, int r, int v) { out[(int64_t)t * R + r] = v; });
 }
 
@@ -307,7 +307,7 @@ __device__ void write_counts(int E, int R, int lo, int epr, const int* total, co
 // Finalizing phase shared by both layout paths.  `total` holds the column totals over all tiles (experts |
 // ranks | invalid).  Computes psum / padpre (LDS), block 0 writes the global outputs, and each of the nblk
 // layout blocks writes its share (experts blockIdx.x + i * nblk) of the dense padding-row list.
-__device__ void finalize_core(int E, int R, int rank, int epr, int A, const int* total, int* psum, int* padpre,
+__device__ inline void finalize_core(int E, int R, int rank, int epr, int A, const int* total, int* psum, int* padpre,
                               int* scratch, const Outputs& o, int nblk) {
     const int tid = threadIdx.x;
     const int lo = rank * epr;
