@@ -34,11 +34,6 @@ constexpr int kMinBlocks = 256;      // at least one workgroup per CU of an MI35
                                      // batch has at most 256 tokens): the padding passes spread over the chip, and
                                      // the layout repeated per workgroup is latency, not throughput
 
-__host__ __device__ size_t fused_lds_bytes(int E, int K, int R, int epr) {
-    return sizeof(int) * ((size_t)kTile * K + (size_t)(E + R + 1) + (size_t)E + (size_t)R + 2 * (size_t)(epr + 1) +
-                          2 * (size_t)kWaves);
-}
-
 struct FusedArgs {
     const int64_t* idx;
     int E, A;
@@ -51,101 +46,30 @@ struct FusedArgs {
 template <bool FP8>
 __global__ __launch_bounds__(kThreads) void k_layout_dispatch_small(FusedArgs f, Params p) {
     const int T = p.T, K = p.K, R = p.R, E = f.E, epr = p.epr, lo = p.rank * epr;
-    int* ent = reinterpret_cast<int*>(layout_smem);   // [256 * K] staged expert ids (-1 none, kBad invalid)
-    int* tot = ent + kTile * K;                       // [E + R + 1] entries per expert | tokens per rank | invalid
-    int* bef = tot + E + R + 1;                       // [E] entries per expert in the tokens before token t
-    int* rbef = bef + E;                              // [R] tokens before token t with an expert on rank r
-    int* psum = rbef + R;                             // [epr + 1]
-    int* padpre = psum + epr + 1;                     // [epr + 1]
-    int* scratch = padpre + epr + 1;                  // [2 * kWaves]
-    const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
+    const TokLds L = carve_tok(layout_smem, E, K, R, epr);
+    const int lane = lane_id(), w = threadIdx.x >> 6;
     const int t = blockIdx.x;                         // this workgroup's token (the grid has >= T workgroups)
     const bool tok = t < T;
-    const int nent = T * K;
 
-    // stage the routing table; the token's first segments (segment s on wave s % 16) and its metadata are loaded
-    // with it, as they do not depend on the layout
-    int64_t v[kEntriesPerThreadMax];
-#pragma unroll
-    for (int u = 0; u < kEntriesPerThreadMax; ++u) {
-        const int j = u * kThreads + tid;
-        v[u] = j < nent ? f.idx[j] : -1;
-    }
-    const bool seg_first = tok && w < p.nstep;
+    // the token's first segments (segment s on wave s % 16) and its metadata do not depend on the layout: their
+    // loads are issued with the routing table's and stay in flight through the layout work
     Fp8Src v8;
     u32x4 vr;
     TokenEntry te;
-    if (seg_first) {
-        if (FP8) v8 = fp8_load(p, t, w, lane);
-        else vr = raw_load(p, t, w, lane);
-        if (w == 0) te = token_entry(p, t, lane);
-    }
-    for (int i = tid; i < E + R + 1; i += kThreads) tot[i] = 0;
-    for (int i = tid; i < E; i += kThreads) bef[i] = 0;
-    if (tid < R) rbef[tid] = 0;
-    int st[kEntriesPerThreadMax];
-#pragma unroll
-    for (int u = 0; u < kEntriesPerThreadMax; ++u) {
-        const int j = u * kThreads + tid;
-        st[u] = (v[u] >= 0 && v[u] < E) ? (int)v[u] : (v[u] == -1 ? -1 : kBad);
-        if (j < nent) ent[j] = st[u];
-    }
-    __syncthreads();
-
-    // Counts by LDS atomic adds (the order of the adds does not change a count): entries per expert, in all tokens
-    // and in the tokens before t; invalid entries; tokens per rank, in all tokens and before t.  The token's rows
-    // follow from these alone -- expert-major row = aligned start of the expert + its entries before t + its
-    // earlier copies in t, window row = tokens before t with an expert on that rank -- so no workgroup ranks
-    // the whole table.
-    int inv = 0;
-#pragma unroll
-    for (int u = 0; u < kEntriesPerThreadMax; ++u) {
-        const int j = u * kThreads + tid;
-        const int e = j < nent ? st[u] : -1;
-        if (e >= 0) {
-            atomicAdd(&tot[e], 1);
-            if (j < t * K) atomicAdd(&bef[e], 1);
+    tok_counts(f.idx, T, K, E, R, epr, f.A, lo, t, L, [&] {
+        if (tok && w < p.nstep) {
+            if (FP8) v8 = fp8_load(p, t, w, lane);
+            else vr = raw_load(p, t, w, lane);
+            if (w == 0) te = token_entry(p, t, lane);
         }
-        inv += popc64(ballot(e == kBad));
-    }
-    if (lane == 0 && inv != 0) atomicAdd(&tot[E + R], inv);
-    // expert -> owning rank as floor((e + 0.5) / epr) in fp32: exact for e < 1024, epr <= 1024
-    const float inv_epr = 1.0f / (float)epr;
-    if (tid < T) {
-        uint64_t m = 0ull;
-        for (int k = 0; k < K; ++k) {
-            const int e = ent[tid * K + k];
-            if (e >= 0) m |= 1ull << (int)(((float)e + 0.5f) * inv_epr);
-        }
-        for (uint64_t mm = m; mm != 0; mm &= mm - 1) {
-            const int r = __builtin_ctzll(mm);
-            atomicAdd(&tot[E + r], 1);
-            if (tid < t) atomicAdd(&rbef[r], 1);
-        }
-    }
-    __syncthreads();
-    local_scan(epr, lo, f.A, tot, psum, padpre, scratch);
-    if (blockIdx.x == 0) write_counts(E, R, lo, epr, tot, psum, padpre, f.o);
+    });
+    if (blockIdx.x == 0) write_counts(E, R, lo, epr, L.tot, L.psum, L.padpre, f.o);
 
     // token t: its rows (lane k < K: expert-major row of entry k; lane r < R: row in rank r's window), then its
     // segments, segment s on wave s % 16
     if (tok && w < p.nstep) {
-        int sexp = -1;
-        if (lane < K) {
-            const int e = ent[t * K + lane];
-            if (e >= lo && e < lo + epr) {
-                int dup = 0;                                   // earlier copies of e in this token
-                for (int k = 0; k < lane; ++k) dup += ent[t * K + k] == e ? 1 : 0;
-                sexp = psum[e - lo] + bef[e] + dup;
-            }
-        }
-        bool has = false;
-        if (lane < R)
-            for (int k = 0; k < K; ++k) {
-                const int e = ent[t * K + k];
-                if (e >= 0 && (int)(((float)e + 0.5f) * inv_epr) == lane) has = true;
-            }
-        const int own = has ? rbef[lane] : -1;
+        int sexp, own;
+        tok_rows(L, t, K, R, lo, epr, sexp, own);
         const int own_here = readlane(own, p.rank);        // the token's row among this rank's tokens
         const int ds = p.token_major ? (lane == 0 ? own_here : -1) : sexp;
         const int js = (p.send_slot != nullptr && lane < R && lane != p.rank) ? own : -1;
@@ -168,10 +92,10 @@ __global__ __launch_bounds__(kThreads) void k_layout_dispatch_small(FusedArgs f,
 
     // padding: the row list (and, without zero padding, the rows' metadata), one row number per lane
     const int64_t gw = (int64_t)w * gridDim.x + blockIdx.x;
-    const int npad = padpre[epr];
+    const int npad = L.padpre[epr];
     const bool meta_only = !p.token_major && !p.zero_pad && (p.recv_src != nullptr || p.recv_w != nullptr);
     for (int64_t q = gw * kWave + lane; q < npad; q += p.nwaves * kWave) {
-        const int row = pad_row_of((int)q, epr, psum, padpre);
+        const int row = pad_row_of((int)q, epr, L.psum, L.padpre);
         if (f.o.pad_rows) f.o.pad_rows[q] = row;
         if (meta_only) pad_meta_row(p, row);
     }
@@ -180,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void k_layout_dispatch_small(FusedArgs f,
         const int64_t nitems = (int64_t)npad * p.nstep;
         for (int64_t i = gw; i < nitems; i += p.nwaves) {
             const int q = (int)(i / p.nstep);
-            pad_zero_segment<FP8>(p, pad_row_of(q, epr, psum, padpre), (int)(i % p.nstep), lane);
+            pad_zero_segment<FP8>(p, pad_row_of(q, epr, L.psum, L.padpre), (int)(i % p.nstep), lane);
         }
     }
 }
@@ -216,7 +140,7 @@ hipError_t launch_layout_dispatch(const Handle& h, const LayoutOutputs& out, con
     f.rows_ws = h.ws.send_slot;
     f.in_rank = out.is_token_in_rank;
 
-    const size_t lds = fused_lds_bytes(h.E, h.K, h.R, h.El);
+    const size_t lds = tok_lds_bytes(h.E, h.K, h.R, h.El);
     if (lds > 65536) {
         const void* k = fp8 ? reinterpret_cast<const void*>(k_layout_dispatch_small<true>)
                             : reinterpret_cast<const void*>(k_layout_dispatch_small<false>);

@@ -3,7 +3,8 @@
 // token-in-rank membership; [DeepEP->MegaMoE] §2.2: per-expert counts and their prefix sum; §2.4: the prefix
 // sum is each expert's start cursor; the same page's cross-reference names the scheme a counting sort).
 //
-// Deterministic throughout (no atomics decide a position).  Work is cut into 256-token tiles.
+// Deterministic throughout: no atomic operation decides a position (the one-tile path counts with LDS atomic
+// adds, whose totals do not depend on their order).  Work is cut into 256-token tiles.
 //   counting phase     (one 1024-thread block per tile) the tile's entries are staged in LDS with one
 //                      cooperative load; each of 16 waves ranks its 16 tokens' entries in flat order with
 //                      key-bit ballots (peers = lanes holding the same expert) against a per-wave LDS
@@ -14,8 +15,9 @@
 //                      prefix, global counts, the dense padding-row list, and the final row of every entry.
 // More than one tile: k_layout_count (counting, tile rows + tile-local ranks to the workspace) then
 // k_layout_finalize (one block per tile, each re-summing the tile rows it needs).  One tile (<= 256 tokens,
-// the decode shape): k_layout_single does both phases without leaving LDS, in one launch; each of its
-// workgroups repeats the small layout and writes a share of the outputs.
+// the decode shape): k_layout_tokens, one launch of one workgroup per token; each stages the table, counts the
+// column totals and the entries and tokens before its own token, scans, and writes that token's rows, which
+// follow from those counts alone (no ranking of the table).
 #include <algorithm>
 
 #include "ep_layout_core.hpp"
@@ -182,36 +184,34 @@ __global__ __launch_bounds__(kThreads) void k_layout_finalize(
 // Every workgroup computes the whole (small) layout in LDS; workgroup 0 writes the counts, the membership and the
 // per-rank token rows, and the workgroups share the slot map and the padding list (finalize_core's split).
 
-constexpr int kSingleMaxBlocks = 64;
-
-__global__ __launch_bounds__(kThreads) void k_layout_single(
-    const int64_t* __restrict__ idx, int T, int K, int E, int R, int rank, int epr, int A, int nbits,
+// One tile (<= 256 tokens): workgroup t < T stages the table, counts and writes token t's slots, per-rank rows
+// and membership (its wave 0); block 0 writes the counts; wave g of the grid writes the padding rows of the
+// local experts g, g + waves, ...
+__global__ __launch_bounds__(kThreads) void k_layout_tokens(
+    const int64_t* __restrict__ idx, int T, int K, int E, int R, int rank, int epr, int A,
     int32_t* __restrict__ slot, int32_t* __restrict__ send_slot, uint8_t* __restrict__ in_rank_out, Outputs o) {
-    const CountLds L = carve_count(layout_smem, E, K, R);
-    int* psum = reinterpret_cast<int*>(layout_smem + count_lds_bytes(E, K, R));   // [epr + 1]
-    int* padpre = psum + epr + 1;                                                 // [epr + 1]
-    int* scratch = padpre + epr + 1;                                              // [2 * kWaves]
-    const int lo = rank * epr;
-    const bool first = blockIdx.x == 0;
-    const uint64_t mask = count_tile(idx, T, K, E, R, epr, nbits, 0, L, first ? in_rank_out : nullptr);
-    finalize_core(E, R, rank, epr, A, L.row, psum, padpre, scratch, o, (int)gridDim.x);
-    // this workgroup's slice of the slot map
-    const int tpw = tokens_per_wave(T, 0);
-    for (int j = (int)blockIdx.x * kThreads + (int)threadIdx.x; j < T * K; j += (int)gridDim.x * kThreads) {
-        const int p = L.ent[j];
-        int s = -1;
-        if (p >= 0) {
-            const int e = p & kPackMask;
-            const int wv = (j / K) / tpw;
-            if (e >= lo && e < lo + epr) s = psum[e - lo] + L.cnt_w[wv * E + e] + (p >> kPackShift);
+    const TokLds L = carve_tok(layout_smem, E, K, R, epr);
+    const int lo = rank * epr, t = blockIdx.x, lane = lane_id(), w = threadIdx.x >> 6;
+    tok_counts(idx, T, K, E, R, epr, A, lo, t, L, [] {});
+    if (blockIdx.x == 0) write_counts(E, R, lo, epr, L.tot, L.psum, L.padpre, o);
+    if (t < T && w == 0) {
+        int sexp, own;
+        tok_rows(L, t, K, R, lo, epr, sexp, own);
+        if (lane < K) slot[(int64_t)t * K + lane] = sexp;
+        if (lane < R) {
+            send_slot[(int64_t)t * R + lane] = own;
+            if (in_rank_out) in_rank_out[(int64_t)t * R + lane] = own >= 0 ? 1 : 0;
         }
-        slot[j] = s;
     }
-    if (first) send_rows(L, mask, T, R, 0, send_slot);
-}
-
-size_t single_lds_bytes(int E, int K, int R, int epr) {
-    return count_lds_bytes(E, K, R) + sizeof(int) * (2 * (size_t)(epr + 1) + 2 * kWaves);
+    if (o.pad_rows != nullptr) {
+        const int nw = (int)gridDim.x * kWaves;
+        for (int j = w * (int)gridDim.x + (int)blockIdx.x; j < epr; j += nw) {
+            const int first = L.psum[j] + L.tot[lo + j];
+            const int n = L.psum[j + 1] - first;
+            int32_t* dst = o.pad_rows + L.padpre[j];
+            for (int r = lane; r < n; r += kWave) dst[r] = first + r;
+        }
+    }
 }
 
 }  // namespace
@@ -226,16 +226,15 @@ hipError_t launch_layout(const Handle& h, const LayoutOutputs& out, hipStream_t 
                     out.num_tokens_per_expert, out.psum, out.num_invalid};
 
     if (h.ntiles == 1) {
-        const size_t lds = single_lds_bytes(h.E, h.K, h.R, epr);
+        const size_t lds = tok_lds_bytes(h.E, h.K, h.R, epr);
         if (lds > 65536) {
-            const hipError_t err = allow_dynamic_lds(reinterpret_cast<const void*>(k_layout_single), (int)lds);
+            const hipError_t err = allow_dynamic_lds(reinterpret_cast<const void*>(k_layout_tokens), (int)lds);
             if (err != hipSuccess) return err;
         }
-        // one workgroup per 16 local experts (one expert's padding rows per wave), each repeating the small layout
-        // in LDS, so that the padding list and the slot map are written by several CUs
-        const int nblk = std::min(kSingleMaxBlocks, std::max(1, (epr + kWaves - 1) / kWaves));
-        hipLaunchKernelGGL(k_layout_single, dim3(nblk), dim3(kThreads), lds, stream, h.topk_idx, h.T, h.K, h.E, h.R,
-                           h.rank, epr, h.A, nbits, h.ws.slot, send, out.is_token_in_rank, o);
+        // one workgroup per token, each repeating the counts in LDS
+        hipLaunchKernelGGL(k_layout_tokens, dim3((unsigned)h.T), dim3(kThreads), lds, stream, h.topk_idx, h.T, h.K,
+                           h.E, h.R, h.rank, epr, h.A, h.ws.slot, send,
+                           out.is_token_in_rank, o);
         return hipGetLastError();
     }
     // the span the caller reads next, in 16-byte units: the count kernel's extra blocks read the first

@@ -340,5 +340,121 @@ __device__ __forceinline__ int pad_row_of(int q, int epr, const int* psum, const
     return psum[lo + 1] - (padpre[lo + 1] - q);
 }
 
+// ---- per-token layout of one tile (<= 256 tokens) ---------------------------------------------------------
+// A token's rows follow from counts alone ([DeepEP->MegaMoE] §2.2: rows stable in (token, k) order): the
+// expert-major row of its entry k is the aligned start of the expert, plus the expert's entries in the tokens
+// before it, plus the copies of the expert among its entries 0..k-1; its row in rank r's window is the number
+// of tokens before it with an expert on r.  A workgroup that writes token t stages the routing table and builds
+// these counts with LDS atomic adds (the order of the adds does not change a count, so the result is
+// deterministic), then the aligned scan of the local experts.
+struct TokLds {
+    int* ent;       // [256 * K]   staged expert ids (-1 none, kBad invalid)
+    int* tot;       // [E + R + 1] column totals: entries per expert | tokens per rank | invalid entries
+    int* bef;       // [E]         entries per expert in the tokens before t
+    int* rbef;      // [R]         tokens before t with an expert on rank r
+    int* psum;      // [epr + 1]   aligned prefix of the local experts
+    int* padpre;    // [epr + 1]   padding prefix of the local experts
+    int* scratch;   // [2 * kWaves]
+};
+
+__host__ __device__ inline size_t tok_lds_bytes(int E, int K, int R, int epr) {
+    return sizeof(int) * ((size_t)kTile * K + 2 * (size_t)E + 2 * (size_t)R + 1 + 2 * (size_t)(epr + 1) +
+                          2 * (size_t)kWaves);
+}
+
+__device__ inline TokLds carve_tok(unsigned char* base, int E, int K, int R, int epr) {
+    TokLds L;
+    L.ent = reinterpret_cast<int*>(base);
+    L.tot = L.ent + kTile * K;
+    L.bef = L.tot + E + R + 1;
+    L.rbef = L.bef + E;
+    L.psum = L.rbef + R;
+    L.padpre = L.psum + epr + 1;
+    L.scratch = L.padpre + epr + 1;
+    return L;
+}
+
+// expert -> owning rank as floor((e + 0.5) / epr) in fp32: exact for e < 1024, epr <= 1024
+__device__ __forceinline__ int rank_of(int e, float inv_epr) { return (int)(((float)e + 0.5f) * inv_epr); }
+
+// Stage the table, count (totals and counts before token t; t >= T counts nothing before), scan.  `pre` runs
+// right after the entry loads are issued (loads that do not depend on the layout go there).  Every thread of
+// the block calls it; it ends with a barrier.
+template <class Pre>
+__device__ inline void tok_counts(const int64_t* __restrict__ idx, int T, int K, int E, int R, int epr, int A,
+                                  int lo, int t, const TokLds& L, Pre pre) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int nent = T * K;
+    static_assert(kTile * kMaxTopk <= kEntriesPerThreadMax * kThreads, "one staging pass per tile");
+    int64_t v[kEntriesPerThreadMax];
+#pragma unroll
+    for (int u = 0; u < kEntriesPerThreadMax; ++u) {
+        const int j = u * kThreads + tid;
+        v[u] = j < nent ? idx[j] : -1;
+    }
+    pre();
+    for (int i = tid; i < E + R + 1; i += kThreads) L.tot[i] = 0;
+    for (int i = tid; i < E; i += kThreads) L.bef[i] = 0;
+    if (tid < R) L.rbef[tid] = 0;
+    int st[kEntriesPerThreadMax];
+#pragma unroll
+    for (int u = 0; u < kEntriesPerThreadMax; ++u) {
+        const int j = u * kThreads + tid;
+        st[u] = (v[u] >= 0 && v[u] < E) ? (int)v[u] : (v[u] == -1 ? -1 : kBad);
+        if (j < nent) L.ent[j] = st[u];
+    }
+    __syncthreads();
+    int inv = 0;
+#pragma unroll
+    for (int u = 0; u < kEntriesPerThreadMax; ++u) {
+        const int j = u * kThreads + tid;
+        const int e = j < nent ? st[u] : -1;
+        if (e >= 0) {
+            atomicAdd(&L.tot[e], 1);
+            if (j < t * K) atomicAdd(&L.bef[e], 1);
+        }
+        inv += popc64(ballot(e == kBad));
+    }
+    if (lane == 0 && inv != 0) atomicAdd(&L.tot[E + R], inv);
+    const float inv_epr = 1.0f / (float)epr;
+    if (tid < T) {                                   // token tid: the ranks it goes to
+        uint64_t m = 0ull;
+        for (int k = 0; k < K; ++k) {
+            const int e = L.ent[tid * K + k];
+            if (e >= 0) m |= 1ull << rank_of(e, inv_epr);
+        }
+        for (uint64_t mm = m; mm != 0; mm &= mm - 1) {
+            const int r = __builtin_ctzll(mm);
+            atomicAdd(&L.tot[E + r], 1);
+            if (tid < t) atomicAdd(&L.rbef[r], 1);
+        }
+    }
+    __syncthreads();
+    local_scan(epr, lo, A, L.tot, L.psum, L.padpre, L.scratch);
+}
+
+// Token t's rows (t < T), in one wave: lane k < K gets the expert-major row of entry k (-1 if the expert is not
+// local or the entry not valid), lane r < R the token's row in rank r's window (-1 if it has no expert on r).
+__device__ inline void tok_rows(const TokLds& L, int t, int K, int R, int lo, int epr, int& sexp, int& own) {
+    const int lane = lane_id();
+    const float inv_epr = 1.0f / (float)epr;
+    sexp = -1;
+    if (lane < K) {
+        const int e = L.ent[t * K + lane];
+        if (e >= lo && e < lo + epr) {
+            int dup = 0;                             // earlier copies of e in this token
+            for (int k = 0; k < lane; ++k) dup += L.ent[t * K + k] == e ? 1 : 0;
+            sexp = L.psum[e - lo] + L.bef[e] + dup;
+        }
+    }
+    bool has = false;
+    if (lane < R)
+        for (int k = 0; k < K; ++k) {
+            const int e = L.ent[t * K + k];
+            if (e >= 0 && rank_of(e, inv_epr) == lane) has = true;
+        }
+    own = has ? L.rbef[lane] : -1;
+}
+
 }  // namespace
 }  // namespace ep
