@@ -12,7 +12,7 @@
 namespace ep {
 
 constexpr uint32_t kHandleMagic = 0x45504831u;   // "EPH1"
-constexpr int kLayoutTileTokens = 256;           // tokens per layout tile (4 waves x 64 tokens)
+constexpr int kLayoutTileTokens = 256;           // tokens per layout tile (one 1024-thread block)
 constexpr int kMaxTopk = 32;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxRanks = 64;

@@ -163,8 +163,8 @@ ep_status_t ep_dispatch(ep_handle_t handle, const void* x, int hidden, const flo
 
 /*
  * ep_layout_dispatch -- ep_get_layout and ep_dispatch in one call: the same arguments, the same outputs and the
- * same handle, bit for bit.  For num_tokens <= 256 (the decode shape) both run in a single kernel launch: every
- * workgroup builds the small layout in LDS and dispatches its share of the rows, so no launch waits for another
+ * same handle, bit for bit.  For num_tokens <= 256 (the decode shape) both run in a single kernel launch:
+ * workgroup t counts in LDS what token t's rows follow from and dispatches token t, so no workgroup waits for another
  * ([DeepEP->MegaMoE] §4.3: at small batches launch overhead, not bytes, sets the time; [DeepEP-hotdry]
  * 性能基准: the low-latency decode path).  Larger batches run the layout and the dispatch launches back to back;
  * when x is 16 to 64 MiB the layout launches also read it (and store nothing) while the layout runs, so that
