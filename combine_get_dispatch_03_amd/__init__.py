@@ -96,12 +96,22 @@ def _check(status: int, what: str):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # a plain int: the c_void_p argument types convert it (cheaper than building a c_void_p per pointer)
+    return None if t is None else t.data_ptr()
+
+
+# torch's current raw stream without building a Stream object (~0.2 us instead of ~2.5 us per call)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_cur_device = getattr(torch._C, "_cuda_getDevice", None)
 
 
 def _stream(stream):
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    """HIP stream handle: the given torch stream's, else torch's current stream on the current device."""
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None and _cur_device is not None:
+        return _raw_stream(_cur_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _need(t, dtype, name, device=None, shape=None):
@@ -137,7 +147,15 @@ class Handle:
         self.num_tokens, self.num_topk, self.num_experts = num_tokens, num_topk, num_experts
         self.num_ranks, self.rank, self.expert_alignment = num_ranks, rank, expert_alignment
         self.num_local_experts = num_experts // num_ranks
-        self.recv_capacity = ep_recv_capacity(num_tokens, num_topk, self.num_local_experts, expert_alignment)
+        self._cap = None
+
+    @property
+    def recv_capacity(self):
+        """Rows of the expert-major receive buffers (ep_recv_capacity of the handle's sizes)."""
+        if self._cap is None:
+            self._cap = ep_recv_capacity(self.num_tokens, self.num_topk, self.num_local_experts,
+                                         self.expert_alignment)
+        return self._cap
 
     @property
     def ptr(self):
@@ -163,11 +181,11 @@ def _layout_prep(topk_idx, num_experts, num_ranks, expert_alignment, workspace, 
         raise ValueError("topk_idx must be [num_tokens, num_topk]")
     T, K = topk_idx.shape
     dev = topk_idx.device
-    nbytes = ep_layout_workspace_bytes(T, K, num_experts, num_ranks, expert_alignment)
-    if nbytes == 0:
-        raise EPError("ep_layout_workspace_bytes rejected the sizes (T=%d K=%d E=%d R=%d A=%d)"
-                      % (T, K, num_experts, num_ranks, expert_alignment))
-    if workspace is None:
+    if workspace is None:   # a caller's workspace is checked (sizes and length) by the library call itself
+        nbytes = ep_layout_workspace_bytes(T, K, num_experts, num_ranks, expert_alignment)
+        if nbytes == 0:
+            raise EPError("ep_layout_workspace_bytes rejected the sizes (T=%d K=%d E=%d R=%d A=%d)"
+                          % (T, K, num_experts, num_ranks, expert_alignment))
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     El = num_experts // max(num_ranks, 1)
     if outputs is None:
@@ -180,10 +198,13 @@ def _layout_prep(topk_idx, num_experts, num_ranks, expert_alignment, workspace, 
     return T, K, workspace, outputs
 
 
+_LAYOUT_KEYS = ("num_tokens_per_rank", "num_tokens_per_expert", "is_token_in_rank",
+                "psum_num_recv_tokens_per_expert", "num_invalid_topk")
+
+
 def _layout_ptrs(outputs):
-    return (_ptr(outputs.get("num_tokens_per_rank")), _ptr(outputs.get("num_tokens_per_expert")),
-            _ptr(outputs.get("is_token_in_rank")), _ptr(outputs.get("psum_num_recv_tokens_per_expert")),
-            _ptr(outputs.get("num_invalid_topk")))
+    g = outputs.get
+    return tuple(None if t is None else t.data_ptr() for t in (g(k) for k in _LAYOUT_KEYS))
 
 
 def ep_get_layout(topk_idx, num_experts, num_ranks=1, rank=0, expert_alignment=1, workspace=None, outputs=None,
@@ -195,9 +216,7 @@ def ep_get_layout(topk_idx, num_experts, num_ranks=1, rank=0, expert_alignment=1
     h = ctypes.c_void_p()
     _check(_lib.ep_get_layout(
         _ptr(topk_idx), T, K, num_experts, num_ranks, rank, expert_alignment, _ptr(workspace), workspace.numel(),
-        _ptr(outputs.get("num_tokens_per_rank")), _ptr(outputs.get("num_tokens_per_expert")),
-        _ptr(outputs.get("is_token_in_rank")), _ptr(outputs.get("psum_num_recv_tokens_per_expert")),
-        _ptr(outputs.get("num_invalid_topk")), ctypes.byref(h), _stream(stream)), "ep_get_layout")
+        *_layout_ptrs(outputs), ctypes.byref(h), _stream(stream)), "ep_get_layout")
     return Handle(h, topk_idx, workspace, T, K, num_experts, num_ranks, rank, expert_alignment), outputs
 
 
@@ -235,15 +254,18 @@ def alloc_dispatch_outputs(handle: Handle, hidden: int, fp8: bool, want_meta=Tru
     return o
 
 
+_RECV_KEYS = ("recv_x", "recv_x_scales", "recv_src_idx", "recv_topk_weights", "recv_topk_idx")
+_SEND_KEYS = ("send_x", "send_x_scales", "send_src_idx", "send_topk_idx", "send_topk_weights")
+
+
 def _dispatch_struct(out):
-    def p(k):
+    s = _DispatchOut()   # zeroed: absent tensors stay NULL
+    for k in _RECV_KEYS + _SEND_KEYS:
         t = out.get(k)
-        return t.data_ptr() if t is not None else None
-    return _DispatchOut(recv_x=p("recv_x"), recv_x_scales=p("recv_x_scales"), recv_src_idx=p("recv_src_idx"),
-                        recv_topk_weights=p("recv_topk_weights"), recv_topk_idx=p("recv_topk_idx"),
-                        recv_capacity=out["recv_x"].shape[0], send_x=p("send_x"), send_x_scales=p("send_x_scales"),
-                        send_src_idx=p("send_src_idx"), send_topk_idx=p("send_topk_idx"),
-                        send_topk_weights=p("send_topk_weights"))
+        if t is not None:
+            setattr(s, k, t.data_ptr())
+    s.recv_capacity = out["recv_x"].shape[0]
+    return s
 
 
 def ep_dispatch(handle: Handle, x, topk_weights=None, fp8=True, do_expand=True, do_zero_padding=False, out=None,
