@@ -79,6 +79,8 @@ CASES = [
     (256, 8, 256, 8, 3, 128, 2048, True, True, "skew"),       # one hot expert
     (128, 8, 256, 1, 0, 128, 7168, True, False, "uniform"),   # decode shape without zero padding
     (300, 4, 32, 2, 0, 8, 256, False, True, "uniform"),       # two tiles: the two-launch path
+    (256, 32, 1024, 64, 5, 128, 256, True, True, "dup"),      # the largest K, E and ranks in one launch
+    (256, 32, 1024, 2, 1, 300, 64, False, True, "invalid"),   # 512 local experts, long padding list, invalid ids
 ]
 
 

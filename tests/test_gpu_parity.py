@@ -213,6 +213,8 @@ EDGE = [
     (65536, 8, 256, 1, 0, 128, 128, True, True, "uniform"),   # 256 layout tiles
     (5, 1, 1, 1, 0, 65536, 8, False, True, "uniform"),        # largest alignment: 65,531 zero-padded rows
     (300, 2, 2, 2, 1, 65536, 128, True, True, "uniform"),     # largest alignment, FP8, two ranks
+    (256, 32, 1024, 64, 5, 128, 256, True, True, "dup"),      # one full tile at the largest K, E and ranks
+    (256, 32, 1024, 1, 0, 7, 128, False, True, "invalid"),    # one full tile, 1024 local experts, invalid ids
 ]
 
 
