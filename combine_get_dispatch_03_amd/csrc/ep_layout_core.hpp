@@ -385,6 +385,7 @@ __device__ inline void tok_counts(const int64_t* __restrict__ idx, int T, int K,
                                   int lo, int t, const TokLds& L, Pre pre) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int nent = T * K;
+    const int tb = t < T ? t : 0;                    // tokens counted as before: none for a workgroup past T
     static_assert(kTile * kMaxTopk <= kEntriesPerThreadMax * kThreads, "one staging pass per tile");
     int64_t v[kEntriesPerThreadMax];
 #pragma unroll
@@ -411,7 +412,7 @@ __device__ inline void tok_counts(const int64_t* __restrict__ idx, int T, int K,
         const int e = j < nent ? st[u] : -1;
         if (e >= 0) {
             atomicAdd(&L.tot[e], 1);
-            if (j < t * K) atomicAdd(&L.bef[e], 1);
+            if (j < tb * K) atomicAdd(&L.bef[e], 1);
         }
         inv += popc64(ballot(e == kBad));
     }
@@ -426,7 +427,7 @@ __device__ inline void tok_counts(const int64_t* __restrict__ idx, int T, int K,
         for (uint64_t mm = m; mm != 0; mm &= mm - 1) {
             const int r = __builtin_ctzll(mm);
             atomicAdd(&L.tot[E + r], 1);
-            if (tid < t) atomicAdd(&L.rbef[r], 1);
+            if (tid < tb) atomicAdd(&L.rbef[r], 1);
         }
     }
     __syncthreads();
