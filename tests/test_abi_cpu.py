@@ -127,3 +127,47 @@ def test_dispatch_combine_reject_bad_handles(lib):
     assert lib.ep_handle_free(None) == 0
     assert lib.ep_combine_tokens(None, None, 128, 0, None, None, None) == 1
     assert b"handle" in lib.ep_last_error()
+
+
+_OUT_FIELDS = ("recv_x", "recv_x_scales", "recv_src_idx", "recv_topk_weights", "recv_topk_idx", "recv_capacity",
+               "send_x", "send_x_scales", "send_src_idx", "send_topk_idx", "send_topk_weights")
+
+
+def test_dispatch_out_struct_matches_header(tmp_path):
+    """The binding's ctypes mirror of ep_dispatch_out_t has the C struct's size and field offsets (gcc compiles a
+    probe against include/ep.h and prints them)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "probe.c"
+    body = "".join('    printf("%%s %%zu\\n", "%s", offsetof(ep_dispatch_out_t, %s));\n' % (f, f) for f in _OUT_FIELDS)
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "ep.h"\nint main(void) {\n'
+                   '    printf("sizeof %zu\\n", sizeof(ep_dispatch_out_t));\n' + body + '    return 0;\n}\n')
+    exe = tmp_path / "probe"
+    subprocess.run([cc, "-std=c11", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], check=True, capture_output=True,
+                                                       text=True).stdout.splitlines())
+    import combine_get_dispatch_03_amd as ep
+    D = ep._DispatchOut
+    assert [f[0] for f in D._fields_] == list(_OUT_FIELDS)
+    assert int(got["sizeof"]) == ctypes.sizeof(D)
+    for f in _OUT_FIELDS:
+        assert int(got[f]) == getattr(D, f).offset, f
+
+
+def test_dispatch_struct_from_tensors():
+    """The binding fills the struct from whichever output tensors are present, NULL for the rest, and takes
+    recv_capacity from recv_x's rows (host tensors stand in: only their addresses are read)."""
+    import torch
+    import combine_get_dispatch_03_amd as ep
+    out = dict(recv_x=torch.empty((37, 16), dtype=torch.uint8), recv_x_scales=torch.empty((37, 1)),
+               recv_src_idx=None, recv_topk_weights=torch.empty(37), send_x=torch.empty((2, 5, 16), dtype=torch.uint8))
+    s = ep._dispatch_struct(out)
+    assert s.recv_capacity == 37
+    for f in _OUT_FIELDS:
+        if f == "recv_capacity":
+            continue
+        t = out.get(f)
+        assert getattr(s, f) == (t.data_ptr() if t is not None else None), f
