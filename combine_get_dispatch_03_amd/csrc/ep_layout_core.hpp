@@ -1,7 +1,8 @@
 // ep_layout_core.hpp -- device-side pieces of the layout ([repo-map] §2.1; [DeepEP->MegaMoE] §2.2 and §2.4:
-// counts, their aligned prefix sum, stable rows), shared by the layout kernels (ep_layout.hip) and the
-// one-launch layout + dispatch kernel for small batches (ep_fused.hip).  The scheme is described in
-// ep_layout.hip.
+// counts, their aligned prefix sum, stable rows) that more than one kernel uses: the aligned scan of the local
+// experts, the global counts, the padding-row lookup, and the per-token counting of a one-tile batch, shared
+// by the layout kernels (ep_layout.hip) and the one-launch layout + dispatch kernel for small batches
+// (ep_fused.hip).  The multi-tile counting sort lives in ep_layout.hip, which describes the scheme.
 #pragma once
 
 #include "ep_device.hpp"
@@ -9,191 +10,15 @@
 
 namespace ep {
 
-extern __shared__ __align__(16) unsigned char layout_smem[];   // dynamic LDS of the counting phase
+extern __shared__ __align__(16) unsigned char layout_smem[];   // dynamic LDS of the layout kernels
 
 namespace {
 
 constexpr int kTile = kLayoutTileTokens;   // 256 tokens per tile
 constexpr int kThreads = 1024;             // every layout block: 16 waves
 constexpr int kWaves = kThreads / 64;
-constexpr int kPackShift = 11;             // packed entry: (rank << 11) | expert, or -1
-constexpr int kPackMask = (1 << kPackShift) - 1;
 constexpr int kBad = -2;                   // staged value of an entry < -1 or >= E
-constexpr int kMaxEntriesPerThread = kTile * kMaxTopk / kThreads;   // 8
-constexpr int kEntriesPerThreadMax = kMaxEntriesPerThread;
-// The token-mask work runs on the last 4 waves, so that for E <= 768 it overlaps the per-expert bases loop (which
-// runs on threads 0..E-1) instead of following it on the same threads.
-constexpr int kTokThread0 = kThreads - kTile;
-constexpr int kTokWave0 = kTokThread0 / 64;
-constexpr int kMaxCols = kMaxExperts + kMaxRanks + 1;               // columns of a tile row
-
-// ---- LDS of the counting phase ---------------------------------------------------------------------------
-struct CountLds {
-    uint16_t* cnt_w;   // [16][E]   per-wave counts, then per-wave exclusive bases within the tile
-    int32_t* ent;      // [256*K]   staged entries, then (wave-local rank << 11) | expert, or -1
-    int32_t* rcnt_w;   // [4][R]    per-wave token-in-rank counts, then exclusive bases (waves 0..3)
-    int32_t* inv_w;    // [16]      per-wave invalid entries
-    int32_t* row;      // [E+R+1]   tile totals: expert counts | token-in-rank counts | invalid
-};
-
-__host__ __device__ constexpr size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
-
-// Tokens ranked per wave in tile `tile`: the tile's tokens spread evenly over the 16 waves (16 for a full tile,
-// 8 for a 128-token batch, so that no wave runs two ranking rounds while others idle).  Wave w ranks tokens
-// [w * tpw, (w + 1) * tpw) of the tile; every reader of the per-wave bases uses the same split.
-__device__ __forceinline__ int tokens_per_wave(int T, int tile) {
-    const int ntok = max(0, min(kTile, T - tile * kTile));
-    return max(1, (ntok + kWaves - 1) / kWaves);
-}
-
-__host__ __device__ inline size_t count_lds_bytes(int E, int K, int R) {
-    return align16(sizeof(uint16_t) * kWaves * (size_t)E) +
-           sizeof(int32_t) * ((size_t)kTile * K + 4 * (size_t)R + kWaves + (size_t)(E + R + 1));
-}
-
-__device__ inline CountLds carve_count(unsigned char* base, int E, int K, int R) {
-    CountLds L;
-    L.cnt_w = reinterpret_cast<uint16_t*>(base);
-    L.ent = reinterpret_cast<int32_t*>(base + align16(sizeof(uint16_t) * kWaves * (size_t)E));
-    L.rcnt_w = L.ent + kTile * K;
-    L.inv_w = L.rcnt_w + 4 * R;
-    L.row = L.inv_w + kWaves;
-    return L;
-}
-
-// Counting phase for one tile.  Every thread of the block calls it; it ends with a barrier.  Returns, for the
-// token threads (the last 256 threads: token = tile start + tid - kTokThread0), the bit mask of ranks that the
-// token has an expert on (0 for the other threads).
-// `pre()` runs right after the tile's entry loads are issued and before they are used: a caller's loads that do
-// not depend on the layout go there, so that their latency overlaps the staging round trip and the rest of the
-// counting phase.
-struct NoPrefetch {
-    __device__ void operator()() const {}
-};
-
-template <class Pre = NoPrefetch>
-__device__ uint64_t count_tile(const int64_t* __restrict__ idx, int T, int K, int E, int R, int epr, int nbits,
-                               int tile, const CountLds& L, uint8_t* __restrict__ in_rank_out, Pre pre = Pre()) {
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    const int tok_tile0 = tile * kTile;
-    const int64_t ent_tile0 = (int64_t)tok_tile0 * K;
-    const int nent_tile = max(0, min(kTile, T - tok_tile0)) * K;
-
-    // stage the tile's entries: at most 256 * 32 = 8 per thread, all loads issued before any is used
-    static_assert(kTile * kMaxTopk <= kEntriesPerThreadMax * kThreads, "one staging pass per tile");
-    int64_t v[kEntriesPerThreadMax];
-#pragma unroll
-    for (int u = 0; u < kEntriesPerThreadMax; ++u) {
-        const int j = u * kThreads + tid;
-        v[u] = j < nent_tile ? idx[ent_tile0 + j] : -1;
-    }
-    pre();
-#pragma unroll
-    for (int u = 0; u < kEntriesPerThreadMax; ++u) {
-        const int j = u * kThreads + tid;
-        if (j < nent_tile) L.ent[j] = (v[u] >= 0 && v[u] < E) ? (int)v[u] : (v[u] == -1 ? -1 : kBad);
-    }
-    for (int i = tid; i < kWaves * E; i += kThreads) L.cnt_w[i] = 0;
-    __syncthreads();
-
-    // each wave ranks its 16 tokens' entries in flat order
-    const int tpw = tokens_per_wave(T, tile);
-    const int nent_w = max(0, min(tpw, T - (tok_tile0 + w * tpw))) * K;
-    int32_t* went = L.ent + w * tpw * K;
-    const uint64_t lt = lanemask_lt();
-    uint16_t* cnt = L.cnt_w + w * E;
-    int inv = 0;
-    for (int j0 = 0; j0 < nent_w; j0 += 64) {
-        const int j = j0 + lane;
-        const int e = j < nent_w ? went[j] : -1;
-        const bool ok = e >= 0;
-        inv += popc64(ballot(e == kBad));
-        const int key = ok ? e : 0;
-        const uint64_t peers = match_peers(key, ok, nbits);
-        const int base = ok ? cnt[key] : 0;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        if (ok && (peers & lt) == 0) cnt[key] = (uint16_t)(base + popc64(peers));
-        if (j < nent_w) went[j] = ok ? (((base + popc64(peers & lt)) << kPackShift) | key) : -1;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-    }
-    if (lane == 0) L.inv_w[w] = inv;
-    __syncthreads();
-
-    // per-wave counts -> per-wave exclusive bases; tile totals
-    for (int e = tid; e < E; e += kThreads) {
-        int c[kWaves];
-#pragma unroll
-        for (int v = 0; v < kWaves; ++v) c[v] = L.cnt_w[v * E + e];
-        int run = 0;
-#pragma unroll
-        for (int v = 0; v < kWaves; ++v) {
-            L.cnt_w[v * E + e] = (uint16_t)run;
-            run += c[v];
-        }
-        L.row[e] = run;
-    }
-    // token threads (waves kTokWave0..kTokWave0+3) <-> tokens of the tile: token-in-rank membership
-    const int tt = tid - kTokThread0;
-    const int t = tok_tile0 + tt;
-    const bool tv = tt >= 0 && t < T;
-    // expert -> owning rank as floor((e + 0.5) / epr) in fp32: exact here, since for e < 1024 and epr <= 1024 the
-    // quotient lies at least 0.5 / epr >= 2^-11 from an integer and the two roundings move it by < 2^-13
-    const float inv_epr = 1.0f / (float)epr;
-    uint64_t mask = 0ull;
-    if (tv) {
-        for (int k = 0; k < K; ++k) {
-            const int p = L.ent[tt * K + k];
-            if (p >= 0) mask |= 1ull << (int)(((float)(p & kPackMask) + 0.5f) * inv_epr);
-        }
-    }
-    if (tv && in_rank_out != nullptr)
-        for (int r = 0; r < R; ++r) in_rank_out[(int64_t)t * R + r] = (uint8_t)((mask >> r) & 1ull);
-    if (w >= kTokWave0) {
-        for (int r = 0; r < R; ++r) {
-            const uint64_t b = ballot((mask >> r) & 1ull);
-            if (lane == 0) L.rcnt_w[(w - kTokWave0) * R + r] = popc64(b);
-        }
-    }
-    __syncthreads();
-    if (tid < R) {
-        const int c0 = L.rcnt_w[tid], c1 = L.rcnt_w[R + tid], c2 = L.rcnt_w[2 * R + tid], c3 = L.rcnt_w[3 * R + tid];
-        L.rcnt_w[tid] = 0;
-        L.rcnt_w[R + tid] = c0;
-        L.rcnt_w[2 * R + tid] = c0 + c1;
-        L.rcnt_w[3 * R + tid] = c0 + c1 + c2;
-        L.row[E + tid] = c0 + c1 + c2 + c3;
-    }
-    if (tid == 0) {
-        int s = 0;
-        for (int v = 0; v < kWaves; ++v) s += L.inv_w[v];
-        L.row[E + R] = s;
-    }
-    __syncthreads();
-    return mask;
-}
-
-// Per-rank token rows of the tile's tokens, from the rank masks of count_tile: the rank of the token among the
-// tile's earlier tokens with an expert on r (tile-local), or -1 when it has none there; handed to
-// put(t, r, row).  The token threads of count_tile (one token each) take part.
-template <class Put>
-__device__ __forceinline__ void token_rows(const CountLds& L, uint64_t mask, int T, int R, int tile, Put put) {
-    const int tid = threadIdx.x, w = tid >> 6;
-    if (w < kTokWave0) return;
-    const int t = tile * kTile + tid - kTokThread0;
-    const bool tv = t < T;
-    const uint64_t lt = lanemask_lt();
-    for (int r = 0; r < R; ++r) {
-        const bool bit = (mask >> r) & 1ull;
-        const uint64_t b = ballot(bit);
-        if (tv) put(t, r, bit ? L.rcnt_w[(w - kTokWave0) * R + r] + popc64(b & lt) : -1);
-    }
-}
-
-__device__ inline void send_rows(const CountLds& L, uint64_t mask, int T, int R, int tile, int32_t* __restrict__ out) {
-    token_rows(L, mask, T, R, tile, [&](int t, int r, int v) { out[(int64_t)t * R + r] = v; });
-}
+constexpr int kMaxEntriesPerThread = kTile * kMaxTopk / kThreads;   // 8: one staging pass covers a tile
 
 // Block-wide exclusive scan of two ints per thread at once (kThreads threads).  Returns the exclusive
 // prefixes in ex0/ex1 and the block totals in all0/all1.  `scratch` holds 2 * kWaves ints.
@@ -304,29 +129,6 @@ __device__ void write_counts(int E, int R, int lo, int epr, const int* total, co
     }
 }
 
-// Finalizing phase shared by both layout paths.  `total` holds the column totals over all tiles (experts |
-// ranks | invalid).  Computes psum / padpre (LDS), block 0 writes the global outputs, and each of the nblk
-// layout blocks writes its share (experts blockIdx.x + i * nblk) of the dense padding-row list.
-__device__ inline void finalize_core(int E, int R, int rank, int epr, int A, const int* total, int* psum, int* padpre,
-                              int* scratch, const Outputs& o, int nblk) {
-    const int tid = threadIdx.x;
-    const int lo = rank * epr;
-    local_scan(epr, lo, A, total, psum, padpre, scratch);
-    if (blockIdx.x == 0) write_counts(E, R, lo, epr, total, psum, padpre, o);
-    if (o.pad_rows != nullptr) {
-        // this block's share: local experts blockIdx.x + i * nblk, one expert per wave, lanes over its rows
-        const int nexp = (epr - (int)blockIdx.x + nblk - 1) / nblk;
-        const int w = tid >> 6, lane = tid & 63;
-        for (int i = w; i < nexp; i += kWaves) {
-            const int j = blockIdx.x + i * nblk;
-            const int first = psum[j] + total[lo + j];
-            const int n = psum[j + 1] - first;
-            int32_t* dst = o.pad_rows + padpre[j];
-            for (int r = lane; r < n; r += 64) dst[r] = first + r;
-        }
-    }
-}
-
 // Padding row number q (0 <= q < padpre[epr]) -> its row: the expert j with padpre[j] <= q < padpre[j+1] (binary
 // search in LDS), whose padding rows are the last padpre[j+1] - padpre[j] rows before psum[j+1].  The same
 // order as the dense padding-row list.
@@ -386,10 +188,10 @@ __device__ inline void tok_counts(const int64_t* __restrict__ idx, int T, int K,
     const int tid = threadIdx.x, lane = tid & 63;
     const int nent = T * K;
     const int tb = t < T ? t : 0;                    // tokens counted as before: none for a workgroup past T
-    static_assert(kTile * kMaxTopk <= kEntriesPerThreadMax * kThreads, "one staging pass per tile");
-    int64_t v[kEntriesPerThreadMax];
+    static_assert(kTile * kMaxTopk <= kMaxEntriesPerThread * kThreads, "one staging pass per tile");
+    int64_t v[kMaxEntriesPerThread];
 #pragma unroll
-    for (int u = 0; u < kEntriesPerThreadMax; ++u) {
+    for (int u = 0; u < kMaxEntriesPerThread; ++u) {
         const int j = u * kThreads + tid;
         v[u] = j < nent ? idx[j] : -1;
     }
@@ -397,9 +199,9 @@ __device__ inline void tok_counts(const int64_t* __restrict__ idx, int T, int K,
     for (int i = tid; i < E + R + 1; i += kThreads) L.tot[i] = 0;
     for (int i = tid; i < E; i += kThreads) L.bef[i] = 0;
     if (tid < R) L.rbef[tid] = 0;
-    int st[kEntriesPerThreadMax];
+    int st[kMaxEntriesPerThread];
 #pragma unroll
-    for (int u = 0; u < kEntriesPerThreadMax; ++u) {
+    for (int u = 0; u < kMaxEntriesPerThread; ++u) {
         const int j = u * kThreads + tid;
         st[u] = (v[u] >= 0 && v[u] < E) ? (int)v[u] : (v[u] == -1 ? -1 : kBad);
         if (j < nent) L.ent[j] = st[u];
@@ -407,7 +209,7 @@ __device__ inline void tok_counts(const int64_t* __restrict__ idx, int T, int K,
     __syncthreads();
     int inv = 0;
 #pragma unroll
-    for (int u = 0; u < kEntriesPerThreadMax; ++u) {
+    for (int u = 0; u < kMaxEntriesPerThread; ++u) {
         const int j = u * kThreads + tid;
         const int e = j < nent ? st[u] : -1;
         if (e >= 0) {
