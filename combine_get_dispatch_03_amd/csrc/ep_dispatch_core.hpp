@@ -41,7 +41,7 @@ struct Params {
     int row_bytes;    // bytes of one destination row
     int G;            // fp32 scales per row (FP8: H / 128; raw: as given, 0 for none)
     int nstep;        // segments per row
-    int64_t ntok_items;   // T * nstep
+    int64_t ntok_items;   // token work items: T x items per token (set by the dispatch launcher)
     int pad_sub;      // padding items per padding row (nstep with zero padding, 1 for metadata only, 0 none)
     int zero_pad;
     int64_t nwaves;   // waves in the grid
@@ -275,7 +275,7 @@ inline Params dispatch_params(const Handle& h, const DispatchArgs& a) {
         p.nstep = (p.row_bytes / 16 + kRawChunks - 1) / kRawChunks;
     }
     if (p.G == 0) p.recv_scales = nullptr;
-    p.ntok_items = (int64_t)h.T * p.nstep;
+    p.ntok_items = 0;
     const bool meta = p.recv_src != nullptr || p.recv_w != nullptr;
     p.pad_sub = (h.A > 1 && !token_major) ? (a.zero_pad ? p.nstep : (meta ? 1 : 0)) : 0;
     p.nwaves = 0;
