@@ -376,12 +376,7 @@ def ep_dispatch_rows(handle: Handle, rows, scales=None, topk_weights=None, do_ze
                    recv_x_scales=torch.empty((cap, G), dtype=torch.float32, device=dev) if G else None,
                    recv_src_idx=torch.empty(cap, dtype=torch.int32, device=dev),
                    recv_topk_weights=torch.empty(cap, dtype=torch.float32, device=dev))
-    s = _DispatchOut(
-        recv_x=out["recv_x"].data_ptr(),
-        recv_x_scales=out["recv_x_scales"].data_ptr() if out.get("recv_x_scales") is not None else None,
-        recv_src_idx=out["recv_src_idx"].data_ptr() if out.get("recv_src_idx") is not None else None,
-        recv_topk_weights=out["recv_topk_weights"].data_ptr() if out.get("recv_topk_weights") is not None else None,
-        recv_capacity=out["recv_x"].shape[0])
+    s = _dispatch_struct(out)   # the library reads the recv fields only
     _check(_lib.ep_dispatch_rows(handle.ptr, _ptr(rows), row_bytes, _ptr(scales), G, _ptr(topk_weights),
                                  int(bool(do_zero_padding)), ctypes.byref(s), _stream(stream)), "ep_dispatch_rows")
     return out
