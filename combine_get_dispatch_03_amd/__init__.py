@@ -114,6 +114,17 @@ def _stream(stream):
     return torch.cuda.current_stream().cuda_stream
 
 
+def _on_stream(stream, fn, *args, **kw):
+    """Run an allocating helper with `stream` current, so that the tensors it makes belong to the stream the
+    call's kernels write them on: torch's caching allocator hands a freed block to later work of the block's
+    own stream only, which then is ordered after those kernels.  stream=None: torch's current stream, where
+    the kernels run anyway."""
+    if stream is None:
+        return fn(*args, **kw)
+    with torch.cuda.stream(stream):
+        return fn(*args, **kw)
+
+
 def _need(t, dtype, name, device=None, shape=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
@@ -212,7 +223,8 @@ def ep_get_layout(topk_idx, num_experts, num_ranks=1, rank=0, expert_alignment=1
     """Layout of `topk_idx` (int64 [T, K] on the GPU).  Returns (Handle, dict) with the device outputs
     num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank, psum_num_recv_tokens_per_expert and
     num_invalid_topk.  `outputs` may supply any of those tensors (or None entries to skip them)."""
-    T, K, workspace, outputs = _layout_prep(topk_idx, num_experts, num_ranks, expert_alignment, workspace, outputs)
+    T, K, workspace, outputs = _on_stream(stream, _layout_prep, topk_idx, num_experts, num_ranks, expert_alignment,
+                                          workspace, outputs)
     h = ctypes.c_void_p()
     _check(_lib.ep_get_layout(
         _ptr(topk_idx), T, K, num_experts, num_ranks, rank, expert_alignment, _ptr(workspace), workspace.numel(),
@@ -279,8 +291,8 @@ def ep_dispatch(handle: Handle, x, topk_weights=None, fp8=True, do_expand=True, 
     if topk_weights is not None:
         _need(topk_weights, torch.float32, "topk_weights", shape=(handle.num_tokens, handle.num_topk))
     if out is None:
-        out = alloc_dispatch_outputs(handle, H, fp8, want_meta, want_send_meta, device=x.device,
-                                     do_expand=do_expand)
+        out = _on_stream(stream, alloc_dispatch_outputs, handle, H, fp8, want_meta, want_send_meta,
+                         device=x.device, do_expand=do_expand)
     cap = out["recv_x"].shape[0]
     s = _dispatch_struct(out)
     _check(_lib.ep_dispatch(handle.ptr, _ptr(x), H, _ptr(topk_weights),
@@ -294,7 +306,8 @@ def ep_layout_dispatch(topk_idx, x, num_experts, num_ranks=1, rank=0, expert_ali
                        want_meta=True, want_send_meta=True, stream=None):
     """ep_get_layout + ep_dispatch in one call (one kernel launch for <= 256 tokens).  Returns (Handle, layout
     outputs dict, dispatch outputs dict), the same as the two calls would."""
-    T, K, workspace, outputs = _layout_prep(topk_idx, num_experts, num_ranks, expert_alignment, workspace, outputs)
+    T, K, workspace, outputs = _on_stream(stream, _layout_prep, topk_idx, num_experts, num_ranks, expert_alignment,
+                                          workspace, outputs)
     _need(x, torch.bfloat16, "x")
     if x.dim() != 2 or x.shape[0] != T:
         raise ValueError("x must be [num_tokens, hidden]")
@@ -303,7 +316,8 @@ def ep_layout_dispatch(topk_idx, x, num_experts, num_ranks=1, rank=0, expert_ali
         _need(topk_weights, torch.float32, "topk_weights", shape=(T, K))
     if out is None:
         tmp = Handle(None, topk_idx, workspace, T, K, num_experts, num_ranks, rank, expert_alignment)
-        out = alloc_dispatch_outputs(tmp, H, fp8, want_meta, want_send_meta, device=x.device, do_expand=do_expand)
+        out = _on_stream(stream, alloc_dispatch_outputs, tmp, H, fp8, want_meta, want_send_meta, device=x.device,
+                         do_expand=do_expand)
     s = _dispatch_struct(out)
     h = ctypes.c_void_p()
     _check(_lib.ep_layout_dispatch(
@@ -326,7 +340,7 @@ def ep_combine(handle: Handle, y, topk_weights=None, bias=None, out=None, stream
     if bias is not None:
         _need(bias, torch.bfloat16, "bias", shape=(T, H))
     if out is None:
-        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+        out = _on_stream(stream, torch.empty, (T, H), dtype=torch.bfloat16, device=y.device)
     else:
         _need(out, torch.bfloat16, "out", shape=(T, H))
     _check(_lib.ep_combine(handle.ptr, _ptr(y), H, y.shape[0], _ptr(topk_weights), _ptr(bias), _ptr(out),
@@ -345,7 +359,7 @@ def ep_combine_tokens(handle: Handle, y, bias=None, out=None, stream=None):
     if bias is not None:
         _need(bias, torch.bfloat16, "bias", shape=(T, H))
     if out is None:
-        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+        out = _on_stream(stream, torch.empty, (T, H), dtype=torch.bfloat16, device=y.device)
     else:
         _need(out, torch.bfloat16, "out", shape=(T, H))
     _check(_lib.ep_combine_tokens(handle.ptr, _ptr(y), H, y.shape[0], _ptr(bias), _ptr(out), _stream(stream)),
@@ -372,10 +386,11 @@ def ep_dispatch_rows(handle: Handle, rows, scales=None, topk_weights=None, do_ze
     cap = handle.recv_capacity
     if out is None:
         dev = rows.device
-        out = dict(recv_x=torch.empty((cap, rows.shape[1]), dtype=rows.dtype, device=dev),
-                   recv_x_scales=torch.empty((cap, G), dtype=torch.float32, device=dev) if G else None,
-                   recv_src_idx=torch.empty(cap, dtype=torch.int32, device=dev),
-                   recv_topk_weights=torch.empty(cap, dtype=torch.float32, device=dev))
+        out = _on_stream(stream, lambda: dict(
+            recv_x=torch.empty((cap, rows.shape[1]), dtype=rows.dtype, device=dev),
+            recv_x_scales=torch.empty((cap, G), dtype=torch.float32, device=dev) if G else None,
+            recv_src_idx=torch.empty(cap, dtype=torch.int32, device=dev),
+            recv_topk_weights=torch.empty(cap, dtype=torch.float32, device=dev)))
     s = _dispatch_struct(out)   # the library reads the recv fields only
     _check(_lib.ep_dispatch_rows(handle.ptr, _ptr(rows), row_bytes, _ptr(scales), G, _ptr(topk_weights),
                                  int(bool(do_zero_padding)), ctypes.byref(s), _stream(stream)), "ep_dispatch_rows")
@@ -395,7 +410,7 @@ def ep_combine_reduce(handle: Handle, partials=None, local=None, bias=None, out=
     if bias is not None:
         _need(bias, torch.bfloat16, "bias", shape=(T, H))
     if out is None:
-        out = torch.empty((T, H), dtype=torch.bfloat16, device=ref.device)
+        out = _on_stream(stream, torch.empty, (T, H), dtype=torch.bfloat16, device=ref.device)
     else:
         _need(out, torch.bfloat16, "out", shape=(T, H))
     _check(_lib.ep_combine_reduce(handle.ptr, _ptr(partials), H, _ptr(local), _ptr(bias), _ptr(out),

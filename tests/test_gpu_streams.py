@@ -100,3 +100,51 @@ def test_calls_follow_stream(ep, name, two_calls, how):
     torch.cuda.synchronize()
     _assert_same(ref, got)
     h.free()
+
+
+def test_threads_call_concurrently(ep):
+    """Two host threads run the path at the same time, each on its own stream with its own inputs and buffers
+    (the binding releases the GIL inside every library call, so the calls overlap in the library).  Each
+    thread's outputs equal those of the same calls made alone: the library keeps no shared per-call state."""
+    import threading
+    cases = []
+    for name, seed in (("decode", 3), ("prefill", 4)):
+        inp = W.make_inputs(name, seed=seed)
+        c = inp["cfg"]
+        cap = ep.ep_recv_capacity(c.num_tokens, c.num_topk, c.num_experts // c.num_ranks, c.expert_alignment)
+        cases.append(dict(c=c, idx=inp["topk_idx"].to(DEV), w=inp["topk_weights"].to(DEV), x=inp["x"].to(DEV),
+                          y=W.random_expert_outputs(cap, c.hidden, seed=seed, device=DEV), cap=cap))
+    refs = []
+    for k in cases:
+        b = _buffers(ep, k["c"], k["cap"])
+        _reset(b)
+        _path(ep, k["c"], k["idx"], k["x"], k["w"], k["y"], b, False, None).free()
+        torch.cuda.synchronize()
+        refs.append(b)
+
+    errors = []
+    def worker(i, k):
+        # Everything a thread allocates, writes and compares stays on its own stream.  (Buffers taken from the
+        # default stream's pool, which both threads share, and written on a side stream could be handed out while
+        # the other thread's default-stream work on them is still queued: torch's caching allocator orders a
+        # freed block only after the work of its own stream.)
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for rep in range(20):
+                    b = _buffers(ep, k["c"], k["cap"])
+                    _reset(b)
+                    _path(ep, k["c"], k["idx"], k["x"], k["w"], k["y"], b, rep % 2 == 1, None).free()
+                    s.synchronize()
+                    _assert_same(refs[i], b)
+                    s.synchronize()
+        except Exception as exc:   # reported by the main thread
+            errors.append((i, repr(exc)))
+
+    threads = [threading.Thread(target=worker, args=(i, k)) for i, k in enumerate(cases)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
