@@ -245,10 +245,12 @@ def measure_copy_ceiling(dev, n, mib=1024):
 
 def measure_workloads(ep, W, dev, names, n):
     """The other workloads at a glance, measured like the headline one: per call, HIP events around n back-to-back
-    launches; the step (one-call layout + dispatch, then combine), n eager steps between device syncs, host
-    clock; algorithmic bytes from the byte model with the device counts.  Parity for each is in the test suite."""
+    launches; the step (one-call layout + dispatch, then combine), the median of five blocks of n eager steps
+    between device syncs, host clock; algorithmic bytes from the byte model with the device counts.  Parity for
+    each is in the test suite."""
     import time
 
+    import numpy as np
     import torch
 
     out = {}
@@ -294,11 +296,16 @@ def measure_workloads(ep, W, dev, names, n):
         for _ in range(3):
             step()
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(n):
-            step()
-        torch.cuda.synchronize()
-        step_us = (time.perf_counter() - t0) * 1e6 / n
+        # five blocks of n steps between device syncs, host clock; the median block, so that one stall of the
+        # host (these steps are short, and for tiny and decode bound by the host's enqueue) does not set it
+        blocks = []
+        for _ in range(5):
+            t0 = time.perf_counter()
+            for _ in range(n):
+                step()
+            torch.cuda.synchronize()
+            blocks.append((time.perf_counter() - t0) * 1e6 / n)
+        step_us = float(np.median(blocks))
         cnt = lay["num_tokens_per_expert"].cpu().numpy()
         psum = lay["psum_num_recv_tokens_per_expert"].cpu().numpy()
         ntr = lay["num_tokens_per_rank"].cpu().numpy()
@@ -594,8 +601,9 @@ def main():
     workloads = measure_workloads(ep, W, dev, others, 20) if others else None
     if workloads:
         workloads["note"] = ("per call: events around back-to-back launches; step: eager one-call layout + dispatch "
-                             "then combine, host clock -- for tiny and decode that is bounded by the host's enqueue "
-                             "of the calls, see decode.step_graph_* for the GPU-side decode step")
+                             "then combine, host clock, the median of five blocks of 20 steps -- for tiny and decode "
+                             "that is bounded by the host's enqueue of the calls, see decode.step_graph_* for the "
+                             "GPU-side decode step")
 
     cpu = None
     if not args.no_cpu_baseline:
