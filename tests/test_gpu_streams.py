@@ -148,3 +148,37 @@ def test_threads_call_concurrently(ep):
         t.join()
     torch.cuda.synchronize()
     assert not errors, errors
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill"])
+def test_binding_allocates_on_given_stream(ep, name):
+    """With stream= given and no output tensors, the binding allocates the outputs and workspace itself (with
+    the given stream current) while torch's current stream stays the default one; the results on that stream
+    equal the default-stream calls bit for bit (rows a call leaves unwritten are compared through the layout
+    only: the allocated buffers start uninitialised)."""
+    inp = W.make_inputs(name)
+    c = inp["cfg"]
+    idx, w, x = inp["topk_idx"].to(DEV), inp["topk_weights"].to(DEV), inp["x"].to(DEV)
+    cap = ep.ep_recv_capacity(c.num_tokens, c.num_topk, c.num_experts // c.num_ranks, c.expert_alignment)
+    y = W.random_expert_outputs(cap, c.hidden, seed=9, device=DEV)
+    h0, lay0, out0 = ep.ep_layout_dispatch(idx, x, c.num_experts, c.num_ranks, c.rank, c.expert_alignment, w,
+                                           fp8=c.fp8, do_zero_padding=c.zero_padding)
+    res0 = ep.ep_combine(h0, y, w)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    for _ in range(3):
+        h1, lay1, out1 = ep.ep_layout_dispatch(idx, x, c.num_experts, c.num_ranks, c.rank, c.expert_alignment, w,
+                                               fp8=c.fp8, do_zero_padding=c.zero_padding, stream=s)
+        res1 = ep.ep_combine(h1, y, w, stream=s)
+        s.synchronize()
+        for k, t in lay0.items():
+            assert torch.equal(t, lay1[k]), k
+        assert torch.equal(res0.view(torch.int16), res1.view(torch.int16))
+        # the written rows: every valid row (recv_src_idx >= 0) and, with zero padding, every row up to psum[-1]
+        rows = int(lay0["psum_num_recv_tokens_per_expert"][-1])
+        src0, src1 = out0["recv_src_idx"][:rows], out1["recv_src_idx"][:rows]
+        assert torch.equal(src0, src1)
+        keep = src0 >= 0 if not c.zero_padding else torch.ones_like(src0, dtype=torch.bool)
+        assert torch.equal(out0["recv_x"][:rows][keep], out1["recv_x"][:rows][keep])
+        h1.free()
+    h0.free()
