@@ -409,7 +409,7 @@ def measure_decode(ep, W, dev, n):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
+        print("bench.py measures one GPU only: this library has no multi-GPU path (--gpus %d requested)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 
