@@ -222,7 +222,7 @@ def measure_epilogues(ep, W, dev, n):
 
 def measure_copy_ceiling(dev, n, mib=1024):
     """A plain device-to-device copy of `mib` MiB (torch's copy_, the runtime's copy kernel), timed with events
-    over n back-to-back copies: the streaming rate this machine reaches on a flat read + flat write, as context for
+    over n back-to-back copies: the streaming rate this GPU reaches on a flat read + flat write, as context for
     the kernels' rates (not the roofline's denominator, which is the published 8 TB/s)."""
     import torch
 
