@@ -126,17 +126,103 @@ def _on_stream(stream, fn, *args, **kw):
 
 
 def _need(t, dtype, name, device=None, shape=None):
+    """t must be a contiguous tensor of `dtype` and `shape` (when given) on `device` (when given; else on a GPU).
+    The shape is checked before the placement, so the shape rules can be exercised without a GPU."""
+    # one expression for the common (valid) case; the checks below only name what is wrong
+    if (type(t) is torch.Tensor and t.dtype is dtype and (shape is None or t.shape == shape)
+            and (t.device == device if device is not None else t.is_cuda) and t.is_contiguous()):
+        return t
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
     if t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
-    if not t.is_cuda:
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if device is not None:
+        if t.device != device:
+            raise ValueError("%s must be on %s, got %s" % (name, device, t.device))
+    elif not t.is_cuda:
         raise ValueError("%s must be a device tensor" % name)
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
-    if shape is not None and tuple(t.shape) != tuple(shape):
-        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
     return t
+
+
+def _opt(out, key, dtype, shape, device):
+    """An optional output: absent/None, or exactly dtype/shape on device."""
+    t = out.get(key)
+    if t is not None:
+        _need(t, dtype, key, device, shape)
+
+
+def check_layout_outputs(outputs, T, E, R, device):
+    """Caller-supplied layout outputs (any entry may be None): the sizes the library writes."""
+    El = E // R
+    _opt(outputs, "num_tokens_per_rank", torch.int32, (R,), device)
+    _opt(outputs, "num_tokens_per_expert", torch.int32, (E,), device)
+    _opt(outputs, "is_token_in_rank", torch.uint8, (T, R), device)
+    _opt(outputs, "psum_num_recv_tokens_per_expert", torch.int32, (El + 1,), device)
+    _opt(outputs, "num_invalid_topk", torch.int32, (1,), device)
+
+
+def check_workspace(workspace, device):
+    """A caller's workspace: one contiguous uint8 buffer on the device (its length is checked by the library)."""
+    _need(workspace, torch.uint8, "workspace", device)
+    if workspace.dim() != 1:
+        raise ValueError("workspace must be a 1-D uint8 tensor")
+
+
+def check_dispatch_outputs(out, T, K, R, hidden, fp8, do_expand, device):
+    """Every dispatch output the library will write, against the sizes it writes: recv_x [cap, hidden] (e4m3
+    bytes or bf16) with every other recv array on the same cap rows, the send windows [R, T, ...].  Returns cap
+    (the recv_capacity passed to the library, which checks it against the layout's bound)."""
+    if not isinstance(out, dict) or out.get("recv_x") is None:
+        raise ValueError("out must be a dict holding recv_x")
+    rx = out["recv_x"]
+    xdt = torch.uint8 if fp8 else torch.bfloat16
+    if not isinstance(rx, torch.Tensor) or rx.dim() != 2:
+        raise ValueError("recv_x must be a 2-D tensor [rows, hidden]")
+    cap = rx.shape[0]
+    _need(rx, xdt, "recv_x", device, (cap, hidden))
+    if fp8:
+        if out.get("recv_x_scales") is None:
+            raise ValueError("FP8 dispatch needs recv_x_scales")
+        _need(out["recv_x_scales"], torch.float32, "recv_x_scales", device, (cap, hidden // 128))
+    _opt(out, "recv_src_idx", torch.int32, (cap,), device)
+    _opt(out, "recv_topk_weights", torch.float32, (cap,) if do_expand else (T, K), device)
+    if not do_expand:
+        _opt(out, "recv_topk_idx", torch.int64, (T, K), device)
+    if R > 1:
+        if out.get("send_x") is None:
+            raise ValueError("num_ranks > 1 needs send_x")
+        _need(out["send_x"], xdt, "send_x", device, (R, T, hidden))
+        if fp8:
+            if out.get("send_x_scales") is None:
+                raise ValueError("num_ranks > 1 with FP8 needs send_x_scales")
+            _need(out["send_x_scales"], torch.float32, "send_x_scales", device, (R, T, hidden // 128))
+        _opt(out, "send_src_idx", torch.int32, (R, T), device)
+        _opt(out, "send_topk_idx", torch.int64, (R, T, K), device)
+        _opt(out, "send_topk_weights", torch.float32, (R, T, K), device)
+    return cap
+
+
+def check_rows_outputs(out, row_dtype, row_elems, G, device):
+    """Outputs of ep_dispatch_rows: recv_x [cap, row_elems] of the rows' dtype, scales [cap, G] when G > 0, and
+    the optional per-row metadata on the same cap rows.  Returns cap."""
+    if not isinstance(out, dict) or out.get("recv_x") is None:
+        raise ValueError("out must be a dict holding recv_x")
+    rx = out["recv_x"]
+    if not isinstance(rx, torch.Tensor) or rx.dim() != 2:
+        raise ValueError("recv_x must be a 2-D tensor [rows, row_elements]")
+    cap = rx.shape[0]
+    _need(rx, row_dtype, "recv_x", device, (cap, row_elems))
+    if G > 0:
+        if out.get("recv_x_scales") is None:
+            raise ValueError("rows with scales need recv_x_scales")
+        _need(out["recv_x_scales"], torch.float32, "recv_x_scales", device, (cap, G))
+    _opt(out, "recv_src_idx", torch.int32, (cap,), device)
+    _opt(out, "recv_topk_weights", torch.float32, (cap,), device)
+    return cap
 
 
 def ep_recv_capacity(num_tokens, num_topk, num_local_experts, expert_alignment) -> int:
@@ -192,14 +278,20 @@ def _layout_prep(topk_idx, num_experts, num_ranks, expert_alignment, workspace, 
         raise ValueError("topk_idx must be [num_tokens, num_topk]")
     T, K = topk_idx.shape
     dev = topk_idx.device
-    if workspace is None:   # a caller's workspace is checked (sizes and length) by the library call itself
+    if num_ranks < 1 or num_experts < 1 or num_experts % num_ranks != 0:
+        raise ValueError("num_experts must be a positive multiple of num_ranks")
+    if workspace is not None:   # its length is checked by the library call itself
+        check_workspace(workspace, dev)
+    else:
         nbytes = ep_layout_workspace_bytes(T, K, num_experts, num_ranks, expert_alignment)
         if nbytes == 0:
             raise EPError("ep_layout_workspace_bytes rejected the sizes (T=%d K=%d E=%d R=%d A=%d)"
                           % (T, K, num_experts, num_ranks, expert_alignment))
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    El = num_experts // max(num_ranks, 1)
-    if outputs is None:
+    El = num_experts // num_ranks
+    if outputs is not None:
+        check_layout_outputs(outputs, T, num_experts, num_ranks, dev)
+    else:
         outputs = dict(
             num_tokens_per_rank=torch.empty(num_ranks, dtype=torch.int32, device=dev),
             num_tokens_per_expert=torch.empty(num_experts, dtype=torch.int32, device=dev),
@@ -270,13 +362,13 @@ _RECV_KEYS = ("recv_x", "recv_x_scales", "recv_src_idx", "recv_topk_weights", "r
 _SEND_KEYS = ("send_x", "send_x_scales", "send_src_idx", "send_topk_idx", "send_topk_weights")
 
 
-def _dispatch_struct(out):
+def _dispatch_struct(out, cap, keys=_RECV_KEYS + _SEND_KEYS):
     s = _DispatchOut()   # zeroed: absent tensors stay NULL
-    for k in _RECV_KEYS + _SEND_KEYS:
+    for k in keys:
         t = out.get(k)
         if t is not None:
             setattr(s, k, t.data_ptr())
-    s.recv_capacity = out["recv_x"].shape[0]
+    s.recv_capacity = cap
     return s
 
 
@@ -288,13 +380,17 @@ def ep_dispatch(handle: Handle, x, topk_weights=None, fp8=True, do_expand=True, 
     if x.dim() != 2 or x.shape[0] != handle.num_tokens:
         raise ValueError("x must be [num_tokens, hidden]")
     H = x.shape[1]
+    dev = x.device
     if topk_weights is not None:
-        _need(topk_weights, torch.float32, "topk_weights", shape=(handle.num_tokens, handle.num_topk))
+        _need(topk_weights, torch.float32, "topk_weights", dev, (handle.num_tokens, handle.num_topk))
     if out is None:
         out = _on_stream(stream, alloc_dispatch_outputs, handle, H, fp8, want_meta, want_send_meta,
-                         device=x.device, do_expand=do_expand)
-    cap = out["recv_x"].shape[0]
-    s = _dispatch_struct(out)
+                         device=dev, do_expand=do_expand)
+        cap = out["recv_x"].shape[0]
+    else:
+        cap = check_dispatch_outputs(out, handle.num_tokens, handle.num_topk, handle.num_ranks, H, fp8,
+                                     do_expand, dev)
+    s = _dispatch_struct(out, cap)
     _check(_lib.ep_dispatch(handle.ptr, _ptr(x), H, _ptr(topk_weights),
                             EP_DTYPE_FP8_E4M3 if fp8 else EP_DTYPE_BF16, int(bool(do_expand)),
                             int(bool(do_zero_padding)), ctypes.byref(s), _stream(stream)), "ep_dispatch")
@@ -308,17 +404,21 @@ def ep_layout_dispatch(topk_idx, x, num_experts, num_ranks=1, rank=0, expert_ali
     outputs dict, dispatch outputs dict), the same as the two calls would."""
     T, K, workspace, outputs = _on_stream(stream, _layout_prep, topk_idx, num_experts, num_ranks, expert_alignment,
                                           workspace, outputs)
-    _need(x, torch.bfloat16, "x")
+    dev = topk_idx.device
+    _need(x, torch.bfloat16, "x", dev)
     if x.dim() != 2 or x.shape[0] != T:
         raise ValueError("x must be [num_tokens, hidden]")
     H = x.shape[1]
     if topk_weights is not None:
-        _need(topk_weights, torch.float32, "topk_weights", shape=(T, K))
+        _need(topk_weights, torch.float32, "topk_weights", dev, (T, K))
     if out is None:
         tmp = Handle(None, topk_idx, workspace, T, K, num_experts, num_ranks, rank, expert_alignment)
-        out = _on_stream(stream, alloc_dispatch_outputs, tmp, H, fp8, want_meta, want_send_meta, device=x.device,
+        out = _on_stream(stream, alloc_dispatch_outputs, tmp, H, fp8, want_meta, want_send_meta, device=dev,
                          do_expand=do_expand)
-    s = _dispatch_struct(out)
+        cap = out["recv_x"].shape[0]
+    else:
+        cap = check_dispatch_outputs(out, T, K, num_ranks, H, fp8, do_expand, dev)
+    s = _dispatch_struct(out, cap)
     h = ctypes.c_void_p()
     _check(_lib.ep_layout_dispatch(
         _ptr(topk_idx), T, K, num_experts, num_ranks, rank, expert_alignment, _ptr(workspace), workspace.numel(),
@@ -335,14 +435,15 @@ def ep_combine(handle: Handle, y, topk_weights=None, bias=None, out=None, stream
         raise ValueError("y must be [rows, hidden]")
     H = y.shape[1]
     T = handle.num_tokens
+    dev = y.device
     if topk_weights is not None:
-        _need(topk_weights, torch.float32, "topk_weights", shape=(T, handle.num_topk))
+        _need(topk_weights, torch.float32, "topk_weights", dev, (T, handle.num_topk))
     if bias is not None:
-        _need(bias, torch.bfloat16, "bias", shape=(T, H))
+        _need(bias, torch.bfloat16, "bias", dev, (T, H))
     if out is None:
-        out = _on_stream(stream, torch.empty, (T, H), dtype=torch.bfloat16, device=y.device)
+        out = _on_stream(stream, torch.empty, (T, H), dtype=torch.bfloat16, device=dev)
     else:
-        _need(out, torch.bfloat16, "out", shape=(T, H))
+        _need(out, torch.bfloat16, "out", dev, (T, H))
     _check(_lib.ep_combine(handle.ptr, _ptr(y), H, y.shape[0], _ptr(topk_weights), _ptr(bias), _ptr(out),
                            _stream(stream)), "ep_combine")
     return out
@@ -356,12 +457,13 @@ def ep_combine_tokens(handle: Handle, y, bias=None, out=None, stream=None):
         raise ValueError("y must be [rows, hidden]")
     H = y.shape[1]
     T = handle.num_tokens
+    dev = y.device
     if bias is not None:
-        _need(bias, torch.bfloat16, "bias", shape=(T, H))
+        _need(bias, torch.bfloat16, "bias", dev, (T, H))
     if out is None:
-        out = _on_stream(stream, torch.empty, (T, H), dtype=torch.bfloat16, device=y.device)
+        out = _on_stream(stream, torch.empty, (T, H), dtype=torch.bfloat16, device=dev)
     else:
-        _need(out, torch.bfloat16, "out", shape=(T, H))
+        _need(out, torch.bfloat16, "out", dev, (T, H))
     _check(_lib.ep_combine_tokens(handle.ptr, _ptr(y), H, y.shape[0], _ptr(bias), _ptr(out), _stream(stream)),
            "ep_combine_tokens")
     return out
@@ -371,27 +473,31 @@ def ep_dispatch_rows(handle: Handle, rows, scales=None, topk_weights=None, do_ze
                      stream=None):
     """Place received rows (uint8 [N, row_bytes] or bf16 [N, H]) expert-major through `handle` (a layout over
     the rows' local expert ids).  scales: fp32 [N, G] travelling with the rows.  Returns the output dict."""
-    if rows.dtype not in (torch.uint8, torch.bfloat16):
-        raise TypeError("rows must be uint8 or bfloat16")
+    if not isinstance(rows, torch.Tensor) or rows.dtype not in (torch.uint8, torch.bfloat16):
+        raise TypeError("rows must be a uint8 or bfloat16 tensor")
     _need(rows, rows.dtype, "rows")
     if rows.dim() != 2 or rows.shape[0] != handle.num_tokens:
         raise ValueError("rows must be [num_received_rows, row_elements]")
+    dev = rows.device
+    N = handle.num_tokens
     row_bytes = rows.shape[1] * rows.element_size()
     G = 0
     if scales is not None:
-        _need(scales, torch.float32, "scales")
+        if not isinstance(scales, torch.Tensor) or scales.dim() != 2:
+            raise ValueError("scales must be a 2-D tensor [num_received_rows, num_scales]")
         G = scales.shape[1]
+        _need(scales, torch.float32, "scales", dev, (N, G))
     if topk_weights is not None:
-        _need(topk_weights, torch.float32, "topk_weights", shape=(handle.num_tokens, handle.num_topk))
+        _need(topk_weights, torch.float32, "topk_weights", dev, (N, handle.num_topk))
     cap = handle.recv_capacity
     if out is None:
-        dev = rows.device
         out = _on_stream(stream, lambda: dict(
             recv_x=torch.empty((cap, rows.shape[1]), dtype=rows.dtype, device=dev),
             recv_x_scales=torch.empty((cap, G), dtype=torch.float32, device=dev) if G else None,
             recv_src_idx=torch.empty(cap, dtype=torch.int32, device=dev),
             recv_topk_weights=torch.empty(cap, dtype=torch.float32, device=dev)))
-    s = _dispatch_struct(out)   # the library reads the recv fields only
+    cap = check_rows_outputs(out, rows.dtype, rows.shape[1], G, dev)
+    s = _dispatch_struct(out, cap, _RECV_KEYS[:4])   # the library reads the recv fields only
     _check(_lib.ep_dispatch_rows(handle.ptr, _ptr(rows), row_bytes, _ptr(scales), G, _ptr(topk_weights),
                                  int(bool(do_zero_padding)), ctypes.byref(s), _stream(stream)), "ep_dispatch_rows")
     return out
@@ -401,18 +507,22 @@ def ep_combine_reduce(handle: Handle, partials=None, local=None, bias=None, out=
     """Sum the combine partials returned by the other ranks (bf16 [R, T, H], window r from rank r) with this
     rank's local combine output and the bias.  Returns out [T, H] bf16."""
     T = handle.num_tokens
-    ref = next(t for t in (partials, local, bias, out) if t is not None)
+    ref = next((t for t in (partials, local, bias, out) if t is not None), None)
+    if ref is None:
+        raise ValueError("ep_combine_reduce needs at least one of partials, local, bias, out")
+    _need(ref, torch.bfloat16, "partials/local/bias/out")
     H = ref.shape[-1] if hidden is None else hidden
+    dev = ref.device
     if partials is not None:
-        _need(partials, torch.bfloat16, "partials", shape=(handle.num_ranks, T, H))
+        _need(partials, torch.bfloat16, "partials", dev, (handle.num_ranks, T, H))
     if local is not None:
-        _need(local, torch.bfloat16, "local", shape=(T, H))
+        _need(local, torch.bfloat16, "local", dev, (T, H))
     if bias is not None:
-        _need(bias, torch.bfloat16, "bias", shape=(T, H))
+        _need(bias, torch.bfloat16, "bias", dev, (T, H))
     if out is None:
-        out = _on_stream(stream, torch.empty, (T, H), dtype=torch.bfloat16, device=ref.device)
+        out = _on_stream(stream, torch.empty, (T, H), dtype=torch.bfloat16, device=dev)
     else:
-        _need(out, torch.bfloat16, "out", shape=(T, H))
+        _need(out, torch.bfloat16, "out", dev, (T, H))
     _check(_lib.ep_combine_reduce(handle.ptr, _ptr(partials), H, _ptr(local), _ptr(bias), _ptr(out),
                                   _stream(stream)), "ep_combine_reduce")
     return out

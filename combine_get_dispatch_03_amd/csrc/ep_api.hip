@@ -6,6 +6,7 @@
 #include <map>
 #include <mutex>
 #include <new>
+#include <unordered_set>
 #include <utility>
 
 #include "ep_internal.hpp"
@@ -42,13 +43,46 @@ const char* check_shape(int T, int K, int E, int R, int rank, int A) {
     if (A < 1 || A > kMaxAlignment) return "expert_alignment must be in [1, 65536]";
     const int64_t cap = (int64_t)T * K + (int64_t)(E / R) * (A - 1);
     if (cap > INT32_MAX) return "receive capacity exceeds int32 rows";
+    // send-window rows r * T + j are int32 in the kernels
+    if ((int64_t)T * R > INT32_MAX) return "num_tokens * num_ranks exceeds int32 rows";
     return nullptr;
+}
+
+// Live handles.  A handle is looked up here before it is read, so a freed or foreign pointer is rejected without
+// being dereferenced (a stale pointer that the allocator has since handed to a new handle is indistinguishable
+// from that new handle).
+// Both are created on first use and never destroyed, so calls made while the process exits (a binding's
+// finaliser freeing its handle) still find them.
+std::mutex& handles_mu() {
+    static std::mutex* m = new std::mutex;
+    return *m;
+}
+std::unordered_set<const Handle*>& live_handles() {
+    static std::unordered_set<const Handle*>* s = new std::unordered_set<const Handle*>;
+    return *s;
+}
+
+bool register_handle(const Handle* h) {
+    std::lock_guard<std::mutex> lock(handles_mu());
+    try {
+        live_handles().insert(h);
+    } catch (...) {
+        return false;
+    }
+    return true;
+}
+
+// Removes h from the live set; false if it was not there.
+bool unregister_handle(const Handle* h) {
+    std::lock_guard<std::mutex> lock(handles_mu());
+    return live_handles().erase(h) != 0;
 }
 
 const Handle* check_handle(ep_handle_t h) {
     const Handle* hd = reinterpret_cast<const Handle*>(h);
-    if (hd == nullptr || hd->magic != kHandleMagic) return nullptr;
-    return hd;
+    if (hd == nullptr) return nullptr;
+    std::lock_guard<std::mutex> lock(handles_mu());
+    return live_handles().count(hd) != 0 ? hd : nullptr;
 }
 
 }  // namespace
@@ -149,7 +183,6 @@ ep_status_t new_handle(const int64_t* topk_idx, int num_tokens, int num_topk, in
 
     Handle* h = new (std::nothrow) Handle;
     if (h == nullptr) return fail(EP_ERR_INVALID_ARG, "out of host memory for the handle");
-    h->magic = kHandleMagic;
     h->T = num_tokens;
     h->K = num_topk;
     h->E = num_experts;
@@ -167,8 +200,17 @@ ep_status_t new_handle(const int64_t* topk_idx, int num_tokens, int num_topk, in
 }
 
 void drop_handle(Handle* h) {
-    h->magic = 0;
     delete h;
+}
+
+// Makes a fully built handle visible to the other calls.
+ep_status_t publish_handle(Handle* h, ep_handle_t* handle_out) {
+    if (!register_handle(h)) {
+        drop_handle(h);
+        return fail(EP_ERR_INVALID_ARG, "out of host memory for the handle registry");
+    }
+    *handle_out = reinterpret_cast<ep_handle_t>(h);
+    return EP_OK;
 }
 
 // Validation of ep_dispatch's arguments against a handle, and its launch arguments (nothing is enqueued).
@@ -233,8 +275,7 @@ ep_status_t ep_get_layout(const int64_t* topk_idx, int num_tokens, int num_topk,
         drop_handle(h);
         return hip_fail(err, "layout launch");
     }
-    *handle_out = reinterpret_cast<ep_handle_t>(h);
-    return EP_OK;
+    return publish_handle(h, handle_out);
 }
 
 ep_status_t ep_dispatch(ep_handle_t handle, const void* x, int hidden, const float* topk_weights,
@@ -276,8 +317,7 @@ ep_status_t ep_layout_dispatch(const int64_t* topk_idx, int num_tokens, int num_
         drop_handle(h);
         return hip_fail(err, "layout_dispatch launch");
     }
-    *handle_out = reinterpret_cast<ep_handle_t>(h);
-    return EP_OK;
+    return publish_handle(h, handle_out);
 }
 
 ep_status_t ep_dispatch_rows(ep_handle_t handle, const void* rows, int row_bytes, const float* row_scales,
@@ -400,9 +440,8 @@ ep_status_t ep_combine_tokens(ep_handle_t handle, const void* y, int hidden, int
 ep_status_t ep_handle_free(ep_handle_t handle) {
     Handle* h = reinterpret_cast<Handle*>(handle);
     if (h == nullptr) return EP_OK;
-    if (h->magic != kHandleMagic) return fail(EP_ERR_INVALID_ARG, "invalid handle");
-    h->magic = 0;
-    delete h;
+    if (!unregister_handle(h)) return fail(EP_ERR_INVALID_ARG, "invalid handle (not live: freed twice or never created)");
+    drop_handle(h);
     return EP_OK;
 }
 

@@ -11,7 +11,6 @@
 
 namespace ep {
 
-constexpr uint32_t kHandleMagic = 0x45504831u;   // "EPH1"
 constexpr int kLayoutTileTokens = 256;           // tokens per layout tile (one 1024-thread block)
 constexpr int kMaxTopk = 32;
 constexpr int kMaxExperts = 1024;
@@ -37,7 +36,6 @@ struct Workspace {
 Workspace carve_workspace(void* base, int T, int K, int E, int R, int A);
 
 struct Handle {
-    uint32_t magic;
     int T, K, E, R, rank, A;
     int El;        // local experts E / R
     int lo;        // first local expert rank * El

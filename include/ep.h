@@ -36,7 +36,14 @@
  *
  * Limits: 0 <= num_tokens; 1 <= num_topk <= 32; 1 <= num_experts <= 1024; 1 <= num_ranks <= 64 with
  * num_experts % num_ranks == 0; 0 <= rank < num_ranks; 1 <= expert_alignment <= 65536; the receive capacity
- * must fit in int32; hidden % 8 == 0, 8 <= hidden <= 32768, and hidden % 128 == 0 for FP8.
+ * must fit in int32, and so must num_tokens * num_ranks (the send-window rows); hidden % 8 == 0,
+ * 8 <= hidden <= 32768, and hidden % 128 == 0 for FP8.
+ *
+ * Handles: every call that takes a handle first looks it up among the live handles (created and not yet freed)
+ * and returns EP_ERR_INVALID_ARG for any other pointer without reading through it, so a handle freed twice or
+ * used after ep_handle_free is an error, not undefined behaviour.  (A stale pointer that the host allocator has
+ * since reused for a new handle refers to that new handle.)  Freeing a handle while another thread is inside a
+ * call with it is a caller error, like freeing any buffer an operation still uses ([MoE-comm] §二).
  */
 #ifndef EP_MI355X_H
 #define EP_MI355X_H
@@ -68,11 +75,16 @@ typedef struct ep_handle* ep_handle_t;   /* opaque host object created by ep_get
  * §一: equal, fixed capacity).  Host only.  Returns -1 for arguments outside the limits. */
 int64_t ep_recv_capacity(int num_tokens, int num_topk, int num_local_experts, int expert_alignment);
 
-/* Bytes of device workspace ep_get_layout needs for these sizes.  Host only.  Returns 0 for arguments
- * outside the limits (a valid call always needs more than 0 bytes). */
+/* Library helper (no page defines it; it sizes the caller-owned scratch that replaces DeepEP's internal
+ * buffers, [MoE-comm] §一: buffers are sized once from the capacity and reused).  Bytes of device workspace
+ * ep_get_layout needs for these sizes.  Host only.  Returns 0 for arguments outside the limits (a valid call
+ * always needs more than 0 bytes). */
 size_t ep_layout_workspace_bytes(int num_tokens, int num_topk, int num_experts, int num_ranks, int expert_alignment);
 
-/* Static description of a status code, and a thread-local description of the last failure in this thread. */
+/* Library helpers (no page defines them; the C ABI's replacement for the exceptions a Python API raises on a
+ * failed pre-launch check, [repo-map] §2.1: the runtime validates arguments before launching).  A static
+ * description of a status code, and a thread-local description of the last failure in this thread ("" after a
+ * successful call). */
 const char* ep_status_string(ep_status_t status);
 const char* ep_last_error(void);
 
@@ -250,7 +262,12 @@ ep_status_t ep_combine_tokens(ep_handle_t handle, const void* y, int hidden, int
 ep_status_t ep_combine_reduce(ep_handle_t handle, const void* partials, int hidden, const void* local,
                               const void* bias, void* out, void* stream);
 
-/* Free the host object of a handle (never blocks, never touches device memory).  NULL is allowed. */
+/* End of a handle's life ([MoE-comm] §二: a handle and the buffers it refers to must outlive every operation
+ * that uses them; §一: the handle carries the dispatch's grouping for the combine and backward).  Frees the host
+ * object only: never blocks, never touches device memory, so kernels already enqueued with the handle are
+ * unaffected (they took their arguments at launch).  NULL is allowed (no-op).  A pointer that is not a live
+ * handle (already freed, or never returned by ep_get_layout / ep_layout_dispatch) returns EP_ERR_INVALID_ARG
+ * without being read. */
 ep_status_t ep_handle_free(ep_handle_t handle);
 
 #ifdef __cplusplus

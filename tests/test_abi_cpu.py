@@ -129,6 +129,31 @@ def test_dispatch_combine_reject_bad_handles(lib):
     assert b"handle" in lib.ep_last_error()
 
 
+def test_handle_lookup_never_dereferences(lib):
+    """A pointer that is not a live handle is rejected without being read: addresses that are not mapped at all
+    (reading them would crash the process) and a host block whose bytes look like anything."""
+    for addr in (0x10, 0x1000, 0x7FFF0000DEAD0):
+        p = ctypes.c_void_p(addr)
+        assert lib.ep_handle_free(p) == 1
+        assert b"not live" in lib.ep_last_error()
+        assert lib.ep_dispatch(p, None, 128, None, 1, 1, 0, None, None) == 1
+        assert lib.ep_combine(p, None, 128, 0, None, None, None, None) == 1
+        assert lib.ep_combine_tokens(p, None, 128, 0, None, None, None) == 1
+    junk = (ctypes.c_uint8 * 4096)(*([0xFF] * 4096))
+    assert lib.ep_handle_free(ctypes.cast(junk, ctypes.c_void_p)) == 1
+
+
+def test_limit_on_window_rows(lib):
+    """num_tokens * num_ranks must fit in int32 (send-window rows are int32 in the kernels)."""
+    h = ctypes.c_void_p()
+    T = (1 << 31) // 64 + 1                                # T * 64 > INT32_MAX, T * K and the capacity fit
+    rc = lib.ep_get_layout(ctypes.c_void_p(0x10000), T, 1, 64, 64, 0, 1, ctypes.c_void_p(0x100000), 1 << 40,
+                           None, None, None, None, None, ctypes.byref(h), None)
+    assert rc == 1 and b"num_ranks" in lib.ep_last_error()
+    assert lib.ep_layout_workspace_bytes(T, 1, 64, 64, 1) == 0
+    assert lib.ep_layout_workspace_bytes(T, 1, 64, 32, 1) > 0
+
+
 _OUT_FIELDS = ("recv_x", "recv_x_scales", "recv_src_idx", "recv_topk_weights", "recv_topk_idx", "recv_capacity",
                "send_x", "send_x_scales", "send_src_idx", "send_topk_idx", "send_topk_weights")
 
@@ -164,7 +189,7 @@ def test_dispatch_struct_from_tensors():
     import combine_get_dispatch_03_amd as ep
     out = dict(recv_x=torch.empty((37, 16), dtype=torch.uint8), recv_x_scales=torch.empty((37, 1)),
                recv_src_idx=None, recv_topk_weights=torch.empty(37), send_x=torch.empty((2, 5, 16), dtype=torch.uint8))
-    s = ep._dispatch_struct(out)
+    s = ep._dispatch_struct(out, 37)
     assert s.recv_capacity == 37
     for f in _OUT_FIELDS:
         if f == "recv_capacity":
