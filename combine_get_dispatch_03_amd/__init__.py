@@ -70,6 +70,9 @@ def _load_library():
     lib.ep_combine_reduce.argtypes = [P, P, I, P, P, P, P]
     lib.ep_combine_tokens.restype = I
     lib.ep_combine_tokens.argtypes = [P, P, I, I64, P, P, P]
+    lib.ep_layout_dispatch_noalloc.restype = I
+    lib.ep_layout_dispatch_noalloc.argtypes = [P, I, I, I, I, I, I, P, P, P, P, P, P, I, P, I, I, I,
+                                               ctypes.POINTER(_DispatchOut), ctypes.POINTER(P), P]
     lib.ep_layout_dispatch.restype = I
     lib.ep_layout_dispatch.argtypes = [P, I, I, I, I, I, I, P, SZ, P, P, P, P, P, P, I, P, I, I, I,
                                        ctypes.POINTER(_DispatchOut), ctypes.POINTER(P), P]
@@ -428,6 +431,44 @@ def ep_layout_dispatch(topk_idx, x, num_experts, num_ranks=1, rank=0, expert_ali
     return Handle(h, topk_idx, workspace, T, K, num_experts, num_ranks, rank, expert_alignment), outputs, out
 
 
+def ep_layout_dispatch_noalloc(topk_idx, x, num_experts, out, num_ranks=1, rank=0, expert_alignment=1,
+                               topk_weights=None, fp8=True, do_expand=True, do_zero_padding=False, outputs=None,
+                               stream=None):
+    """ep_layout_dispatch for callers that cannot allocate: no workspace (the library's static per-GPU scratch
+    serves as one), caller-supplied dispatch outputs `out`, and optional layout `outputs` (None: not written).
+    Nothing is allocated here either.  The returned Handle wraps the GPU's static handle: valid until the next
+    call of this function on the same GPU, which overwrites it; freeing it is a no-op.  Returns (Handle,
+    outputs, out)."""
+    _need(topk_idx, torch.int64, "topk_idx")
+    if topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be [num_tokens, num_topk]")
+    T, K = topk_idx.shape
+    dev = topk_idx.device
+    if num_ranks < 1 or num_experts < 1 or num_experts % num_ranks != 0:
+        raise ValueError("num_experts must be a positive multiple of num_ranks")
+    _need(x, torch.bfloat16, "x", dev)
+    if x.dim() != 2 or x.shape[0] != T:
+        raise ValueError("x must be [num_tokens, hidden]")
+    H = x.shape[1]
+    if topk_weights is not None:
+        _need(topk_weights, torch.float32, "topk_weights", dev, (T, K))
+    if out is None:
+        raise ValueError("ep_layout_dispatch_noalloc needs caller-allocated dispatch outputs (out)")
+    cap = check_dispatch_outputs(out, T, K, num_ranks, H, fp8, do_expand, dev)
+    if outputs is None:
+        outputs = {}
+    else:
+        check_layout_outputs(outputs, T, num_experts, num_ranks, dev)
+    s = _dispatch_struct(out, cap)
+    h = ctypes.c_void_p()
+    _check(_lib.ep_layout_dispatch_noalloc(
+        _ptr(topk_idx), T, K, num_experts, num_ranks, rank, expert_alignment, *_layout_ptrs(outputs), _ptr(x), H,
+        _ptr(topk_weights), EP_DTYPE_FP8_E4M3 if fp8 else EP_DTYPE_BF16, int(bool(do_expand)),
+        int(bool(do_zero_padding)), ctypes.byref(s), ctypes.byref(h), _stream(stream)),
+        "ep_layout_dispatch_noalloc")
+    return Handle(h, topk_idx, None, T, K, num_experts, num_ranks, rank, expert_alignment), outputs, out
+
+
 def ep_combine(handle: Handle, y, topk_weights=None, bias=None, out=None, stream=None):
     """Combine expert outputs `y` (bf16 [>= recv_capacity, H]) back to token order.  Returns out [T, H] bf16."""
     _need(y, torch.bfloat16, "y")
@@ -532,7 +573,7 @@ def ep_handle_free(handle: Handle):
     handle.free()
 
 
-__all__ = ["ep_get_layout", "ep_dispatch", "ep_layout_dispatch", "ep_combine", "ep_combine_tokens", "ep_handle_free", "ep_recv_capacity",
+__all__ = ["ep_get_layout", "ep_dispatch", "ep_layout_dispatch", "ep_layout_dispatch_noalloc", "ep_combine", "ep_combine_tokens", "ep_handle_free", "ep_recv_capacity",
            "ep_dispatch_rows", "ep_combine_reduce",
            "ep_layout_workspace_bytes", "alloc_dispatch_outputs", "Handle", "EPError", "LIB_PATH",
            "hip_runtimes_loaded"]

@@ -3,13 +3,18 @@
 // allocates device memory or synchronises.
 #include <cstdarg>
 #include <cstdio>
-#include <map>
 #include <mutex>
 #include <new>
 #include <unordered_set>
 #include <utility>
 
 #include "ep_internal.hpp"
+
+// Device scratch of ep_layout_dispatch_noalloc: the layout workspace of a caller that cannot allocate device
+// memory.  One copy per GPU, for the life of the process.  In host code `scratch` names a host-side stand-in,
+// not device memory: host code uses only the per-device address that hipGetSymbolAddress returns for it.
+constexpr size_t kNoAllocScratchBytes = 4u << 20;   // 4 MiB
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 namespace ep {
 namespace {
@@ -78,9 +83,33 @@ bool unregister_handle(const Handle* h) {
     return live_handles().erase(h) != 0;
 }
 
+// Per-device state of ep_layout_dispatch_noalloc: the device address of `scratch` (looked up once, with the
+// device current) and the handle that the call returns, overwritten by each call on that device.  Host statics:
+// nothing is allocated for them.
+constexpr int kMaxDevices = 64;
+struct NoAllocSlot {
+    void* scratch = nullptr;   // device address of this device's copy of `scratch`
+    bool ready = false;
+    Handle handle;
+};
+std::mutex g_noalloc_mu;
+NoAllocSlot g_noalloc[kMaxDevices];
+
+// The slot index of a static handle, or -1.
+int static_handle_index(const Handle* h) {
+    for (int d = 0; d < kMaxDevices; ++d)
+        if (h == &g_noalloc[d].handle) return d;
+    return -1;
+}
+
 const Handle* check_handle(ep_handle_t h) {
     const Handle* hd = reinterpret_cast<const Handle*>(h);
     if (hd == nullptr) return nullptr;
+    const int d = static_handle_index(hd);
+    if (d >= 0) {
+        std::lock_guard<std::mutex> lock(g_noalloc_mu);
+        return g_noalloc[d].ready && g_noalloc[d].handle.T >= 0 ? hd : nullptr;
+    }
     std::lock_guard<std::mutex> lock(handles_mu());
     return live_handles().count(hd) != 0 ? hd : nullptr;
 }
@@ -91,14 +120,24 @@ hipError_t allow_dynamic_lds(const void* kernel, int bytes) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
+    // (kernel, device) -> largest size set; a fixed table, so that no call allocates host memory for it
+    struct Entry {
+        const void* kernel;
+        int dev, bytes;
+    };
+    constexpr int kEntries = 256;
     static std::mutex mu;
-    static std::map<std::pair<const void*, int>, int> allowed;   // (kernel, device) -> largest size set
+    static Entry table[kEntries];
+    static int used = 0;
     std::lock_guard<std::mutex> lock(mu);
-    const auto it = allowed.find({kernel, dev});
-    if (it != allowed.end() && it->second >= bytes) return hipSuccess;
+    int i = 0;
+    while (i < used && !(table[i].kernel == kernel && table[i].dev == dev)) ++i;
+    if (i < used && table[i].bytes >= bytes) return hipSuccess;
     e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e == hipSuccess) allowed[{kernel, dev}] = bytes;
-    return e;
+    if (e != hipSuccess) return e;
+    if (i == used && used < kEntries) table[used++] = Entry{kernel, dev, 0};
+    if (i < used) table[i].bytes = bytes;   // (a full table only costs a repeated attribute call)
+    return hipSuccess;
 }
 
 Workspace carve_workspace(void* base, int T, int K, int E, int R, int A) {
@@ -166,10 +205,10 @@ const char* ep_last_error(void) { return g_last_error; }
 
 namespace {
 
-// Validation and the handle of ep_get_layout (nothing is enqueued).
-ep_status_t new_handle(const int64_t* topk_idx, int num_tokens, int num_topk, int num_experts, int num_ranks, int rank,
-                       int expert_alignment, void* workspace, size_t workspace_bytes, ep_handle_t* handle_out,
-                       Handle** h_out) {
+// Validation of ep_get_layout's arguments and the carve-up of its workspace (nothing is enqueued).
+ep_status_t layout_args(const int64_t* topk_idx, int num_tokens, int num_topk, int num_experts, int num_ranks,
+                        int rank, int expert_alignment, void* workspace, size_t workspace_bytes,
+                        ep_handle_t* handle_out, Workspace* ws) {
     if (handle_out == nullptr) return fail(EP_ERR_INVALID_ARG, "handle_out is NULL");
     if (const char* why = check_shape(num_tokens, num_topk, num_experts, num_ranks, rank, expert_alignment))
         return fail(EP_ERR_INVALID_ARG, "%s", why);
@@ -177,12 +216,14 @@ ep_status_t new_handle(const int64_t* topk_idx, int num_tokens, int num_topk, in
     if (workspace == nullptr) return fail(EP_ERR_INVALID_ARG, "workspace is NULL");
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return fail(EP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-    const Workspace ws = carve_workspace(workspace, num_tokens, num_topk, num_experts, num_ranks, expert_alignment);
-    if (workspace_bytes < ws.bytes)
-        return fail(EP_ERR_INVALID_ARG, "workspace_bytes %zu < required %zu", workspace_bytes, ws.bytes);
+    *ws = carve_workspace(workspace, num_tokens, num_topk, num_experts, num_ranks, expert_alignment);
+    if (workspace_bytes < ws->bytes)
+        return fail(EP_ERR_INVALID_ARG, "workspace_bytes %zu < required %zu", workspace_bytes, ws->bytes);
+    return EP_OK;
+}
 
-    Handle* h = new (std::nothrow) Handle;
-    if (h == nullptr) return fail(EP_ERR_INVALID_ARG, "out of host memory for the handle");
+void fill_handle(Handle* h, const int64_t* topk_idx, int num_tokens, int num_topk, int num_experts, int num_ranks,
+                 int rank, int expert_alignment, const Workspace& ws) {
     h->T = num_tokens;
     h->K = num_topk;
     h->E = num_experts;
@@ -195,6 +236,19 @@ ep_status_t new_handle(const int64_t* topk_idx, int num_tokens, int num_topk, in
     h->cap = (int64_t)num_tokens * num_topk + (int64_t)h->El * (expert_alignment - 1);
     h->topk_idx = topk_idx;
     h->ws = ws;
+}
+
+// Validation and a new handle for ep_get_layout / ep_layout_dispatch (nothing is enqueued).
+ep_status_t new_handle(const int64_t* topk_idx, int num_tokens, int num_topk, int num_experts, int num_ranks, int rank,
+                       int expert_alignment, void* workspace, size_t workspace_bytes, ep_handle_t* handle_out,
+                       Handle** h_out) {
+    Workspace ws;
+    const ep_status_t st = layout_args(topk_idx, num_tokens, num_topk, num_experts, num_ranks, rank,
+                                       expert_alignment, workspace, workspace_bytes, handle_out, &ws);
+    if (st != EP_OK) return st;
+    Handle* h = new (std::nothrow) Handle;
+    if (h == nullptr) return fail(EP_ERR_INVALID_ARG, "out of host memory for the handle");
+    fill_handle(h, topk_idx, num_tokens, num_topk, num_experts, num_ranks, rank, expert_alignment, ws);
     *h_out = h;
     return EP_OK;
 }
@@ -320,6 +374,58 @@ ep_status_t ep_layout_dispatch(const int64_t* topk_idx, int num_tokens, int num_
     return publish_handle(h, handle_out);
 }
 
+ep_status_t ep_layout_dispatch_noalloc(const int64_t* topk_idx, int num_tokens, int num_topk, int num_experts,
+                                       int num_ranks, int rank, int expert_alignment, int32_t* num_tokens_per_rank,
+                                       int32_t* num_tokens_per_expert, uint8_t* is_token_in_rank,
+                                       int32_t* psum_num_recv_tokens_per_expert, int32_t* num_invalid_topk,
+                                       const void* x, int hidden, const float* topk_weights, ep_dtype_t recv_dtype,
+                                       int do_expand, int do_zero_padding, const ep_dispatch_out_t* out,
+                                       ep_handle_t* handle_out, void* stream) {
+    g_last_error[0] = '\0';
+    if (handle_out == nullptr) return fail(EP_ERR_INVALID_ARG, "handle_out is NULL");
+    if (const char* why = check_shape(num_tokens, num_topk, num_experts, num_ranks, rank, expert_alignment))
+        return fail(EP_ERR_INVALID_ARG, "%s", why);
+    const size_t need = carve_workspace(nullptr, num_tokens, num_topk, num_experts, num_ranks, expert_alignment).bytes;
+    if (need > kNoAllocScratchBytes)
+        return fail(EP_ERR_INVALID_ARG,
+                    "ep_layout_dispatch_noalloc: these sizes need %zu bytes of layout workspace, more than its "
+                    "static scratch of %zu bytes; call ep_layout_dispatch with a workspace instead",
+                    need, kNoAllocScratchBytes);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(EP_ERR_INVALID_ARG, "ep_layout_dispatch_noalloc: device %d beyond the first %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_noalloc_mu);
+    NoAllocSlot& slot = g_noalloc[dev];
+    if (!slot.ready) {   // set-up, once per device, with that device current
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (ptr == nullptr || (reinterpret_cast<uintptr_t>(ptr) & 255u) != 0)
+            return fail(EP_ERR_HIP, "hipGetSymbolAddress(scratch) returned an unusable address");
+        slot.scratch = ptr;
+        slot.handle.T = -1;   // no layout yet
+        slot.ready = true;
+    }
+    Workspace ws;
+    ep_status_t st = layout_args(topk_idx, num_tokens, num_topk, num_experts, num_ranks, rank, expert_alignment,
+                                 slot.scratch, kNoAllocScratchBytes, handle_out, &ws);
+    if (st != EP_OK) return st;
+    Handle h;
+    fill_handle(&h, topk_idx, num_tokens, num_topk, num_experts, num_ranks, rank, expert_alignment, ws);
+    DispatchArgs a;
+    st = dispatch_args(&h, x, hidden, topk_weights, recv_dtype, do_expand, do_zero_padding, out, &a);
+    if (st != EP_OK) return st;
+    const LayoutOutputs lo{num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank,
+                           psum_num_recv_tokens_per_expert, num_invalid_topk};
+    e = launch_layout_dispatch(h, lo, a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "layout_dispatch_noalloc launch");
+    slot.handle = h;
+    *handle_out = reinterpret_cast<ep_handle_t>(&slot.handle);
+    return EP_OK;
+}
+
 ep_status_t ep_dispatch_rows(ep_handle_t handle, const void* rows, int row_bytes, const float* row_scales,
                              int num_scales, const float* topk_weights, int do_zero_padding,
                              const ep_dispatch_out_t* out, void* stream) {
@@ -440,6 +546,7 @@ ep_status_t ep_combine_tokens(ep_handle_t handle, const void* y, int hidden, int
 ep_status_t ep_handle_free(ep_handle_t handle) {
     Handle* h = reinterpret_cast<Handle*>(handle);
     if (h == nullptr) return EP_OK;
+    if (static_handle_index(h) >= 0) return EP_OK;   // a device's ep_layout_dispatch_noalloc handle: never freed
     if (!unregister_handle(h)) return fail(EP_ERR_INVALID_ARG, "invalid handle (not live: freed twice or never created)");
     drop_handle(h);
     return EP_OK;

@@ -195,6 +195,33 @@ ep_status_t ep_layout_dispatch(const int64_t* topk_idx, int num_tokens, int num_
                                const ep_dispatch_out_t* out, ep_handle_t* handle_out, void* stream);
 
 /*
+ * ep_layout_dispatch_noalloc -- ep_layout_dispatch for callers that cannot allocate: code under HIP graph capture,
+ * tight serving loops, and harnesses that forbid device allocation.  The same arguments without the workspace,
+ * the same outputs bit for bit.  It calls no device or host allocator: the layout workspace is a static device
+ * array of 4 MiB in this library (one copy per GPU, held until the process ends), and the handle is a static
+ * per-GPU object.  Set-up on the first call on a GPU (with that GPU current) looks up that GPU's copy of the
+ * array; make that first call outside any graph capture.
+ *
+ *   Limit: sizes whose workspace (ep_layout_workspace_bytes) exceeds 4 MiB are rejected with
+ *   EP_ERR_INVALID_ARG before anything is enqueued (about 100,000 tokens at top-8 with 256 experts and
+ *   alignment 128).  Every byte of the array that the kernels read is written earlier in the same call, so no
+ *   contents need clearing between calls.
+ *   Sharing: every call on a GPU uses that GPU's one array and one handle.  The returned handle is valid for
+ *   ep_dispatch / ep_combine / ep_combine_tokens / ep_combine_reduce until the next ep_layout_dispatch_noalloc
+ *   on the same GPU, which overwrites both (a handle kept from an earlier call then refers to the new layout).
+ *   Calls that overlap on one GPU -- from two host threads, or a new call enqueued on another stream while
+ *   kernels of an earlier call or of its handle's dispatch / combine may still run -- race on the array.
+ *   ep_handle_free on this handle is a no-op returning EP_OK.
+ */
+ep_status_t ep_layout_dispatch_noalloc(const int64_t* topk_idx, int num_tokens, int num_topk, int num_experts,
+                                       int num_ranks, int rank, int expert_alignment, int32_t* num_tokens_per_rank,
+                                       int32_t* num_tokens_per_expert, uint8_t* is_token_in_rank,
+                                       int32_t* psum_num_recv_tokens_per_expert, int32_t* num_invalid_topk,
+                                       const void* x, int hidden, const float* topk_weights, ep_dtype_t recv_dtype,
+                                       int do_expand, int do_zero_padding, const ep_dispatch_out_t* out,
+                                       ep_handle_t* handle_out, void* stream);
+
+/*
  * ep_dispatch_rows -- the receiver's copy epilogue ([DeepEP->MegaMoE] §2.4: rows that arrived
  * destination-major are placed expert-major, each at its expert's rows).  Rows already carry their receive
  * format (the bytes and scales of a sender's send window), so nothing is converted.

@@ -154,6 +154,25 @@ def test_limit_on_window_rows(lib):
     assert lib.ep_layout_workspace_bytes(T, 1, 64, 32, 1) > 0
 
 
+def test_noalloc_rejects_oversize_before_anything(lib):
+    """ep_layout_dispatch_noalloc rejects sizes whose layout workspace exceeds its 4 MiB static scratch, on the host,
+    before it looks up a device (so this runs without a GPU; the pointers are never read)."""
+    P, I = ctypes.c_void_p, ctypes.c_int
+    f = lib.ep_layout_dispatch_noalloc
+    f.restype = I
+    f.argtypes = [P, I, I, I, I, I, I, P, P, P, P, P, P, I, P, I, I, I, P, ctypes.POINTER(P), P]
+    ws = lib.ep_layout_workspace_bytes
+    assert ws(110000, 8, 256, 1, 128) > 4 << 20 >= ws(100000, 8, 256, 1, 128)
+    h = ctypes.c_void_p()
+    rc = f(P(0x10000), 110000, 8, 256, 1, 0, 128, None, None, None, None, None, P(0x20000), 128, None, 1, 1, 0,
+           None, ctypes.byref(h), None)
+    assert rc == 1 and b"static scratch" in lib.ep_last_error()
+    assert h.value is None
+    rc = f(P(0x10000), 100, 8, 256, 1, 0, 128, None, None, None, None, None, P(0x20000), 128, None, 1, 1, 0,
+           None, None, None)
+    assert rc == 1 and b"handle_out" in lib.ep_last_error()
+
+
 _OUT_FIELDS = ("recv_x", "recv_x_scales", "recv_src_idx", "recv_topk_weights", "recv_topk_idx", "recv_capacity",
                "send_x", "send_x_scales", "send_src_idx", "send_topk_idx", "send_topk_weights")
 
