@@ -614,7 +614,7 @@ def main():
         metric="dispatch/combine effective HBM GB/s + % of peak, 4096 tok\u00d77168 top-8, 1 GPU",
         value=round(value, 1), unit="GB/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
         ms_per_step=round(ms_per_step, 4), higher_is_better=True, scaling="weak", vs_baseline=None,
-        dtype="fp32", data="synthetic",
+        dtype="bf16/fp8-e4m3", data="synthetic",
         config=dict(workload="%s: %d tok x hidden %d, %d experts%s, top-%d, FP8 e4m3 per-128 dispatch%s, "
                               "BF16 combine, alignment %d" % (
                                   cfg.name, T, cfg.hidden, E,

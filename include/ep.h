@@ -156,6 +156,9 @@ typedef struct ep_dispatch_out {
  *                   recv_topk_weights and send_topk_weights only.
  *   recv_dtype      EP_DTYPE_BF16 or EP_DTYPE_FP8_E4M3.  FP8: per token and 128-channel group,
  *                   a = max(max|x|, 1e-4), scale = a / 448, q = e4m3_rne_saturating(x * (448 / a)).
+ *                   x must be finite for FP8: the codes and the scale of a group holding a NaN or an infinity
+ *                   are unspecified (no page defines them); the token's other groups and all other rows are
+ *                   unaffected.  BF16 rows are bit copies whatever they hold.
  *   do_expand       1: expert-major rows, one per routed entry, at the rows of the layout.
  *                   0: token-major rows ([MoE-comm] §一 dispatch arguments, do_expand): one row per token
  *                   with an expert on this rank, in ascending token order (row j = the j-th such token),

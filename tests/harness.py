@@ -19,24 +19,103 @@ CANARY_F32 = -7.0
 ATOL, RTOL = 1e-2, 8e-3     # combine tolerance: |gpu - oracle| <= ATOL + RTOL * |oracle|
 
 
+GUARD_ROWS = 2              # rows of canary past the end of every guarded output
+
+
+class Guarded(dict):
+    """Output tensors, each the leading part of a larger buffer whose tail (at least GUARD_ROWS rows past the
+    documented size, and at least 256 elements) no call may touch: a store past the end of an output lands in
+    the tail and is caught by assert_guards."""
+
+    def __init__(self, *a, **kw):
+        super().__init__(*a, **kw)
+        self.parents = {}       # key -> (parent buffer, numel of the view)
+
+
+def _guarded_empty(shape, dtype, device):
+    shape = tuple(int(d) for d in shape)
+    n = int(np.prod(shape)) if shape else 1
+    row = shape[-1] if len(shape) > 1 else 1
+    parent = torch.empty(n + max(GUARD_ROWS * row, 256), dtype=dtype, device=device)
+    return parent[:n].view(shape), parent, n
+
+
+def guard(o):
+    """The same outputs (shapes and dtypes) as views into guarded buffers."""
+    g = Guarded()
+    for k, t in o.items():
+        if t is None:
+            g[k] = None
+            continue
+        v, parent, n = _guarded_empty(t.shape, t.dtype, t.device)
+        g[k] = v
+        g.parents[k] = (parent, n)
+    return g
+
+
+def guarded_tensor(shape, dtype, device, key="out"):
+    """One guarded, canary-filled output tensor; returns (tensor, Guarded dict holding it)."""
+    g = Guarded()
+    v, parent, n = _guarded_empty(shape, dtype, device)
+    g[key] = v
+    g.parents[key] = (parent, n)
+    fill_canaries(g)
+    return v, g
+
+
 def dispatch_outputs_with_canary(ep, h, hidden, fp8, dev, do_expand=True):
-    """Dispatch output tensors, pre-filled with canaries (the binding itself never initialises them)."""
-    return fill_canaries(ep.alloc_dispatch_outputs(h, hidden, fp8, device=dev, do_expand=do_expand))
+    """Dispatch output tensors, pre-filled with canaries (the binding itself never initialises them), each with a
+    canary tail past its end."""
+    return fill_canaries(guard(ep.alloc_dispatch_outputs(h, hidden, fp8, device=dev, do_expand=do_expand)))
+
+
+def layout_outputs_with_canary(T, E, R, dev):
+    El = E // R
+    o = dict(num_tokens_per_rank=torch.empty(R, dtype=torch.int32, device=dev),
+             num_tokens_per_expert=torch.empty(E, dtype=torch.int32, device=dev),
+             is_token_in_rank=torch.empty((T, R), dtype=torch.uint8, device=dev),
+             psum_num_recv_tokens_per_expert=torch.empty(El + 1, dtype=torch.int32, device=dev),
+             num_invalid_topk=torch.empty(1, dtype=torch.int32, device=dev))
+    return fill_canaries(guard(o))
+
+
+def _canary_fill(t, key):
+    if t.dtype in (torch.uint8,):
+        t.fill_(CANARY_BYTE)
+    elif t.dtype == torch.bfloat16:
+        t.view(torch.int16).fill_(np.int16(np.uint16(CANARY_BYTE * 257).view(np.int16)))
+    elif t.dtype == torch.float32:
+        t.fill_(CANARY_SCALE if "scales" in key else CANARY_F32)
+    else:
+        t.fill_(CANARY_I32)
 
 
 def fill_canaries(o):
     for k, t in o.items():
         if t is None:
             continue
-        if t.dtype in (torch.uint8,):
-            t.fill_(CANARY_BYTE)
-        elif t.dtype == torch.bfloat16:
-            t.view(torch.int16).fill_(np.int16(np.uint16(CANARY_BYTE * 257).view(np.int16)))
-        elif t.dtype == torch.float32:
-            t.fill_(CANARY_SCALE if "scales" in k else CANARY_F32)
+        if isinstance(o, Guarded) and k in o.parents:
+            _canary_fill(o.parents[k][0], k)      # the tail too
         else:
-            t.fill_(CANARY_I32)
+            _canary_fill(t, k)
     return o
+
+
+def assert_guards(o):
+    """Every guarded output's tail still holds its canary."""
+    if not isinstance(o, Guarded):
+        return
+    for k, (parent, n) in o.parents.items():
+        tail = parent[n:]
+        ref = torch.empty_like(tail)
+        _canary_fill(ref, k)
+        if tail.dtype == torch.bfloat16:
+            tail, ref = tail.view(torch.int16), ref.view(torch.int16)
+        elif tail.dtype == torch.float32:
+            tail, ref = tail.view(torch.int32), ref.view(torch.int32)
+        bad = (tail != ref).nonzero()
+        assert bad.numel() == 0, "%s: %d element(s) written past its end, first at +%d" % (
+            k, bad.shape[0], int(bad[0, 0]))
 
 
 def to_np(t):
@@ -63,7 +142,8 @@ def oracle_run(inp, recv_fill=True, do_expand=True):
 def gpu_layout_dispatch(ep, inp, dev="cuda", do_expand=True):
     c = inp["cfg"]
     idx = inp["topk_idx"].to(dev)
-    h, lay = ep.ep_get_layout(idx, c.num_experts, c.num_ranks, c.rank, c.expert_alignment)
+    lay_out = layout_outputs_with_canary(c.num_tokens, c.num_experts, c.num_ranks, dev)
+    h, lay = ep.ep_get_layout(idx, c.num_experts, c.num_ranks, c.rank, c.expert_alignment, outputs=lay_out)
     out = dispatch_outputs_with_canary(ep, h, c.hidden, c.fp8, dev, do_expand=do_expand)
     ep.ep_dispatch(h, inp["x"].to(dev), inp["topk_weights"].to(dev), fp8=c.fp8, do_expand=do_expand,
                    do_zero_padding=c.zero_padding, out=out)
@@ -71,6 +151,7 @@ def gpu_layout_dispatch(ep, inp, dev="cuda", do_expand=True):
 
 
 def assert_layout_equal(glay, olay, c):
+    assert_guards(glay)
     assert np.array_equal(to_np(glay["num_tokens_per_expert"]), olay["cnt"])
     assert np.array_equal(to_np(glay["num_tokens_per_rank"]), olay["ntok_rank"])
     assert np.array_equal(to_np(glay["is_token_in_rank"]), olay["in_rank"])
@@ -79,7 +160,8 @@ def assert_layout_equal(glay, olay, c):
 
 
 def assert_dispatch_equal(gout, od, c):
-    """Bit-exact comparison of every dispatch output, including untouched (canary) rows."""
+    """Bit-exact comparison of every dispatch output, including untouched (canary) rows and the guard tails."""
+    assert_guards(gout)
     gx = to_np(gout["recv_x"])
     if c.fp8:
         assert np.array_equal(gx, od["recv_x"]), _first_diff(gx, od["recv_x"])

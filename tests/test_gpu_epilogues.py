@@ -48,17 +48,15 @@ def test_dispatch_rows_parity(ep, fp8, zero_pad, N, K, El, A, H):
     h, _ = ep.ep_get_layout(tk.to(DEV), El, 1, 0, A)
     cap = h.recv_capacity
     G = 0 if scales is None else scales.shape[1]
-    out = dict(recv_x=torch.empty((cap, H), dtype=rows.dtype, device=DEV),
-               recv_x_scales=torch.empty((cap, G), dtype=torch.float32, device=DEV) if G else None,
-               recv_src_idx=torch.empty(cap, dtype=torch.int32, device=DEV),
-               recv_topk_weights=torch.empty(cap, dtype=torch.float32, device=DEV))
-    out["recv_x"].view(torch.uint8).fill_(0xA5)
-    _fill(out["recv_x_scales"], -3.0)
-    _fill(out["recv_src_idx"], -7)
-    _fill(out["recv_topk_weights"], -7.0)
+    out = Hn.fill_canaries(Hn.guard(dict(
+        recv_x=torch.empty((cap, H), dtype=rows.dtype, device=DEV),
+        recv_x_scales=torch.empty((cap, G), dtype=torch.float32, device=DEV) if G else None,
+        recv_src_idx=torch.empty(cap, dtype=torch.int32, device=DEV),
+        recv_topk_weights=torch.empty(cap, dtype=torch.float32, device=DEV))))
     ep.ep_dispatch_rows(h, rows.to(DEV), scales.to(DEV) if scales is not None else None, w.to(DEV),
                         do_zero_padding=zero_pad, out=out)
     torch.cuda.synchronize()
+    Hn.assert_guards(out)
     rows_u8 = rows.view(torch.uint8).numpy() if fp8 else rows.view(torch.int16).numpy().view(np.uint8).reshape(N, 2 * H)
     lay = O.layout(tk.numpy(), El, 1, 0, A)
     ref = O.dispatch_rows(rows_u8, scales.numpy() if scales is not None else None, tk.numpy(), w.numpy(), lay, El, A,
@@ -81,9 +79,11 @@ def test_combine_reduce_parity(ep, with_local, with_bias):
     partials = W.normal_bf16((R, T, H), g)
     local = W.normal_bf16((T, H), g) if with_local else None
     bias = W.normal_bf16((T, H), g, 0.1) if with_bias else None
-    out = ep.ep_combine_reduce(h, partials.to(DEV), local.to(DEV) if with_local else None,
-                               bias.to(DEV) if with_bias else None)
+    out, guard = Hn.guarded_tensor((T, H), torch.bfloat16, DEV)
+    ep.ep_combine_reduce(h, partials.to(DEV), local.to(DEV) if with_local else None,
+                         bias.to(DEV) if with_bias else None, out=out)
     torch.cuda.synchronize()
+    Hn.assert_guards(guard)
     lay = O.layout(inp["topk_idx"].numpy(), c.num_experts, R, c.rank, c.expert_alignment)
     ref = O.combine_reduce(W.bf16_bits(partials), lay["send_slot"], c.rank,
                            W.bf16_bits(local) if with_local else None, W.bf16_bits(bias) if with_bias else None)

@@ -85,8 +85,10 @@ def test_combine_parity_random_y(ep, name):
     y = W.random_expert_outputs(h.recv_capacity, c.hidden, seed=100 + W.ORDER.index(name), device=DEV)
     bias = inp["bias"].to(DEV) if inp["bias"] is not None else None
     w = inp["topk_weights"].to(DEV)
-    out = ep.ep_combine(h, y, w, bias)
+    out, guard = Hn.guarded_tensor((c.num_tokens, c.hidden), torch.bfloat16, DEV)
+    ep.ep_combine(h, y, w, bias, out=out)
     torch.cuda.synchronize()
+    Hn.assert_guards(guard)
     ref = O.combine(Hn.to_np(y), olay["slot"], inp["topk_weights"].numpy(),
                     W.bf16_bits(inp["bias"]) if inp["bias"] is not None else None)
     ok, mabs, mrel, nbad = Hn.combine_check(Hn.to_np(out), ref)
@@ -193,6 +195,79 @@ def test_quantizer_sweep_all_bf16(ep):
         assert np.array_equal(gs[t].view(np.uint32), s.view(np.uint32)), t
 
 
+def _quantize_on_gpu(ep, xb):
+    """FP8 dispatch of bf16 bits xb [T, H] with every token routed to one expert: row t of the output is token t."""
+    T = xb.shape[0]
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16)
+    idx = torch.zeros(T, 1, dtype=torch.int64)
+    h, _ = ep.ep_get_layout(idx.to(DEV), 1)
+    out = Hn.dispatch_outputs_with_canary(ep, h, xb.shape[1], True, DEV)
+    ep.ep_dispatch(h, x.to(DEV), None, fp8=True, out=out)
+    torch.cuda.synchronize()
+    Hn.assert_guards(out)
+    return Hn.to_np(out["recv_x"])[:T], Hn.to_np(out["recv_x_scales"])[:T]
+
+
+def test_quantizer_every_group_max(ep):
+    """Every finite positive bf16 value (0x0001..0x7F7F, 32,639 of them) as a 128-channel group maximum, each
+    heading 8 groups whose other 127 values are drawn from the bf16 codes between 0 and the maximum (magnitudes
+    log-uniform, random signs; the first group of each maximum also holds -max, +0 and -0): codes and scales
+    bit-equal to the oracle.  With the sweep above (every x under 15 maxima) this pins scale = amax / 448 and
+    inv = 448 / amax for every maximum and the cast of x * inv across each maximum's range (33.4 M values)."""
+    G_PER = 8
+    maxima = np.arange(0x0001, 0x7F80, dtype=np.uint16)
+    n = maxima.size * G_PER
+    m = np.repeat(maxima, G_PER)
+    rng = np.random.default_rng(20240607)
+    codes = np.minimum((rng.random((n, 127)) * (m[:, None].astype(np.float64) + 1)).astype(np.uint32), m[:, None])
+    signs = (rng.random((n, 127)) < 0.5).astype(np.uint32) << 15
+    groups = np.empty((n, 128), np.uint16)
+    groups[:, 0] = m
+    groups[:, 1:] = (codes | signs).astype(np.uint16)
+    groups[::G_PER, 1] = maxima | 0x8000
+    groups[::G_PER, 2] = 0x0000
+    groups[::G_PER, 3] = 0x8000
+    assert (np.abs(O.bf16_to_f32(groups)) <= O.bf16_to_f32(m)[:, None]).all()
+    H = 7168
+    flat = groups.reshape(-1)
+    T = -(-flat.size // H)
+    xb = np.zeros(T * H, np.uint16)
+    xb[: flat.size] = flat
+    xb = xb.reshape(T, H)
+    print("[quantizer] %d groups, %d tokens" % (n, T), flush=True)
+    gq, gs = _quantize_on_gpu(ep, xb)
+    q, sc = O.quantize_row(xb.reshape(-1))
+    q, sc = q.reshape(T, H), sc.reshape(T, H // 128)
+    assert np.array_equal(gs.view(np.uint32), sc.view(np.uint32)), Hn._first_diff(gs.view(np.uint32),
+                                                                                   sc.view(np.uint32))
+    assert np.array_equal(gq, q), Hn._first_diff(gq, q)
+
+
+def test_nonfinite_groups_do_not_disturb_others(ep):
+    """Non-finite x (NaN, +-inf) has no defined e4m3 code here: the codes and the scale of the 128-channel group
+    holding it are unspecified.  Every other group of the same token, every other token and everything past the
+    outputs stay as they would be (bit-equal to the oracle; guard tails intact)."""
+    T, H = 64, 7168
+    xb = W.bf16_bits(W.normal_bf16((T, H), torch.Generator().manual_seed(9))).copy()
+    planted = {(3, 5, 7): 0x7FC0,      # quiet NaN
+               (3, 6, 0): 0xFFC0,      # negative quiet NaN, next group
+               (10, 0, 0): 0x7F80,     # +inf, first group
+               (20, 55, 127): 0xFF80,  # -inf, last group, last channel
+               (40, 12, 64): 0x7F81,   # signalling NaN
+               (41, 30, 1): 0x7F80}
+    for (t, g, c), v in planted.items():
+        xb[t, 128 * g + c] = v
+    gq, gs = _quantize_on_gpu(ep, xb)
+    q, sc = O.quantize_row(xb.reshape(-1))
+    q, sc = q.reshape(T, H // 128, 128), sc.reshape(T, H // 128)
+    gq = gq.reshape(T, H // 128, 128)
+    keep = np.ones((T, H // 128), bool)
+    for (t, g, _c) in planted:
+        keep[t, g] = False
+    assert np.array_equal(gq[keep], q[keep])
+    assert np.array_equal(gs[keep].view(np.uint32), sc[keep].view(np.uint32))
+
+
 # ---- edge cases -----------------------------------------------------------------------------------------
 
 EDGE = [
@@ -250,7 +325,10 @@ def test_edge_cases(ep, case):
     Hn.assert_dispatch_equal(gout, od, cfg)
     y = W.random_expert_outputs(h.recv_capacity, H, seed=T, device=DEV)
     bias = W.normal_bf16((T, H), torch.Generator().manual_seed(1), 0.1)
-    out = ep.ep_combine(h, y, w.to(DEV), bias.to(DEV))
+    out, guard = Hn.guarded_tensor((T, H), torch.bfloat16, DEV)
+    ep.ep_combine(h, y, w.to(DEV), bias.to(DEV), out=out)
+    torch.cuda.synchronize()
+    Hn.assert_guards(guard)
     ref = O.combine(Hn.to_np(y), olay["slot"], w.numpy(), W.bf16_bits(bias))
     ok, mabs, mrel, nbad = Hn.combine_check(Hn.to_np(out), ref)
     assert ok, (mabs, mrel, nbad)
