@@ -5,24 +5,29 @@ with zero padding (one ep_layout_dispatch call, whose layout kernels also read t
 dispatch), then the weighted BF16 combine (4096 tokens, hidden 7168, 256 experts in 8 groups with group-limited
 top-4-group / top-8 routing, alignment 128).  Inputs and expert outputs are resident in HBM before timing
 starts.  W untimed warm-up steps, then exactly K timed steps bracketed by device syncs; the host enqueues the
-calls of a step (~35 us of host time) far faster than the GPU runs them (~175 us), so no step waits on the
-host.  The same step captured in a HIP graph and replayed K times is reported too
-(`step_graph_replay_us`): each replay adds a few microseconds of GPU-side overhead that a graph of a whole
-model pass would spread over many more kernels.  Each call's average duration comes from HIP events on the
-launch stream around K back-to-back launches of that call, enqueued by the host ahead of the GPU.
+calls of a step far faster than the GPU runs them, so no step waits on the host.  The same step captured in a
+HIP graph and replayed K times is reported too (`step_graph_replay_us`).
+
+Per call, two timings:
+  * back to back: HIP events on the launch stream around K back-to-back launches of the call;
+  * flushed (the pages' method: a cache flush -- a 2 GiB read sweep -- before every sample, 10 warm-up + 50
+    samples): each sample's kernels timed by their GPU start/end timestamps from a kernel trace (torch's
+    profiler), so nothing is inserted between a flush and the call after it.  Median and min.
 
 Prints one JSON line.  `value` is the step's effective HBM throughput: the algorithmic bytes of layout +
 dispatch + combine per step divided by the measured step time.  Algorithmic bytes are what the method must
 move: every token row read once, every routed row written once, padding rows when zero padding is requested,
-the expert rows gathered once by combine and the output written once (the byte model is in
-bytes_model()).  Two extra objects: `roofline` for the dominant kernel and `cpu_baseline` (the oracle timed
-on the host).
+the expert rows gathered once by combine and the output written once (bytes_model()).  `roofline` is for the
+dominant kernel, `cpu_baseline` the oracle timed on the host (one pinned core, and all cores over token
+ranges).  `workloads` has every workload (tiny, decode, prefill, ep8, skewed) measured the same way;
+`dispatch_bound` times the prefill dispatch's write stream and read stream on their own (bench_probe.hip).
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--flush-samples 50] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -35,7 +40,10 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0        # MI355X published HBM3E peak
 WORKLOAD = "prefill"
+ALL_WORKLOADS = ("tiny", "decode", "prefill", "ep8", "skewed")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill.json")
+PROBE_LIB = os.path.join(ROOT, "libbench_probe.so")
+FLUSH_BYTES = 2 << 30         # the flush reads 2 GiB: more than the memory-side cache and every L2
 # the source files each kernel is compiled from (their hash marks counter figures taken from an older kernel)
 KERNEL_SOURCES = {
     "k_dispatch_fp8": ("ep_dispatch.hip", "ep_dispatch_core.hpp", "ep_device.hpp"),
@@ -49,8 +57,6 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--flush-samples", type=int, default=50,
-                    help="per-kernel samples with a cache flush before each (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before the steps (counter calibration)")
@@ -58,11 +64,15 @@ def parse():
     ap.add_argument("--no-epilogues", dest="epilogues", action="store_false",
                     help="skip the receiver-placement / source-reduce measurement at the EP8 shapes")
     ap.add_argument("--no-workloads", dest="workloads", action="store_false",
-                    help="skip the per-call summary of the other workloads (tiny, decode, ep8, skewed)")
+                    help="skip the per-call table of the other workloads (tiny, decode, ep8, skewed)")
     ap.add_argument("--no-copy-ceiling", dest="copy_ceiling", action="store_false",
                     help="skip the timed plain device copy reported as context")
     ap.add_argument("--no-decode", dest="decode", action="store_false",
                     help="skip the decode-shape comparison of the one-launch layout + dispatch")
+    ap.add_argument("--no-flushed", dest="flushed", action="store_false",
+                    help="skip the flushed (pages' method) timings")
+    ap.add_argument("--no-bound", dest="bound", action="store_false",
+                    help="skip the dispatch write-stream / read-stream probes")
     return ap.parse_args()
 
 
@@ -116,31 +126,43 @@ def host_cpu_model():
     return "unknown"
 
 
+# ---- the oracle on the host (cpu_baseline) -----------------------------------------------------------------
+
 def cpu_baseline(inp, y_bits, cfg):
-    """The oracle as it stands (single thread, plain C) on the full workload, pinned to one host core, repeated
-    until about 10 s of CPU time have been spent (at least 3 runs); the median run is reported."""
+    """The oracle as it stands on the full workload.  (i) One thread pinned to one host core: layout, dispatch
+    and combine, repeated until about 10 s of CPU time (at least 3 runs), the median run.  (ii) All the host
+    cores this process may use: the layout once (serial), then the same C dispatch and combine functions over
+    contiguous token ranges, one thread per core (the calls release the GIL); zero padding is written by the
+    first range only, so every row is written once; the median of 3 runs."""
     import numpy as np
 
     import oracle as O
     import workloads as W
 
-    idx = inp["topk_idx"].numpy()
-    w = inp["topk_weights"].numpy()
-    x = W.bf16_bits(inp["x"])
+    idx = np.ascontiguousarray(inp["topk_idx"].numpy())
+    w = np.ascontiguousarray(inp["topk_weights"].numpy())
+    x = np.ascontiguousarray(W.bf16_bits(inp["x"]))
     bias = W.bf16_bits(inp["bias"]) if inp["bias"] is not None else None
     allowed = sorted(os.sched_getaffinity(0))
     core = allowed[0]
-    os.sched_setaffinity(0, {core})
-    times = []
-    while len(times) < 3 or sum(times) < 10.0:
-        t0 = time.perf_counter()
+    El = cfg.num_experts // cfg.num_ranks
+
+    def one_pass():
         lay = O.layout(idx, cfg.num_experts, cfg.num_ranks, cfg.rank, cfg.expert_alignment)
         O.dispatch(x, idx, w, lay, cfg.num_experts, cfg.num_ranks, cfg.rank, cfg.expert_alignment, fp8=cfg.fp8,
                    zero_pad=cfg.zero_padding, recv_fill=None)
         O.combine(y_bits, lay["slot"], w, bias)
-        times.append(time.perf_counter() - t0)
-    os.sched_setaffinity(0, set(allowed))
-    El = cfg.num_experts // cfg.num_ranks
+        return lay
+
+    os.sched_setaffinity(0, {core})
+    times = []
+    try:
+        while len(times) < 3 or sum(times) < 10.0:
+            t0 = time.perf_counter()
+            lay = one_pass()
+            times.append(time.perf_counter() - t0)
+    finally:
+        os.sched_setaffinity(0, set(allowed))
     cnt = lay["cnt"][cfg.rank * El:(cfg.rank + 1) * El]
     V = int(cnt.sum())
     counts = dict(V=V, P=int(lay["psum"][-1]) - V, N_send=int(sum(lay["ntok_rank"][r] for r in range(cfg.num_ranks)
@@ -148,17 +170,356 @@ def cpu_baseline(inp, y_bits, cfg):
     bm = bytes_model(cfg, counts)
     total = bm["layout"] + bm["dispatch"] + bm["combine"]
     med = float(np.median(times))
-    return dict(value=round(total / med / 1e9, 3), unit="GB/s", cores=1, kind="oracle",
-                sample="full %s workload (layout + FP8 dispatch + combine), median of %d runs, %.2f s each"
-                       % (cfg.name, len(times), med),
-                pinned_core=core, host_cores_available=len(allowed), host_cpu=host_cpu_model())
 
+    # (ii) all cores: token ranges
+    ncores = len(allowed)
+    if cfg.num_ranks == 1:
+        runs = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            _, t_lay = oracle_token_ranges(x, idx, w, y_bits, bias, cfg, ncores)
+            runs.append((t_lay, time.perf_counter() - t0))
+        med_all = sorted(b for _, b in runs)[1]
+        all_cores = dict(value=round(total / med_all / 1e9, 3), unit="GB/s", cores=ncores, kind="oracle",
+                         sample="full %s workload, layout serial (%.2f ms) then dispatch + combine over %d token "
+                                "ranges on %d threads; median of 3 runs, %.3f s each"
+                                % (cfg.name, 1e3 * float(np.median([a for a, _ in runs])), ncores, ncores, med_all))
+    else:
+        all_cores = None
+    return dict(value=round(total / med / 1e9, 3), unit="GB/s", cores=1, kind="oracle",
+                sample="full %s workload (layout + FP8 dispatch + combine), one thread pinned to one core, median "
+                       "of %d runs, %.2f s each" % (cfg.name, len(times), med),
+                pinned_core=core, host_cores_available=len(allowed), host_cpu=host_cpu_model(),
+                all_cores=all_cores)
+
+
+def oracle_token_ranges(x, idx, w, y_bits, bias, cfg, ncores):
+    """The oracle's layout (serial), then its C dispatch and combine functions over `ncores` contiguous token
+    ranges, one thread each (ctypes releases the GIL inside the calls).  One rank only (the send windows' rows
+    depend on the whole batch).  Zero padding is written by the first range only, so every row is written
+    once.  Returns (dict of outputs, layout seconds)."""
+    import concurrent.futures
+
+    import numpy as np
+
+    import oracle as O
+
+    assert cfg.num_ranks == 1
+    lib, P = O._load(), O._ptr
+    T, H, K = cfg.num_tokens, cfg.hidden, cfg.num_topk
+    G = H // 128 if cfg.fp8 else 0
+    rowb = H if cfg.fp8 else 2 * H
+    t0 = time.perf_counter()
+    lay = O.layout(idx, cfg.num_experts, 1, 0, cfg.expert_alignment)
+    t_lay = time.perf_counter() - t0
+    cap = lay["cap"]
+    o = dict(recv_x=np.zeros((cap, rowb), np.uint8), recv_scales=np.zeros((cap, max(G, 1)), np.float32),
+             recv_src=np.full(cap, -7, np.int32), recv_w=np.full(cap, -7.0, np.float32),
+             out=np.empty((T, H), np.float64), lay=lay)
+    slot = lay["slot"]
+    bounds = [(T * i // ncores, T * (i + 1) // ncores) for i in range(ncores)]
+
+    def part(i):
+        a, b = bounds[i]
+        if b <= a and not (i == 0 and cfg.zero_padding):
+            return
+        rc = lib.oracle_dispatch(P(x[a:b]), b - a, H, K, P(w[a:b]), P(idx[a:b]), cfg.num_experts, 1, 0,
+                                 cfg.expert_alignment, int(cfg.fp8), int(cfg.zero_padding and i == 0), 1,
+                                 P(lay["cnt"]), P(lay["psum"]), P(slot[a:b]), P(lay["send_slot"][a:b]),
+                                 P(o["recv_x"]), P(o["recv_scales"]) if G else None, P(o["recv_src"]),
+                                 P(o["recv_w"]), None, None, None, None, None, None)
+        if rc != 0:
+            raise ValueError("oracle_dispatch rejected a token range")
+        if a > 0:   # the call numbers its tokens from the start of its range
+            rows = slot[a:b].ravel()
+            o["recv_src"][rows[rows >= 0]] += a
+        lib.oracle_combine(P(y_bits), H, P(slot[a:b]), P(w[a:b]), b - a, K,
+                           P(bias[a:b]) if bias is not None else None, P(o["out"][a:b]))
+
+    with concurrent.futures.ThreadPoolExecutor(ncores) as ex:
+        list(ex.map(part, range(ncores)))
+    return o, t_lay
+
+
+# ---- GPU timing helpers -------------------------------------------------------------------------------------
+
+class Probe:
+    """bench_probe.hip: the flush used between flushed samples and the dispatch's write-stream / read-stream
+    probes.  Launches go to torch's current stream."""
+
+    def __init__(self, dev):
+        import torch
+        if not os.path.exists(PROBE_LIB):
+            raise RuntimeError("libbench_probe.so is not built: run __graft_entry__.build()")
+        self.lib = ctypes.CDLL(PROBE_LIB)
+        Pt, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+        self.lib.probe_flush.restype = I
+        self.lib.probe_flush.argtypes = [Pt, I64, Pt, Pt]
+        self.lib.probe_dispatch_writes.restype = I
+        self.lib.probe_dispatch_writes.argtypes = [Pt, I, I, Pt, I, Pt, Pt, Pt, Pt, I, Pt]
+        self.lib.probe_dispatch_reads.restype = I
+        self.lib.probe_dispatch_reads.argtypes = [Pt, Pt, I, I, I, Pt, Pt]
+        self.junk = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev).fill_(3)
+        self.sink = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    @staticmethod
+    def _stream():
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+
+    def flush(self):
+        rc = self.lib.probe_flush(self.junk.data_ptr(), self.junk.numel(), self.sink.data_ptr(), self._stream())
+        if rc != 0:
+            raise RuntimeError("probe_flush failed (%d)" % rc)
+
+
+def events_us(fn, n):
+    """Average µs of fn over n back-to-back calls, HIP events on the launch stream around them (the GPU first spins
+    ~20 ms so that the host enqueues every call before the first runs)."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2.4e9 * 0.02))
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
+def flushed_us(fn, probe, warmup=10, samples=50):
+    """The pages' method: a cache flush before every sample, 10 warm-up samples, then 50 timed ones, each timed
+    by the GPU's own start and end timestamps of its kernels from a kernel trace (torch's profiler, which
+    records every kernel dispatched in the process), so nothing is inserted between a flush and the call after
+    it.  A sample's time is the sum of its kernels' durations (the gaps between a call's own kernels, a launch
+    gap each, are not in it).  Returns (median, min) in µs."""
+    import numpy as np
+    import torch
+    from torch.profiler import ProfilerActivity, profile
+
+    for _ in range(warmup):
+        probe.flush()
+        fn()
+    torch.cuda.synchronize()
+    with profile(activities=[ProfilerActivity.CUDA]) as prof:
+        for _ in range(samples):
+            probe.flush()
+            fn()
+        torch.cuda.synchronize()
+    evs = sorted((e for e in prof.events() if e.device_type == torch.autograd.DeviceType.CUDA),
+                 key=lambda e: e.time_range.start)
+    per = []
+    for e in evs:
+        if "k_probe_flush" in e.name:
+            per.append(0.0)
+        elif per:
+            per[-1] += e.time_range.end - e.time_range.start
+    if len(per) != samples or min(per) <= 0.0:
+        raise RuntimeError("flushed timing: %d samples traced, expected %d" % (len(per), samples))
+    return float(np.median(per)), float(np.min(per))
+
+
+def rate(b, us):
+    return b / (us * 1e-6) / 1e9
+
+
+def progress(msg):
+    print("[bench] %s" % msg, file=sys.stderr, flush=True)
+
+
+# ---- per-workload table -------------------------------------------------------------------------------------
+
+def measure_workload(ep, W, dev, name, n, probe, flushed=True):
+    """One workload measured per call (layout, dispatch, combine, layout + dispatch as two calls and as one call):
+    back to back and flushed; algorithmic bytes and GB/s against the median; tokens/s = T / median; padding
+    amplification A_pad (rows used / valid rows) and max / mean rows per local expert; and the eager step
+    (one-call layout + dispatch, then combine), the median of five blocks of n steps between device syncs."""
+    import numpy as np
+    import torch
+
+    inp = W.make_inputs(name)
+    cfg = inp["cfg"]
+    T, K, E, R, A = cfg.num_tokens, cfg.num_topk, cfg.num_experts, cfg.num_ranks, cfg.expert_alignment
+    idx = inp["topk_idx"].to(dev)
+    w = inp["topk_weights"].to(dev)
+    x = inp["x"].to(dev)
+    bias = inp["bias"].to(dev) if inp["bias"] is not None else None
+    ws = torch.empty(ep.ep_layout_workspace_bytes(T, K, E, R, A), dtype=torch.uint8, device=dev)
+    lay = dict(num_tokens_per_rank=torch.empty(R, dtype=torch.int32, device=dev),
+               num_tokens_per_expert=torch.empty(E, dtype=torch.int32, device=dev),
+               is_token_in_rank=torch.empty((T, R), dtype=torch.uint8, device=dev),
+               psum_num_recv_tokens_per_expert=torch.empty(E // R + 1, dtype=torch.int32, device=dev),
+               num_invalid_topk=torch.empty(1, dtype=torch.int32, device=dev))
+    h, _ = ep.ep_get_layout(idx, E, R, cfg.rank, A, workspace=ws, outputs=lay)
+    dout = ep.alloc_dispatch_outputs(h, cfg.hidden, cfg.fp8, device=dev)
+    y = W.random_expert_outputs(h.recv_capacity, cfg.hidden, seed=1234, device=dev)
+    res = torch.empty((T, cfg.hidden), dtype=torch.bfloat16, device=dev)
+
+    calls = {
+        "layout": lambda: ep.ep_get_layout(idx, E, R, cfg.rank, A, workspace=ws, outputs=lay),
+        "dispatch": lambda: ep.ep_dispatch(h, x, w, fp8=cfg.fp8, do_zero_padding=cfg.zero_padding, out=dout),
+        "combine": lambda: ep.ep_combine(h, y, w, bias, out=res),
+    }
+
+    def two_calls():
+        hh, _ = ep.ep_get_layout(idx, E, R, cfg.rank, A, workspace=ws, outputs=lay)
+        ep.ep_dispatch(hh, x, w, fp8=cfg.fp8, do_zero_padding=cfg.zero_padding, out=dout)
+
+    def one_call():
+        ep.ep_layout_dispatch(idx, x, E, R, cfg.rank, A, w, fp8=cfg.fp8, do_zero_padding=cfg.zero_padding,
+                              out=dout, workspace=ws, outputs=lay)
+
+    calls["layout_then_dispatch"] = two_calls
+    calls["layout_dispatch_one_call"] = one_call
+
+    def step():
+        hs, _, _ = ep.ep_layout_dispatch(idx, x, E, R, cfg.rank, A, w, fp8=cfg.fp8,
+                                         do_zero_padding=cfg.zero_padding, out=dout, workspace=ws, outputs=lay)
+        ep.ep_combine(hs, y, w, bias, out=res)
+
+    for fn in calls.values():
+        fn()
+    torch.cuda.synchronize()
+    cnt = lay["num_tokens_per_expert"].cpu().numpy()
+    psum = lay["psum_num_recv_tokens_per_expert"].cpu().numpy()
+    ntr = lay["num_tokens_per_rank"].cpu().numpy()
+    El = E // R
+    cl = cnt[cfg.rank * El:(cfg.rank + 1) * El]
+    V = int(cl.sum())
+    counts = dict(V=V, P=int(psum[-1]) - V, N_send=int(sum(ntr[r] for r in range(R) if r != cfg.rank)))
+    bm = bytes_model(cfg, counts)
+    bm["layout_then_dispatch"] = bm["layout"] + bm["dispatch"]
+    bm["layout_dispatch_one_call"] = bm["layout_then_dispatch"]
+
+    out = dict(workload=describe(cfg), tokens=T, valid_rows=V, pad_rows=counts["P"], send_rows=counts["N_send"],
+               A_pad=round(int(psum[-1]) / max(V, 1), 4),
+               max_mean_rows_per_expert=[int(cl.max()), round(float(cl.mean()), 2)], calls={})
+    for k, fn in calls.items():
+        us = events_us(fn, n)
+        c = dict(us=round(us, 2), bytes=bm[k])
+        if flushed:
+            fmed, fmin = flushed_us(fn, probe)
+            c.update(us_flushed_median=round(fmed, 2), us_flushed_min=round(fmin, 2))
+        ref = c.get("us_flushed_median", us)
+        c["tokens_per_s"] = round(T / (ref * 1e-6), 1)
+        if k != "layout":
+            c["GBps"] = round(rate(bm[k], us), 1)
+            c["pct_peak"] = round(100 * rate(bm[k], us) / HBM_PEAK_GBPS, 1)
+            if flushed:
+                c["GBps_flushed"] = round(rate(bm[k], c["us_flushed_median"]), 1)
+                c["pct_peak_flushed"] = round(100 * rate(bm[k], c["us_flushed_median"]) / HBM_PEAK_GBPS, 1)
+        out["calls"][k] = c
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    blocks = []
+    for _ in range(5):
+        t0 = time.perf_counter()
+        for _ in range(n):
+            step()
+        torch.cuda.synchronize()
+        blocks.append((time.perf_counter() - t0) * 1e6 / n)
+    step_us = float(np.median(blocks))
+    out["step_us"] = round(step_us, 2)
+    out["step_GBps"] = round(rate(bm["layout"] + bm["dispatch"] + bm["combine"], step_us), 1)
+    h.free()
+    del ws, lay, dout, y, res, idx, w, x, bias
+    torch.cuda.empty_cache()
+    return out
+
+
+def describe(cfg):
+    return ("%s: %d tok x hidden %d, %d experts%s, top-%d, %s dispatch%s, BF16 combine%s, alignment %d%s" % (
+        cfg.name, cfg.num_tokens, cfg.hidden, cfg.num_experts,
+        " (8 groups, top-4 groups)" if cfg.routing == "grouped" else
+        (" (Zipf %.1f)" % cfg.zipf_s if cfg.routing == "zipf" else ""), cfg.num_topk,
+        "FP8 e4m3 per-128" if cfg.fp8 else "BF16", " + zero padding" if cfg.zero_padding else "",
+        " + bias" if cfg.bias else "", cfg.expert_alignment,
+        ", %d ranks (rank %d), %d send windows" % (cfg.num_ranks, cfg.rank, cfg.num_ranks - 1)
+        if cfg.num_ranks > 1 else ""))
+
+
+# ---- the prefill dispatch's write stream and read stream on their own ---------------------------------------
+
+def measure_dispatch_bound(ep, W, dev, n, probe):
+    """The FP8 dispatch with zero padding on the prefill workload, taken apart:
+    * the dispatch's stores alone (probe_dispatch_writes: the same destination rows, scales, row metadata and
+      padding rows, in the same work split, no reads) and its source reads alone (probe_dispatch_reads: the
+      token rows and the slot map, no stores).  Reads and writes share each HBM channel's data bus, so their
+      sum bounds the dispatch from below;
+    * the product dispatch without zero padding (routed rows only) and with alignment 1 (no padding rows at
+      all), and the increment that zero padding adds."""
+    import numpy as np
+    import torch
+
+    inp = W.make_inputs("prefill")
+    cfg = inp["cfg"]
+    T, K, E, A, H = cfg.num_tokens, cfg.num_topk, cfg.num_experts, cfg.expert_alignment, cfg.hidden
+    G = H // 128
+    idx, w, x = inp["topk_idx"].to(dev), inp["topk_weights"].to(dev), inp["x"].to(dev)
+    h, lay = ep.ep_get_layout(idx, E, 1, 0, A)
+    d = ep.ep_dispatch(h, x, w, fp8=True, do_zero_padding=True)
+    torch.cuda.synchronize()
+    src = d["recv_src_idx"].cpu().numpy()
+    used = int(lay["psum_num_recv_tokens_per_expert"][-1].item())
+    rows = np.nonzero(src[:used] >= 0)[0]
+    pads = np.nonzero(src[:used] < 0)[0].astype(np.int32)
+    toks = src[rows]
+    order = np.lexsort((rows, toks))
+    token_rows = np.full((T, K), -1, np.int32)
+    kpos = np.zeros(T, np.int64)
+    for r, t in zip(rows[order], toks[order]):
+        token_rows[t, kpos[t]] = r
+        kpos[t] += 1
+    tr = torch.from_numpy(token_rows).to(dev)
+    pr = torch.from_numpy(pads).to(dev) if pads.size else torch.zeros(1, dtype=torch.int32, device=dev)
+    lib, stream = probe.lib, probe._stream
+
+    def writes():
+        rc = lib.probe_dispatch_writes(tr.data_ptr(), T, K, pr.data_ptr(), int(pads.size), d["recv_x"].data_ptr(),
+                                       d["recv_x_scales"].data_ptr(), d["recv_src_idx"].data_ptr(),
+                                       d["recv_topk_weights"].data_ptr(), H, stream())
+        assert rc == 0, rc
+
+    def reads():
+        rc = lib.probe_dispatch_reads(x.data_ptr(), tr.data_ptr(), T, K, H, probe.sink.data_ptr(), stream())
+        assert rc == 0, rc
+
+    V, P = rows.size, pads.size
+    wbytes = (V + P) * (H + 4 * G + 8)
+    rbytes = T * 2 * H + T * K * 4
+    full = lambda: ep.ep_dispatch(h, x, w, fp8=True, do_zero_padding=True, out=d)
+    routed = lambda: ep.ep_dispatch(h, x, w, fp8=True, do_zero_padding=False, out=d)
+    h1, _ = ep.ep_get_layout(idx, E, 1, 0, 1)
+    d1 = ep.ep_dispatch(h1, x, w, fp8=True)
+    no_pad = lambda: ep.ep_dispatch(h1, x, w, fp8=True, out=d1)
+    us = {k: events_us(f, n) for k, f in (("writes", writes), ("reads", reads), ("dispatch", full),
+                                          ("routed_only", routed), ("alignment_1", no_pad))}
+    bm = bytes_model(cfg, dict(V=V, P=P, N_send=0))
+    s = us["writes"] + us["reads"]
+    pad_bytes = P * (H + 4 * G)
+    h.free()
+    h1.free()
+    return dict(
+        note="prefill FP8 dispatch with zero padding: its stores alone and its source reads alone "
+             "(bench_probe.hip, same destination rows and work split), back to back, events",
+        write_only_us=round(us["writes"], 2), write_bytes=wbytes, write_only_GBps=round(rate(wbytes, us["writes"]), 1),
+        read_only_us=round(us["reads"], 2), read_bytes=rbytes, read_only_GBps=round(rate(rbytes, us["reads"]), 1),
+        sum_us=round(s, 2), dispatch_us=round(us["dispatch"], 2), dispatch_bytes=bm["dispatch"],
+        bound_GBps=round(rate(bm["dispatch"], s), 1),
+        bound_pct_peak=round(100 * rate(bm["dispatch"], s) / HBM_PEAK_GBPS, 1),
+        routed_only_us=round(us["routed_only"], 2), alignment_1_us=round(us["alignment_1"], 2),
+        zero_padding_increment_us=round(us["dispatch"] - us["routed_only"], 2),
+        zero_padding_increment_GBps=round(rate(pad_bytes, max(us["dispatch"] - us["routed_only"], 1e-3)), 1))
+
+
+# ---- context measurements -----------------------------------------------------------------------------------
 
 def measure_epilogues(ep, W, dev, n):
     """Receiver-side placement and source-side reduce at the EP8 shapes: rank 0 (experts 0..31 of 256) receiving
     the rows of 7 other ranks of 4096 tokens each (top-8 uniform routing, FP8 rows + 56 scales, alignment 128),
     and the reduce of 8 returned windows of 4096 x 7168 BF16 rows with the local part and a bias."""
-    import numpy as np
     import torch
 
     cfg = W.CONFIGS["ep8"]
@@ -188,19 +549,7 @@ def measure_epilogues(ep, W, dev, n):
     V = int(cnt.sum())
     P = int(lr["psum_num_recv_tokens_per_expert"][-1].item()) - V
     row_b = H + 4 * G
-
-    def timed(fn):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        torch.cuda._sleep(int(2.4e9 * 0.02))
-        e0.record()
-        for _ in range(n):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n
-
-    t_rows = timed(lambda: ep.ep_dispatch_rows(hr, rows, sc, tw, do_zero_padding=False, out=out))
+    t_rows = events_us(lambda: ep.ep_dispatch_rows(hr, rows, sc, tw, do_zero_padding=False, out=out), n)
     b_rows = n_valid * row_b + R * T * K * 12 + V * (row_b + 8) + P * 8
 
     inp = W.make_inputs("ep8")
@@ -209,14 +558,16 @@ def measure_epilogues(ep, W, dev, n):
     local = W.random_expert_outputs(T, H, seed=4, device=dev)
     bias = W.random_expert_outputs(T, H, seed=5, device=dev)
     red = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    t_red = timed(lambda: ep.ep_combine_reduce(h0, parts, local, bias, out=red))
+    t_red = events_us(lambda: ep.ep_combine_reduce(h0, parts, local, bias, out=red), n)
     ntr = l0["num_tokens_per_rank"].cpu().numpy()
     n_part = int(sum(ntr[r] for r in range(1, R)))
     b_red = n_part * 2 * H + 3 * T * 2 * H + T * R * 4
+    hr.free()
+    h0.free()
     return dict(
-        dispatch_rows=dict(us=round(t_rows * 1e3, 2), bytes=b_rows, GBps=round(b_rows / (t_rows * 1e-3) / 1e9, 1),
+        dispatch_rows=dict(us=round(t_rows, 2), bytes=b_rows, GBps=round(rate(b_rows, t_rows), 1),
                            received_rows=n_valid, placed_rows=V),
-        combine_reduce=dict(us=round(t_red * 1e3, 2), bytes=b_red, GBps=round(b_red / (t_red * 1e-3) / 1e9, 1),
+        combine_reduce=dict(us=round(t_red, 2), bytes=b_red, GBps=round(rate(b_red, t_red), 1),
                             partial_rows=n_part))
 
 
@@ -230,111 +581,18 @@ def measure_copy_ceiling(dev, n, mib=1024):
     b = torch.empty_like(a)
     for _ in range(3):
         b.copy_(a)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(n):
-        b.copy_(a)
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / n
+    us = events_us(lambda: b.copy_(a), n)
     del a, b
-    return dict(bytes_per_copy=2 * (mib << 20), us=round(us, 2), GBps=round(2 * (mib << 20) / (us * 1e-6) / 1e9, 1),
+    return dict(bytes_per_copy=2 * (mib << 20), us=round(us, 2), GBps=round(rate(2 * (mib << 20), us), 1),
                 note="device copy of %d MiB (read + write bytes), events around %d copies" % (mib, n))
-
-
-def measure_workloads(ep, W, dev, names, n):
-    """The other workloads at a glance, measured like the headline one: per call, HIP events around n back-to-back
-    launches; the step (one-call layout + dispatch, then combine), the median of five blocks of n eager steps
-    between device syncs, host clock; algorithmic bytes from the byte model with the device counts.  Parity for
-    each is in the test suite."""
-    import time
-
-    import numpy as np
-    import torch
-
-    out = {}
-    for name in names:
-        inp = W.make_inputs(name)
-        cfg = inp["cfg"]
-        T, K, E, R, A = cfg.num_tokens, cfg.num_topk, cfg.num_experts, cfg.num_ranks, cfg.expert_alignment
-        idx = inp["topk_idx"].to(dev)
-        w = inp["topk_weights"].to(dev)
-        x = inp["x"].to(dev)
-        bias = inp["bias"].to(dev) if inp["bias"] is not None else None
-        ws = torch.empty(ep.ep_layout_workspace_bytes(T, K, E, R, A), dtype=torch.uint8, device=dev)
-        lay = dict(num_tokens_per_rank=torch.empty(R, dtype=torch.int32, device=dev),
-                   num_tokens_per_expert=torch.empty(E, dtype=torch.int32, device=dev),
-                   is_token_in_rank=torch.empty((T, R), dtype=torch.uint8, device=dev),
-                   psum_num_recv_tokens_per_expert=torch.empty(E // R + 1, dtype=torch.int32, device=dev),
-                   num_invalid_topk=torch.empty(1, dtype=torch.int32, device=dev))
-        h, _ = ep.ep_get_layout(idx, E, R, cfg.rank, A, workspace=ws, outputs=lay)
-        dout = ep.alloc_dispatch_outputs(h, cfg.hidden, cfg.fp8, device=dev)
-        y = W.random_expert_outputs(h.recv_capacity, cfg.hidden, seed=1234, device=dev)
-        res = torch.empty((T, cfg.hidden), dtype=torch.bfloat16, device=dev)
-
-        def timed(fn):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            torch.cuda._sleep(int(2.4e9 * 0.02))
-            e0.record()
-            for _ in range(n):
-                fn()
-            e1.record()
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1) * 1e3 / n
-
-        def step():
-            hs, _, _ = ep.ep_layout_dispatch(idx, x, E, R, cfg.rank, A, w, fp8=cfg.fp8,
-                                             do_zero_padding=cfg.zero_padding, out=dout, workspace=ws, outputs=lay)
-            ep.ep_combine(hs, y, w, bias, out=res)
-
-        us = dict(layout=timed(lambda: ep.ep_get_layout(idx, E, R, cfg.rank, A, workspace=ws, outputs=lay)),
-                  dispatch=timed(lambda: ep.ep_dispatch(h, x, w, fp8=cfg.fp8, do_zero_padding=cfg.zero_padding,
-                                                        out=dout)),
-                  combine=timed(lambda: ep.ep_combine(h, y, w, bias, out=res)))
-        for _ in range(3):
-            step()
-        torch.cuda.synchronize()
-        # five blocks of n steps between device syncs, host clock; the median block, so that one stall of the
-        # host (these steps are short, and for tiny and decode bound by the host's enqueue) does not set it
-        blocks = []
-        for _ in range(5):
-            t0 = time.perf_counter()
-            for _ in range(n):
-                step()
-            torch.cuda.synchronize()
-            blocks.append((time.perf_counter() - t0) * 1e6 / n)
-        step_us = float(np.median(blocks))
-        cnt = lay["num_tokens_per_expert"].cpu().numpy()
-        psum = lay["psum_num_recv_tokens_per_expert"].cpu().numpy()
-        ntr = lay["num_tokens_per_rank"].cpu().numpy()
-        El = E // R
-        V = int(cnt[cfg.rank * El:(cfg.rank + 1) * El].sum())
-        bm = bytes_model(cfg, dict(V=V, P=int(psum[-1]) - V,
-                                   N_send=int(sum(ntr[r] for r in range(R) if r != cfg.rank))))
-        rate = lambda b, u: b / (u * 1e-6) / 1e9
-        out[name] = dict(
-            layout_us=round(us["layout"], 2), dispatch_us=round(us["dispatch"], 2),
-            dispatch_GBps=round(rate(bm["dispatch"], us["dispatch"]), 1),
-            dispatch_pct_peak=round(100 * rate(bm["dispatch"], us["dispatch"]) / HBM_PEAK_GBPS, 1),
-            combine_us=round(us["combine"], 2), combine_GBps=round(rate(bm["combine"], us["combine"]), 1),
-            combine_pct_peak=round(100 * rate(bm["combine"], us["combine"]) / HBM_PEAK_GBPS, 1),
-            step_us=round(step_us, 2),
-            step_GBps=round(rate(bm["layout"] + bm["dispatch"] + bm["combine"], step_us), 1))
-        h.free()
-        del ws, lay, dout, y, res, idx, w, x, bias
-        torch.cuda.empty_cache()
-    return out
 
 
 def measure_decode(ep, W, dev, n):
     """The decode shape (128 tokens x 7168, 256 experts, top-8, FP8, alignment 128, no zero padding): layout +
-    dispatch as two calls (ep_get_layout, ep_dispatch: two launches) and as one (ep_layout_dispatch: one
-    launch), each timed as n back-to-back calls between HIP events; and the whole step (layout, dispatch,
-    combine) captured in a HIP graph both ways, timed over n replays."""
-    import time
-
+    dispatch as two calls (two launches) and as one (ep_layout_dispatch: one launch), each timed as n back-to-back
+    calls between HIP events; and the whole step (layout, dispatch, combine) captured in a HIP graph both ways:
+    a graph of 20 consecutive steps, timed over its replays (one replay per step would time the host's replay
+    cost, not the GPU)."""
     import torch
 
     inp = W.make_inputs("decode")
@@ -361,20 +619,7 @@ def measure_decode(ep, W, dev, n):
         h, _, _ = ep.ep_layout_dispatch(idx, x, E, 1, 0, A, w, fp8=True, out=dout, workspace=ws, outputs=lay)
         return h
 
-    def timed(fn):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        torch.cuda._sleep(int(2.4e9 * 0.02))
-        e0.record()
-        for _ in range(n):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / n
-
     def graph_step(first, reps=20):
-        # reps consecutive decode steps captured in one graph, so that the host's cost of a replay is spread over
-        # them; HIP events around the replays give the GPU-side time of a step
         for _ in range(2):
             ep.ep_combine(first(), y, w, out=out)
         torch.cuda.synchronize()
@@ -395,9 +640,9 @@ def measure_decode(ep, W, dev, n):
         return e0.elapsed_time(e1) * 1e3 / (nrep * reps)
 
     res = dict(workload="decode: 128 tok x 7168, 256 experts, top-8, FP8, alignment 128, no zero padding",
-               layout_then_dispatch_us=round(timed(two_calls), 2),
-               layout_dispatch_one_launch_us=round(timed(one_call), 2),
-               combine_us=round(timed(lambda: ep.ep_combine(h0, y, w, out=out)), 2),
+               layout_then_dispatch_us=round(events_us(two_calls, n), 2),
+               layout_dispatch_one_launch_us=round(events_us(one_call, n), 2),
+               combine_us=round(events_us(lambda: ep.ep_combine(h0, y, w, out=out), n), 2),
                step_graph_two_launches_us=round(graph_step(two_calls), 2),
                step_graph_one_launch_us=round(graph_step(one_call), 2),
                step_graph_note="per step of a graph of 20 consecutive steps (layout + dispatch, then combine), "
@@ -405,6 +650,8 @@ def measure_decode(ep, W, dev, n):
     h0.free()
     return res
 
+
+# ---- main ---------------------------------------------------------------------------------------------------
 
 def main():
     args = parse()
@@ -451,26 +698,15 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    def step(ev=None):
-        """One pass of the path.  Timed steps (ev None) make the one-call layout + dispatch, which reads the token
-        rows into the memory-side cache while the layout runs; the flushed per-call samples (ev given) make the
-        two calls separately so that each can be bracketed by its own events."""
-        stream = torch.cuda.current_stream()
-        if ev is None:
-            h, _, _ = ep.ep_layout_dispatch(idx, x, E, R, cfg.rank, cfg.expert_alignment, w, fp8=cfg.fp8,
-                                            do_zero_padding=cfg.zero_padding, out=dout, workspace=ws,
-                                            outputs=lay_out)
-            ep.ep_combine(h, y, w, bias, out=out)
-            return h
-        ev[0].record(stream)
-        h, _ = ep.ep_get_layout(idx, E, R, cfg.rank, cfg.expert_alignment, workspace=ws, outputs=lay_out)
-        ev[1].record(stream)
-        ep.ep_dispatch(h, x, w, fp8=cfg.fp8, do_zero_padding=cfg.zero_padding, out=dout)
-        ev[2].record(stream)
+    def step():
+        """One pass of the path: the one-call layout + dispatch (the layout kernels read the token rows into the
+        memory-side cache while the layout runs), then the combine."""
+        h, _, _ = ep.ep_layout_dispatch(idx, x, E, R, cfg.rank, cfg.expert_alignment, w, fp8=cfg.fp8,
+                                        do_zero_padding=cfg.zero_padding, out=dout, workspace=ws, outputs=lay_out)
         ep.ep_combine(h, y, w, bias, out=out)
-        ev[3].record(stream)
         return h
 
+    progress("steps")
     # W untimed warm-up steps
     for _ in range(max(args.warmup, 1)):
         step()
@@ -487,7 +723,7 @@ def main():
     # the same step as a HIP graph: W warm-up replays, then K timed replays
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        graph_handle = step()
+        step()
     torch.cuda.synchronize()
     for _ in range(max(args.warmup, 1)):
         graph.replay()
@@ -497,60 +733,7 @@ def main():
         graph.replay()
     torch.cuda.synchronize()
     step_graph_us = (time.perf_counter() - g0) * 1e6 / args.steps
-
-    # per-kernel durations: HIP events on the launch stream bracketing N back-to-back launches of one call
-    # (an event marker between kernels costs several microseconds of GPU time, so each kernel is timed in a run
-    # of its own launches and the marker cost is divided by N); the calls are the same as inside the step
-    def timed(fn, n):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        torch.cuda._sleep(int(2.4e9 * 0.02))   # ~20 ms of GPU spin while the host enqueues the launches
-        e0.record()
-        for _ in range(n):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n
-
-    hk, _ = ep.ep_get_layout(idx, E, R, cfg.rank, cfg.expert_alignment, workspace=ws, outputs=lay_out)
-    avg = {
-        "layout": timed(lambda: ep.ep_get_layout(idx, E, R, cfg.rank, cfg.expert_alignment, workspace=ws,
-                                                 outputs=lay_out), args.steps),
-        "dispatch": timed(lambda: ep.ep_dispatch(hk, x, w, fp8=cfg.fp8, do_zero_padding=cfg.zero_padding,
-                                                 out=dout), args.steps),
-        "combine": timed(lambda: ep.ep_combine(hk, y, w, bias, out=out), args.steps),
-    }
-
-    def layout_then_dispatch():
-        h, _ = ep.ep_get_layout(idx, E, R, cfg.rank, cfg.expert_alignment, workspace=ws, outputs=lay_out)
-        ep.ep_dispatch(h, x, w, fp8=cfg.fp8, do_zero_padding=cfg.zero_padding, out=dout)
-
-    layout_dispatch_us = timed(layout_then_dispatch, args.steps) * 1e3
-
-    def layout_dispatch_one_call():
-        ep.ep_layout_dispatch(idx, x, E, R, cfg.rank, cfg.expert_alignment, w, fp8=cfg.fp8,
-                              do_zero_padding=cfg.zero_padding, out=dout, workspace=ws, outputs=lay_out)
-
-    layout_dispatch_one_us = timed(layout_dispatch_one_call, args.steps) * 1e3
-
-    # per-kernel samples with a cache flush before each (10 warm-up + N samples, the pages' method)
-    flushed = None
-    if args.flush_samples > 0:
-        junk = torch.empty(2 << 30, dtype=torch.uint8, device=dev).fill_(3)
-        fl = {"layout": [], "dispatch": [], "combine": []}
-        for i in range(10 + args.flush_samples):
-            junk.sum(dtype=torch.int64)
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-            step(ev)
-            torch.cuda.synchronize()
-            if i >= 10:
-                fl["layout"].append(ev[0].elapsed_time(ev[1]))  # includes event-marker overhead
-                fl["dispatch"].append(ev[1].elapsed_time(ev[2]))
-                fl["combine"].append(ev[2].elapsed_time(ev[3]))
-        del junk
-        flushed = {k: float(np.median(v)) for k, v in fl.items()}
-        flushed_min = {k: float(np.min(v)) for k, v in fl.items()}
+    del graph
 
     # device counts after the timed loop
     cnt = lay_out["num_tokens_per_expert"].cpu().numpy()
@@ -563,78 +746,61 @@ def main():
     step_bytes = bm["layout"] + bm["dispatch"] + bm["combine"]
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
-    def gbps(b, ms):
-        return b / (ms * 1e-3) / 1e9
+    # per-call table of every workload (the headline one first)
+    probe = Probe(dev) if (args.flushed or args.bound) else None
+    names = [args.workload] + ([n for n in ALL_WORKLOADS if n != args.workload] if args.workloads else [])
+    table = {}
+    for name in names:
+        progress("workload %s" % name)
+        table[name] = measure_workload(ep, W, dev, name, args.steps, probe, flushed=args.flushed)
+    head = table[args.workload]["calls"]
 
-    kern = {
-        "layout": dict(us=round(avg["layout"] * 1e3, 2), bytes=bm["layout"]),
-        "dispatch": dict(us=round(avg["dispatch"] * 1e3, 2), bytes=bm["dispatch"],
-                         GBps=round(gbps(bm["dispatch"], avg["dispatch"]), 1),
-                         pct_peak=round(100 * gbps(bm["dispatch"], avg["dispatch"]) / HBM_PEAK_GBPS, 1)),
-        "combine": dict(us=round(avg["combine"] * 1e3, 2), bytes=bm["combine"],
-                        GBps=round(gbps(bm["combine"], avg["combine"]), 1),
-                        pct_peak=round(100 * gbps(bm["combine"], avg["combine"]) / HBM_PEAK_GBPS, 1)),
-    }
-    if flushed is not None:
-        for k in ("dispatch", "combine"):
-            kern[k]["us_flushed_median"] = round(flushed[k] * 1e3, 2)
-            kern[k]["us_flushed_min"] = round(flushed_min[k] * 1e3, 2)
-            kern[k]["GBps_flushed"] = round(gbps(bm[k], flushed[k]), 1)
-        kern["layout"]["us_flushed_median"] = round(flushed["layout"] * 1e3, 2)
-        kern["layout"]["us_flushed_min"] = round(flushed_min["layout"] * 1e3, 2)
-    kern["layout_then_dispatch"] = dict(us=round(layout_dispatch_us, 2))
-    kern["layout_dispatch_one_call"] = dict(us=round(layout_dispatch_one_us, 2),
-                                            note="ep_layout_dispatch: the layout kernels also read x ahead of "
-                                                 "the dispatch")
-
-    dom = "dispatch" if avg["dispatch"] >= avg["combine"] else "combine"
+    dom = "dispatch" if head["dispatch"]["us"] >= head["combine"]["us"] else "combine"
     dom_kernel = {"dispatch": "k_dispatch_fp8", "combine": "k_combine"}[dom]
-    achieved = gbps(bm[dom], avg[dom])
+    achieved = rate(bm[dom], head[dom]["us"])
     roofline = dict(bound="hbm", kernel=dom_kernel, achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=load_traffic(dom_kernel),
-                    algorithmic_bytes=bm[dom], avg_launch_us=round(avg[dom] * 1e3, 2))
+                    algorithmic_bytes=bm[dom], avg_launch_us=round(head[dom]["us"], 2),
+                    timing="HIP events around %d back-to-back launches on the launch stream" % args.steps)
+    if "us_flushed_median" in head[dom]:
+        roofline["frac_flushed"] = round(rate(bm[dom], head[dom]["us_flushed_median"]) / HBM_PEAK_GBPS, 4)
 
+    progress("dispatch bound, epilogues, decode, copy ceiling")
+    bound = measure_dispatch_bound(ep, W, dev, args.steps, probe) if (args.bound and args.workload == "prefill") \
+        else None
     epi = measure_epilogues(ep, W, dev, args.steps) if args.epilogues else None
     decode = measure_decode(ep, W, dev, args.steps) if args.decode else None
     copy_ceiling = measure_copy_ceiling(dev, 20) if args.copy_ceiling else None
-    others = ([n for n in ("tiny", "decode", "ep8", "skewed") if n != args.workload] if args.workloads else [])
-    workloads = measure_workloads(ep, W, dev, others, 20) if others else None
-    if workloads:
-        workloads["note"] = ("per call: events around back-to-back launches; step: eager one-call layout + dispatch "
-                             "then combine, host clock, the median of five blocks of 20 steps -- for tiny and decode "
-                             "that is bounded by the host's enqueue of the calls, see decode.step_graph_* for the "
-                             "GPU-side decode step")
+    del probe
 
     cpu = None
     if not args.no_cpu_baseline:
+        progress("cpu baseline")
         y_bits = y.cpu().view(torch.int16).numpy().view(np.uint16)
         cpu = cpu_baseline(inp, y_bits, cfg)
 
     line = dict(
-        metric="dispatch/combine effective HBM GB/s + % of peak, 4096 tok\u00d77168 top-8, 1 GPU",
+        metric="dispatch/combine effective HBM GB/s + % of peak, 4096 tok×7168 top-8, 1 GPU",
         value=round(value, 1), unit="GB/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
         ms_per_step=round(ms_per_step, 4), higher_is_better=True, scaling="weak", vs_baseline=None,
         dtype="bf16/fp8-e4m3", data="synthetic",
-        config=dict(workload="%s: %d tok x hidden %d, %d experts%s, top-%d, FP8 e4m3 per-128 dispatch%s, "
-                              "BF16 combine, alignment %d" % (
-                                  cfg.name, T, cfg.hidden, E,
-                                  " (8 groups, top-4 groups)" if cfg.routing == "grouped" else "", K,
-                                  " + zero padding" if cfg.zero_padding else "", cfg.expert_alignment),
-                    tokens=T, hidden=cfg.hidden, experts=E, topk=K, ranks=R, expert_alignment=cfg.expert_alignment,
-                    valid_rows=V, pad_rows=counts["P"], A_pad=round(int(psum[-1]) / max(V, 1), 4),
+        config=dict(workload=describe(cfg), tokens=T, hidden=cfg.hidden, experts=E, topk=K, ranks=R,
+                    expert_alignment=cfg.expert_alignment, valid_rows=V, pad_rows=counts["P"],
+                    A_pad=round(int(psum[-1]) / max(V, 1), 4),
                     data_dtypes="x bf16 -> recv e4m3 + fp32 scales; y bf16 -> out bf16 (fp32 accumulate)"),
         tokens_per_s=round(T / (ms_per_step * 1e-3), 1),
         timing="step: K eager steps of ep_layout_dispatch (layout kernels reading x ahead, then the dispatch) + "
-               "ep_combine between device syncs; per call: "
-               "events around K back-to-back launches",
+               "ep_combine between device syncs, host clock; per call: events around K back-to-back launches, "
+               "and flushed (2 GiB read sweep before each of 10 + 50 samples, kernel durations from a trace)",
         step_graph_replay_us=round(step_graph_us, 2),
-        kernels=kern,
+        kernels=head,
         roofline=roofline,
         cpu_baseline=cpu,
+        dispatch_bound=bound,
+        workloads=table,
         epilogues=epi,
         decode=decode,
         copy_ceiling=copy_ceiling,
-        workloads=workloads,
     )
     print(json.dumps(line), flush=True)
 

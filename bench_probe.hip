@@ -1,0 +1,175 @@
+// bench_probe.hip -- measurement probes for bench.py (not part of the library, and not behind include/ep.h).
+//
+// Each probe replays one half of the FP8 dispatch's memory traffic with the dispatch's own work split and
+// launch shape (one wave per 1024-channel segment of a token, then padding segments), so that bench.py can
+// time what the hardware gives for that address stream alone:
+//   probe_dispatch_writes  every store of an FP8 dispatch with zero padding -- the routed rows' e4m3 bytes
+//                          (16-byte non-temporal stores to each destination row), their scales and row metadata,
+//                          and the zero-padding rows -- and no source reads;
+//   probe_dispatch_reads   every source read of that dispatch -- the token rows (32 bytes per lane, non-temporal)
+//                          and the slot map -- and no stores;
+//   probe_flush            plain loads over a large buffer (a cache flush between timed samples).
+// The bytes stored are a constant pattern, so these say nothing about correctness; they bound the dispatch's
+// time from below: on HBM the reads and the writes share each channel's data bus.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;
+constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int kPadPerWave = 2;   // padding segments per wave, as the dispatch's grid is sized
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct WriteArgs {
+    const int32_t* token_rows;   // [T, K] destination row of each entry, -1 none
+    const int32_t* pad_rows;     // [npad] padding rows
+    uint8_t* recv_x;             // [rows, H] e4m3 bytes
+    float* recv_scales;          // [rows, H / 128]
+    int32_t* recv_src;           // [rows]
+    float* recv_w;               // [rows]
+    int T, K, H, npad;
+    int nstep;                   // 1024-channel segments per row
+    int64_t ntok_items, nwaves;
+};
+
+__global__ __launch_bounds__(kBlock) void k_probe_writes(WriteArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    const int G = a.H / 128;
+    const int64_t npad_items = (int64_t)a.npad * a.nstep;
+    int prow[kPadPerWave];
+#pragma unroll
+    for (int j = 0; j < kPadPerWave; ++j) {
+        const int64_t i = gw + j * a.nwaves;
+        prow[j] = i < npad_items ? a.pad_rows[i / a.nstep] : 0;
+    }
+    if (gw < a.ntok_items) {
+        const int t = (int)(gw / a.nstep), s = (int)(gw % a.nstep);
+        const int d = lane < a.K ? a.token_rows[(int64_t)t * a.K + lane] : -1;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(d >= 0);
+        const u32x4 q = {0x3C3C3C3Cu, 0x3C3C3C3Cu, 0x3C3C3C3Cu, 0x3C3C3C3Cu};
+        const bool sc_lane = (lane & 7) == 0;
+        const int g = s * 8 + (lane >> 3);
+        for (uint64_t mm = m; mm != 0; mm &= mm - 1) {
+            const int row = __builtin_amdgcn_readlane(d, __builtin_ctzll(mm));
+            __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(a.recv_x + (int64_t)row * a.H) + s * kWave + lane);
+            if (sc_lane && g < G) a.recv_scales[(int64_t)row * G + g] = 1.0f;
+        }
+        if (s == 0 && d >= 0) {
+            a.recv_src[d] = t;
+            a.recv_w[d] = 0.125f;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kPadPerWave; ++j) {
+        const int64_t i = gw + j * a.nwaves;
+        if (i >= npad_items) break;
+        const int s = (int)(i % a.nstep);
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        __builtin_nontemporal_store(z, reinterpret_cast<u32x4*>(a.recv_x + (int64_t)prow[j] * a.H) + s * kWave + lane);
+        if (lane < 8 && s * 8 + lane < G) a.recv_scales[(int64_t)prow[j] * G + s * 8 + lane] = 0.0f;
+        if (s == 0 && lane == 0) {
+            a.recv_src[prow[j]] = -1;
+            a.recv_w[prow[j]] = 0.0f;
+        }
+    }
+}
+
+struct ReadArgs {
+    const uint8_t* x;            // [T, 2H] bf16 rows
+    const int32_t* token_rows;   // [T, K]
+    int T, K, H, nstep;
+    int64_t ntok_items;
+    int32_t* sink;               // written only if the loads' xor equals `never` (it does not)
+    uint32_t never;
+};
+
+__global__ __launch_bounds__(kBlock) void k_probe_reads(ReadArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    if (gw >= a.ntok_items) return;
+    const int t = (int)(gw / a.nstep), s = (int)(gw % a.nstep);
+    const int d = lane < a.K ? a.token_rows[(int64_t)t * a.K + lane] : 0;
+    const int ch = (s * kWave + lane) * 16;
+    uint32_t acc = (uint32_t)d;
+    if (ch < a.H) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(a.x + ((int64_t)t * a.H + ch) * 2);
+        const u32x4 v0 = __builtin_nontemporal_load(src);
+        const u32x4 v1 = __builtin_nontemporal_load(src + 1);
+        acc ^= v0[0] ^ v0[1] ^ v0[2] ^ v0[3] ^ v1[0] ^ v1[1] ^ v1[2] ^ v1[3];
+    }
+    if (acc == a.never) a.sink[0] = (int32_t)acc;
+}
+
+__global__ __launch_bounds__(kBlock) void k_probe_flush(const u32x4* p, int64_t n16, int32_t* sink, uint32_t never) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    uint32_t acc = 0;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n16; i += 4 * stride) {
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = p[i + u * stride < n16 ? i + u * stride : i];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc ^= v[u][0] ^ v[u][3];
+    }
+    if (acc == never) sink[0] = (int32_t)acc;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Returns 0, or -1 on an argument outside what the probe handles (nothing is launched then), or the HIP error.
+int probe_dispatch_writes(const int32_t* token_rows, int T, int K, const int32_t* pad_rows, int npad, void* recv_x,
+                          float* recv_scales, int32_t* recv_src, float* recv_w, int H, void* stream) {
+    if (T < 1 || K < 1 || K > kWave || npad < 0 || H < 1024 || H % 1024 != 0) return -1;
+    WriteArgs a;
+    a.token_rows = token_rows;
+    a.pad_rows = pad_rows;
+    a.recv_x = static_cast<uint8_t*>(recv_x);
+    a.recv_scales = recv_scales;
+    a.recv_src = recv_src;
+    a.recv_w = recv_w;
+    a.T = T;
+    a.K = K;
+    a.H = H;
+    a.npad = npad;
+    a.nstep = H / 1024;
+    a.ntok_items = (int64_t)T * a.nstep;
+    int64_t nwaves = a.ntok_items;
+    const int64_t pad_waves = ((int64_t)npad * a.nstep + kPadPerWave - 1) / kPadPerWave;
+    if (pad_waves > nwaves) nwaves = pad_waves;
+    const int64_t nblocks = (nwaves + kWavesPerBlock - 1) / kWavesPerBlock;
+    a.nwaves = nblocks * kWavesPerBlock;
+    hipLaunchKernelGGL(k_probe_writes, dim3((unsigned)nblocks), dim3(kBlock), 0, static_cast<hipStream_t>(stream), a);
+    return (int)hipGetLastError();
+}
+
+int probe_dispatch_reads(const void* x, const int32_t* token_rows, int T, int K, int H, int32_t* sink, void* stream) {
+    if (T < 1 || K < 1 || K > kWave || H < 1024 || H % 1024 != 0) return -1;
+    ReadArgs a;
+    a.x = static_cast<const uint8_t*>(x);
+    a.token_rows = token_rows;
+    a.T = T;
+    a.K = K;
+    a.H = H;
+    a.nstep = H / 1024;
+    a.ntok_items = (int64_t)T * a.nstep;
+    a.sink = sink;
+    a.never = 0x9E3779B9u;
+    const int64_t nblocks = (a.ntok_items + kWavesPerBlock - 1) / kWavesPerBlock;
+    hipLaunchKernelGGL(k_probe_reads, dim3((unsigned)nblocks), dim3(kBlock), 0, static_cast<hipStream_t>(stream), a);
+    return (int)hipGetLastError();
+}
+
+int probe_flush(const void* buf, int64_t bytes, int32_t* sink, void* stream) {
+    if (bytes < 16) return -1;
+    hipLaunchKernelGGL(k_probe_flush, dim3(2048), dim3(kBlock), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const u32x4*>(buf), bytes / 16, sink, 0x9E3779B9u);
+    return (int)hipGetLastError();
+}
+
+}  // extern "C"

@@ -41,3 +41,32 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_all_cores_leg_computes_the_oracle():
+    """The all-cores CPU leg (the oracle's C dispatch and combine over token ranges, one thread each) writes the
+    same dispatch outputs, byte for byte, and the same combine as the single-threaded oracle calls."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+
+    cfg = W.Config("t", 300, 1024, 32, 4, "uniform", 16, True, True, bias=True, bias_std=0.1)
+    inp = W.make_inputs(cfg, seed=5)
+    idx = np.ascontiguousarray(inp["topk_idx"].numpy())
+    w = np.ascontiguousarray(inp["topk_weights"].numpy())
+    x = np.ascontiguousarray(W.bf16_bits(inp["x"]))
+    bias = W.bf16_bits(inp["bias"])
+    lay = O.layout(idx, cfg.num_experts, 1, 0, cfg.expert_alignment)
+    y = W.bf16_bits(W.normal_bf16((lay["cap"], cfg.hidden), torch.Generator().manual_seed(2)))
+    ref = O.dispatch(x, idx, w, lay, cfg.num_experts, 1, 0, cfg.expert_alignment, fp8=True, zero_pad=True,
+                     recv_fill=(0, 0.0))
+    ref_out = O.combine(y, lay["slot"], w, bias)
+    for ncores in (1, 3, 7):
+        got, _ = bench.oracle_token_ranges(x, idx, w, y, bias, cfg, ncores)
+        used = int(lay["psum"][-1])
+        assert np.array_equal(got["recv_x"][:used], ref["recv_x"][:used])
+        assert np.array_equal(got["recv_scales"][:used].view(np.uint32), ref["recv_scales"][:used].view(np.uint32))
+        assert np.array_equal(got["recv_src"][:used], ref["recv_src"][:used])
+        assert np.array_equal(got["recv_w"][:used].view(np.uint32), ref["recv_w"][:used].view(np.uint32))
+        assert np.array_equal(got["out"], ref_out)
