@@ -21,6 +21,8 @@
 //                           the padding prefix in LDS, writes the list entry and (without zero padding) the
 //                           row's metadata;
 //   zero-padding items      (row number, segment) pairs, zeros written as in the dispatch kernels.
+// The padding runs on the waves that have no token segment (at hidden 7168, 9 of the 16 waves of every token's
+// workgroup), beside the token segments instead of after them.
 #include <algorithm>
 
 #include "ep_dispatch_core.hpp"
@@ -87,19 +89,23 @@ __global__ __launch_bounds__(kThreads) void k_layout_dispatch_small(FusedArgs f,
         }
     }
 
-    // padding: the row list (and, without zero padding, the rows' metadata), one row number per lane
-    const int64_t gw = (int64_t)w * gridDim.x + blockIdx.x;
+    // padding, on the waves without a token segment (waves nt.. of the token workgroups, every wave of the
+    // workgroups past T), so that it runs beside the token segments: the row list (and, without zero padding,
+    // the rows' metadata), one row number per lane; then, with zero padding, (row number, segment) items
+    const int nt = min(p.nstep, kWaves);
+    if (tok && w < nt) return;
+    const int64_t iw = tok ? (int64_t)blockIdx.x * (kWaves - nt) + (w - nt)
+                           : (int64_t)T * (kWaves - nt) + ((int64_t)blockIdx.x - T) * kWaves + w;
     const int npad = L.padpre[epr];
     const bool meta_only = !p.token_major && !p.zero_pad && (p.recv_src != nullptr || p.recv_w != nullptr);
-    for (int64_t q = gw * kWave + lane; q < npad; q += p.nwaves * kWave) {
+    for (int64_t q = iw * kWave + lane; q < npad; q += p.nwaves * kWave) {
         const int row = pad_row_of((int)q, epr, L.psum, L.padpre);
         if (f.o.pad_rows) f.o.pad_rows[q] = row;
         if (meta_only) pad_meta_row(p, row);
     }
-    // zero padding: (row number, segment) items
     if (p.zero_pad && !p.token_major) {
         const int64_t nitems = (int64_t)npad * p.nstep;
-        for (int64_t i = gw; i < nitems; i += p.nwaves) {
+        for (int64_t i = iw; i < nitems; i += p.nwaves) {
             const int q = (int)(i / p.nstep);
             pad_zero_segment<FP8>(p, pad_row_of(q, epr, L.psum, L.padpre), (int)(i % p.nstep), lane);
         }
@@ -122,12 +128,15 @@ hipError_t launch_layout_dispatch(const Handle& h, const LayoutOutputs& out, con
     const int64_t max_pad = (int64_t)h.El * (h.A - 1);
     int64_t pad_waves = (max_pad + kWave - 1) / kWave;
     if (p.zero_pad && !p.token_major) pad_waves = std::max(pad_waves, (max_pad * p.nstep + kPadItemsPerWave - 1) / kPadItemsPerWave);
-    const int64_t nwaves = std::min(pad_waves, (int64_t)kMaxPadWaves);
-    // one workgroup per token (workgroup t owns token t), more only if the padding passes need them: workgroups
-    // without a token were measured to cost time (decode 8.12 -> 8.06 us, one token 6.04 -> 5.92 us without the
-    // 256 that one per CU would give)
-    const int64_t nblocks = std::max<int64_t>((nwaves + kWaves - 1) / kWaves, std::max(h.T, 1));
-    p.nwaves = nblocks * kWaves;
+    const int64_t want = std::min(pad_waves, (int64_t)kMaxPadWaves);   // 0 without any padding
+    // one workgroup per token (workgroup t owns token t), more only if its idle waves (those without a token
+    // segment) are too few for the padding passes: workgroups without a token were measured to cost time
+    // (decode 8.12 -> 8.06 us, one token 6.04 -> 5.92 us without the 256 that one per CU would give)
+    const int64_t idle_per_tok = kWaves - std::min(p.nstep, kWaves);
+    const int64_t have = (int64_t)h.T * idle_per_tok;
+    const int64_t nblocks = h.T + (have >= want ? 0 : (want - have + kWaves - 1) / kWaves);
+    // the padding waves, the stride of the padding passes (>= 1 whenever a wave runs a padding pass)
+    p.nwaves = have + (nblocks - h.T) * kWaves;
 
     FusedArgs f;
     f.idx = h.topk_idx;

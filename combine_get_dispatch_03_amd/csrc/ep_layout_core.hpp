@@ -220,16 +220,27 @@ __device__ inline void tok_counts(const int64_t* __restrict__ idx, int T, int K,
     }
     if (lane == 0 && inv != 0) atomicAdd(&L.tot[E + R], inv);
     const float inv_epr = 1.0f / (float)epr;
-    if (tid < T) {                                   // token tid: the ranks it goes to
-        uint64_t m = 0ull;
-        for (int k = 0; k < K; ++k) {
-            const int e = L.ent[tid * K + k];
-            if (e >= 0) m |= 1ull << rank_of(e, inv_epr);
+    if ((tid & ~(kWave - 1)) < T) {                  // waves holding tokens (token tid on thread tid)
+        uint64_t m = 0ull;                           // the ranks token tid goes to
+        if (tid < T)
+            for (int k = 0; k < K; ++k) {
+                const int e = L.ent[tid * K + k];
+                if (e >= 0) m |= 1ull << rank_of(e, inv_epr);
+            }
+        // per rank present in the wave: one ballot for its tokens, one for those before t, one LDS add each
+        uint32_t lo32 = (uint32_t)m, hi32 = (uint32_t)(m >> 32);
+        for (int o = 1; o < kWave; o <<= 1) {
+            lo32 |= (uint32_t)__shfl_xor((int)lo32, o);
+            hi32 |= (uint32_t)__shfl_xor((int)hi32, o);
         }
-        for (uint64_t mm = m; mm != 0; mm &= mm - 1) {
-            const int r = __builtin_ctzll(mm);
-            atomicAdd(&L.tot[E + r], 1);
-            if (tid < tb) atomicAdd(&L.rbef[r], 1);
+        for (uint64_t rr = ((uint64_t)hi32 << 32) | lo32; rr != 0; rr &= rr - 1) {
+            const int r = __builtin_ctzll(rr);
+            const bool bit = (m >> r) & 1ull;
+            const int all = popc64(ballot(bit)), before = popc64(ballot(bit && tid < tb));
+            if (lane == 0) {
+                atomicAdd(&L.tot[E + r], all);
+                if (before != 0) atomicAdd(&L.rbef[r], before);
+            }
         }
     }
     __syncthreads();
@@ -238,25 +249,20 @@ __device__ inline void tok_counts(const int64_t* __restrict__ idx, int T, int K,
 
 // Token t's rows (t < T), in one wave: lane k < K gets the expert-major row of entry k (-1 if the expert is not
 // local or the entry not valid), lane r < R the token's row in rank r's window (-1 if it has no expert on r).
+// Each lane reads one entry from LDS; the other entries are read back from their lanes as scalars.
 __device__ inline void tok_rows(const TokLds& L, int t, int K, int R, int lo, int epr, int& sexp, int& own) {
     const int lane = lane_id();
     const float inv_epr = 1.0f / (float)epr;
-    sexp = -1;
-    if (lane < K) {
-        const int e = L.ent[t * K + lane];
-        if (e >= lo && e < lo + epr) {
-            int dup = 0;                             // earlier copies of e in this token
-            for (int k = 0; k < lane; ++k) dup += L.ent[t * K + k] == e ? 1 : 0;
-            sexp = L.psum[e - lo] + L.bef[e] + dup;
-        }
+    const int e = lane < K ? L.ent[t * K + lane] : -1;
+    int dup = 0;                                     // copies of e among entries 0..lane-1
+    bool has = false;                                // lane < R: an entry of the token is on rank `lane`
+    for (int k = 0; k < K; ++k) {
+        const int ek = readlane(e, k);
+        dup += (k < lane && ek == e) ? 1 : 0;
+        has = has || (ek >= 0 && rank_of(ek, inv_epr) == lane);
     }
-    bool has = false;
-    if (lane < R)
-        for (int k = 0; k < K; ++k) {
-            const int e = L.ent[t * K + k];
-            if (e >= 0 && rank_of(e, inv_epr) == lane) has = true;
-        }
-    own = has ? L.rbef[lane] : -1;
+    sexp = (lane < K && e >= lo && e < lo + epr) ? L.psum[e - lo] + L.bef[e] + dup : -1;
+    own = (lane < R && has) ? L.rbef[lane] : -1;
 }
 
 }  // namespace
