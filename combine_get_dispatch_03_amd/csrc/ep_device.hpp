@@ -53,6 +53,18 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
     return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
 
+// OR over the 64 lanes, the same in every lane: four DPP row shifts within each 16-lane row (lanes with no
+// source read 0), then the four row results read back from lanes 15, 31, 47 and 63.
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+    int x = (int)v;
+    x |= __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+    x |= __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+    x |= __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+    x |= __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+    return (uint32_t)(__builtin_amdgcn_readlane(x, 15) | __builtin_amdgcn_readlane(x, 31) |
+                      __builtin_amdgcn_readlane(x, 47) | __builtin_amdgcn_readlane(x, 63));
+}
+
 // Lane permutation within rows of 16 lanes by a DPP control (every lane has a source for the controls used here).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {

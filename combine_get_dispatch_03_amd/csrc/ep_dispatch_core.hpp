@@ -126,10 +126,13 @@ __device__ __forceinline__ Fp8Src fp8_load(const Params& p, int t, int st, int l
     return v;
 }
 
-__device__ __forceinline__ void fp8_emit(const Params& p, int st, int lane, const Fp8Src& v, int ds, int js,
-                                         uint64_t lmask, uint64_t smask) {
-    const int H = p.H, G = H / 128;
-    const bool active = (st * kWave + lane) * 16 < H;
+// The cast of one lane's 16 channels: 16 e4m3 bytes and its group's scale.
+struct Fp8Row {
+    u32x4 q;
+    float scale;
+};
+
+__device__ __forceinline__ Fp8Row fp8_cast(const Fp8Src& v) {
     const u32x4 a = v.a, b = v.b;
     float f[16];
 #pragma unroll
@@ -144,27 +147,39 @@ __device__ __forceinline__ void fp8_emit(const Params& p, int st, int lane, cons
     for (int k = 0; k < 16; ++k) m = fmaxf(m, fabsf(f[k]));
     m = group8_max(m);
     const float amax = fmaxf(m, 1e-4f);
-    const float scale = amax / 448.0f;           // IEEE division (correctly rounded)
+    Fp8Row r;
+    r.scale = amax / 448.0f;                     // IEEE division (correctly rounded)
     const float inv = 448.0f / amax;
-    u32x4 q;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-        q[k] = pack_e4m3x4(f[4 * k] * inv, f[4 * k + 1] * inv, f[4 * k + 2] * inv, f[4 * k + 3] * inv);
+        r.q[k] = pack_e4m3x4(f[4 * k] * inv, f[4 * k + 1] * inv, f[4 * k + 2] * inv, f[4 * k + 3] * inv);
+    return r;
+}
+
+// Stores of segment st's cast bytes and scales to every destination row (local rows, then send rows).
+__device__ __forceinline__ void fp8_store(const Params& p, int st, int lane, const Fp8Row& c, int ds, int js,
+                                          uint64_t lmask, uint64_t smask) {
+    const int H = p.H, G = H / 128;
+    const bool active = (st * kWave + lane) * 16 < H;
     // lane 8 j stores the scale of group 8 st + j: the 8 stores of a segment are contiguous (one 32-byte write)
-    const float sg = scale;
     const int g = st * 8 + (lane >> 3);
     const bool sc_lane = (lane & 7) == 0 && g < G;
     for (uint64_t mm = lmask; mm != 0; mm &= mm - 1) {
         const int s = readlane(ds, __builtin_ctzll(mm));
-        if (active) st_nt(reinterpret_cast<u32x4*>(p.recv_x + (int64_t)s * H) + st * kWave + lane, q);
-        if (sc_lane) p.recv_scales[(int64_t)s * G + g] = sg;
+        if (active) st_nt(reinterpret_cast<u32x4*>(p.recv_x + (int64_t)s * H) + st * kWave + lane, c.q);
+        if (sc_lane) p.recv_scales[(int64_t)s * G + g] = c.scale;
     }
     for (uint64_t mm = smask; mm != 0; mm &= mm - 1) {
         const int r = __builtin_ctzll(mm);
         const int64_t row = (int64_t)r * p.T + readlane(js, r);
-        if (active) st_nt(reinterpret_cast<u32x4*>(p.send_x + row * H) + st * kWave + lane, q);
-        if (sc_lane) p.send_scales[row * G + g] = sg;
+        if (active) st_nt(reinterpret_cast<u32x4*>(p.send_x + row * H) + st * kWave + lane, c.q);
+        if (sc_lane) p.send_scales[row * G + g] = c.scale;
     }
+}
+
+__device__ __forceinline__ void fp8_emit(const Params& p, int st, int lane, const Fp8Src& v, int ds, int js,
+                                         uint64_t lmask, uint64_t smask) {
+    fp8_store(p, st, lane, fp8_cast(v), ds, js, lmask, smask);
 }
 
 

@@ -53,6 +53,7 @@ __global__ __launch_bounds__(kThreads) void k_layout_dispatch_small(FusedArgs f,
     // the token's first segments (segment s on wave s % 16) and its metadata do not depend on the layout: their
     // loads are issued with the routing table's and stay in flight through the layout work
     Fp8Src v8;
+    Fp8Row c8;
     u32x4 vr;
     TokenEntry te;
     tok_counts(f.idx, T, K, E, R, epr, f.A, lo, t, L, [&] {
@@ -61,6 +62,9 @@ __global__ __launch_bounds__(kThreads) void k_layout_dispatch_small(FusedArgs f,
             else vr = raw_load(p, t, w, lane);
             if (w == 0) te = token_entry(p, t, lane);
         }
+    }, [&] {
+        // the FP8 cast needs only the token's bytes: done while the other waves count
+        if (FP8 && tok && w < p.nstep) c8 = fp8_cast(v8);
     });
     if (blockIdx.x == 0) write_counts(E, R, lo, epr, L.tot, L.psum, L.padpre, f.o);
 
@@ -83,7 +87,7 @@ __global__ __launch_bounds__(kThreads) void k_layout_dispatch_small(FusedArgs f,
         }
         if ((lmask | smask) != 0) {
             for (int s = w; s < p.nstep; s += kWaves) {
-                if (FP8) fp8_emit(p, s, lane, s == w ? v8 : fp8_load(p, t, s, lane), ds, js, lmask, smask);
+                if (FP8) fp8_store(p, s, lane, s == w ? c8 : fp8_cast(fp8_load(p, t, s, lane)), ds, js, lmask, smask);
                 else raw_emit(p, t, s, lane, s == w ? vr : raw_load(p, t, s, lane), ds, js, lmask, smask);
             }
         }

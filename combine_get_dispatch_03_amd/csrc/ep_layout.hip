@@ -381,7 +381,7 @@ __global__ __launch_bounds__(kThreads) void k_layout_tokens(
     int32_t* __restrict__ slot, int32_t* __restrict__ send_slot, uint8_t* __restrict__ in_rank_out, Outputs o) {
     const TokLds L = carve_tok(layout_smem, E, K, R, epr);
     const int lo = rank * epr, t = blockIdx.x, lane = lane_id(), w = threadIdx.x >> 6;
-    tok_counts(idx, T, K, E, R, epr, A, lo, t, L, [] {});
+    tok_counts(idx, T, K, E, R, epr, A, lo, t, L, [] {}, [] {});
     if (blockIdx.x == 0) write_counts(E, R, lo, epr, L.tot, L.psum, L.padpre, o);
     if (t < T && w == 0) {
         int sexp, own;

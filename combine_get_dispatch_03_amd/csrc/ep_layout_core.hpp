@@ -180,11 +180,12 @@ __device__ inline TokLds carve_tok(unsigned char* base, int E, int K, int R, int
 __device__ __forceinline__ int rank_of(int e, float inv_epr) { return (int)(((float)e + 0.5f) * inv_epr); }
 
 // Stage the table, count (totals and counts before token t; t >= T counts nothing before), scan.  `pre` runs
-// right after the entry loads are issued (loads that do not depend on the layout go there).  Every thread of
+// right after the entry loads are issued (loads that do not depend on the layout go there), `mid` after this
+// thread's counting (work on those loads' data can overlap the other waves' counting there).  Every thread of
 // the block calls it; it ends with a barrier.
-template <class Pre>
+template <class Pre, class Mid>
 __device__ inline void tok_counts(const int64_t* __restrict__ idx, int T, int K, int E, int R, int epr, int A,
-                                  int lo, int t, const TokLds& L, Pre pre) {
+                                  int lo, int t, const TokLds& L, Pre pre, Mid mid) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int nent = T * K;
     const int tb = t < T ? t : 0;                    // tokens counted as before: none for a workgroup past T
@@ -228,12 +229,9 @@ __device__ inline void tok_counts(const int64_t* __restrict__ idx, int T, int K,
                 if (e >= 0) m |= 1ull << rank_of(e, inv_epr);
             }
         // per rank present in the wave: one ballot for its tokens, one for those before t, one LDS add each
-        uint32_t lo32 = (uint32_t)m, hi32 = (uint32_t)(m >> 32);
-        for (int o = 1; o < kWave; o <<= 1) {
-            lo32 |= (uint32_t)__shfl_xor((int)lo32, o);
-            hi32 |= (uint32_t)__shfl_xor((int)hi32, o);
-        }
-        for (uint64_t rr = ((uint64_t)hi32 << 32) | lo32; rr != 0; rr &= rr - 1) {
+        const uint64_t present = R > 32 ? ((uint64_t)wave_or((uint32_t)(m >> 32)) << 32) | wave_or((uint32_t)m)
+                                        : (uint64_t)wave_or((uint32_t)m);
+        for (uint64_t rr = present; rr != 0; rr &= rr - 1) {
             const int r = __builtin_ctzll(rr);
             const bool bit = (m >> r) & 1ull;
             const int all = popc64(ballot(bit)), before = popc64(ballot(bit && tid < tb));
@@ -243,6 +241,7 @@ __device__ inline void tok_counts(const int64_t* __restrict__ idx, int T, int K,
             }
         }
     }
+    mid();
     __syncthreads();
     local_scan(epr, lo, A, L.tot, L.psum, L.padpre, L.scratch);
 }
