@@ -73,6 +73,8 @@ def parse():
                     help="skip the flushed (pages' method) timings")
     ap.add_argument("--no-bound", dest="bound", action="store_false",
                     help="skip the dispatch write-stream / read-stream probes")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="skip the HIP-graph replay of the step (a kernel trace then holds eager launches only)")
     return ap.parse_args()
 
 
@@ -721,19 +723,21 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
     # the same step as a HIP graph: W warm-up replays, then K timed replays
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        step()
-    torch.cuda.synchronize()
-    for _ in range(max(args.warmup, 1)):
-        graph.replay()
-    torch.cuda.synchronize()
-    g0 = time.perf_counter()
-    for _ in range(args.steps):
-        graph.replay()
-    torch.cuda.synchronize()
-    step_graph_us = (time.perf_counter() - g0) * 1e6 / args.steps
-    del graph
+    step_graph_us = None
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(max(args.warmup, 1)):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        step_graph_us = round((time.perf_counter() - g0) * 1e6 / args.steps, 2)
+        del graph
 
     # device counts after the timed loop
     cnt = lay_out["num_tokens_per_expert"].cpu().numpy()
@@ -792,7 +796,7 @@ def main():
         timing="step: K eager steps of ep_layout_dispatch (layout kernels reading x ahead, then the dispatch) + "
                "ep_combine between device syncs, host clock; per call: events around K back-to-back launches, "
                "and flushed (2 GiB read sweep before each of 10 + 50 samples, kernel durations from a trace)",
-        step_graph_replay_us=round(step_graph_us, 2),
+        step_graph_replay_us=step_graph_us,
         kernels=head,
         roofline=roofline,
         cpu_baseline=cpu,
