@@ -49,6 +49,7 @@ KERNEL_SOURCES = {
     "k_dispatch_fp8": ("ep_dispatch.hip", "ep_dispatch_core.hpp", "ep_device.hpp"),
     "k_combine": ("ep_combine.hip", "ep_device.hpp"),
     "layout": ("ep_layout.hip", "ep_layout_core.hpp", "ep_device.hpp"),
+    "k_layout_dispatch_small": ("ep_fused.hip", "ep_layout_core.hpp", "ep_dispatch_core.hpp", "ep_device.hpp"),
 }
 
 

@@ -36,7 +36,7 @@ def commands(workload, out, repo="<repo>"):
     """The rocprofv3 runs a summary is made from (run from /tmp)."""
     bound = "" if workload == "prefill" else " --no-bound"
     b = "python3 %s/bench.py --workload %s %s%s" % (repo, workload, SKIP, bound)
-    return [
+    cmds = [
         "rocprofv3 --kernel-trace --stats --output-format csv -d %s/%s_kt -o kt -- %s --steps 50 --warmup 10 "
         "> %s/%s_kt.json" % (out, workload, b, out, workload),
         "rocprofv3 --pmc FETCH_SIZE --output-format csv -d %s/%s_fetch -o fetch -- %s --steps 2 --warmup 1 "
@@ -44,6 +44,11 @@ def commands(workload, out, repo="<repo>"):
         "rocprofv3 --pmc WRITE_SIZE --output-format csv -d %s/%s_write -o write -- %s --steps 2 --warmup 1 "
         "--calib-copy-mib %d" % (out, workload, b, COPY_MIB),
     ]
+    if workload == "prefill":   # the step's eager launches and its graph replays (bench.py's default order)
+        g = "python3 %s/bench.py --workload %s %s --no-bound" % (repo, workload, SKIP.replace("--no-graph ", ""))
+        cmds.append("rocprofv3 --kernel-trace --output-format csv -d %s/%s_ktg -o ktg -- %s --steps 50 --warmup 10 "
+                    "> %s/%s_ktg.json" % (out, workload, g, out, workload))
+    return cmds
 
 
 def _rows(folder, suffix):
@@ -142,6 +147,32 @@ def summarize(workload, out, traffic_json=None):
         if len(v) >= 10:
             lines.append("| %s | %d x %d | %s | %d | %.2f | %.2f |" % (name, nb, wg, p, len(v), sum(v) / len(v),
                                                                      statistics.median(v)))
+    # eager steps against graph replays: bench.py runs W + K eager steps, then W + K replays of the step graph,
+    # so the step's kernels occur in that order; the warm-ups of each are left out
+    ktg = kernel_trace(os.path.join(out, "%s_ktg" % workload))
+    try:
+        with open(os.path.join(out, "%s_ktg.json" % workload)) as f:
+            gline = json.loads(f.read().strip().splitlines()[-1])
+    except (OSError, ValueError, IndexError):
+        gline = None
+    if ktg and gline:
+        W, K = gline["warmup"], gline["steps"]
+        lines += ["", "Eager steps against HIP-graph replays of the same step (4th command; %d warm-ups of each "
+                  "left out): step %.1f us eager (host clock), %.1f us per graph replay." % (
+                      W, gline["ms_per_step"] * 1e3, gline["step_graph_replay_us"] or 0.0), "",
+                  "| kernel | blocks | eager avg | eager median | graph avg | graph median |",
+                  "|---|---|---|---|---|---|"]
+        seq = {}
+        for name, nb, wg, d, _ in ktg:
+            seq.setdefault((name, nb), []).append(d)
+        for (name, nb), v in sorted(seq.items(), key=lambda kv: -sum(kv[1])):
+            if not name.startswith("k_") or len(v) < 2 * (W + K):
+                continue
+            eager, graph = v[W:W + K], v[2 * W + K:2 * (W + K)]
+            lines.append("| %s | %d | %.2f | %.2f | %.2f | %.2f |" % (name, nb, sum(eager) / K, statistics.median(eager),
+                                                                    sum(graph) / K, statistics.median(graph)))
+    lines += ["", "Kernel sources profiled (sha256, first 16 hex digits, as bench.py tags counter figures): " +
+              ", ".join("%s %s" % (k, bench.source_hash(v)) for k, v in bench.KERNEL_SOURCES.items())]
     if line:
         calls = line["kernels"]
         lines += ["", "bench.py in the same run (HIP events around 50 back-to-back launches of each call, us): " +
