@@ -21,6 +21,8 @@ the expert rows gathered once by combine and the output written once (bytes_mode
 dominant kernel, `cpu_baseline` the oracle timed on the host (one pinned core, and all cores over token
 ranges).  `workloads` has every workload (tiny, decode, prefill, ep8, skewed) measured the same way;
 `dispatch_bound` times the prefill dispatch's write stream and read stream on their own (bench_probe.hip).
+`step_kernels_us` gives each kernel's GPU time inside the step (a kernel trace of K more eager steps), and
+`roofline.frac_in_step` the dominant kernel's rate there.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
 """
@@ -74,9 +76,14 @@ def parse():
                     help="skip the flushed (pages' method) timings")
     ap.add_argument("--no-bound", dest="bound", action="store_false",
                     help="skip the dispatch write-stream / read-stream probes")
+    ap.add_argument("--no-trace", dest="trace", action="store_false",
+                    help="no in-process kernel trace (no flushed timings, no step_kernels_us): for runs under rocprofv3")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="skip the HIP-graph replay of the step (a kernel trace then holds eager launches only)")
-    return ap.parse_args()
+    a = ap.parse_args()
+    if not a.trace:
+        a.flushed = False
+    return a
 
 
 def bytes_model(cfg, counts):
@@ -321,6 +328,27 @@ def flushed_us(fn, probe, warmup=10, samples=50):
     if len(per) != samples or min(per) <= 0.0:
         raise RuntimeError("flushed timing: %d samples traced, expected %d" % (len(per), samples))
     return float(np.median(per)), float(np.min(per))
+
+
+def traced_kernels_us(fn, n):
+    """GPU duration of every kernel fn launches, from a kernel trace (torch's profiler) of n calls: {kernel name:
+    average µs}, names shortened to the kernel's own identifier."""
+    import re
+
+    import torch
+    from torch.profiler import ProfilerActivity, profile
+
+    with profile(activities=[ProfilerActivity.CUDA]) as prof:
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+    out = {}
+    for e in prof.events():
+        if e.device_type != torch.autograd.DeviceType.CUDA:
+            continue
+        m = re.search(r"\b(k_\w+?)(?:<[^>]*>)?\(", e.name)
+        out.setdefault(m.group(1) if m else e.name[:40], []).append(e.time_range.end - e.time_range.start)
+    return {k: round(sum(v) / len(v), 2) for k, v in out.items()}
 
 
 def rate(b, us):
@@ -723,6 +751,9 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
+    # the step's own kernels, traced over K more steps (after the timed region, so that it is untouched)
+    step_kernels = traced_kernels_us(step, args.steps) if args.trace else {}
+
     # the same step as a HIP graph: W warm-up replays, then K timed replays
     step_graph_us = None
     if args.graph:
@@ -769,6 +800,9 @@ def main():
                     timing="HIP events around %d back-to-back launches on the launch stream" % args.steps)
     if "us_flushed_median" in head[dom]:
         roofline["frac_flushed"] = round(rate(bm[dom], head[dom]["us_flushed_median"]) / HBM_PEAK_GBPS, 4)
+    if dom_kernel in step_kernels:
+        roofline["in_step_us"] = step_kernels[dom_kernel]
+        roofline["frac_in_step"] = round(rate(bm[dom], step_kernels[dom_kernel]) / HBM_PEAK_GBPS, 4)
 
     progress("dispatch bound, epilogues, decode, copy ceiling")
     bound = measure_dispatch_bound(ep, W, dev, args.steps, probe) if (args.bound and args.workload == "prefill") \
@@ -798,6 +832,7 @@ def main():
                "ep_combine between device syncs, host clock; per call: events around K back-to-back launches, "
                "and flushed (2 GiB read sweep before each of 10 + 50 samples, kernel durations from a trace)",
         step_graph_replay_us=step_graph_us,
+        step_kernels_us=step_kernels,
         kernels=head,
         roofline=roofline,
         cpu_baseline=cpu,

@@ -29,7 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 COPY_MIB = 1024
-SKIP = ("--no-graph --no-flushed --no-cpu-baseline --no-epilogues --no-decode --no-copy-ceiling --no-workloads")
+SKIP = ("--no-graph --no-trace --no-cpu-baseline --no-epilogues --no-decode --no-copy-ceiling --no-workloads")
 
 
 def commands(workload, out, repo="<repo>"):
