@@ -103,3 +103,39 @@ def test_noalloc_bf16_token_major(ep):
         for k, t in out_ref.items():
             if t is not None:
                 assert np.array_equal(Hn.to_np(t).view(np.uint8), Hn.to_np(out_new[k]).view(np.uint8)), (expand, k)
+
+
+def test_noalloc_in_graph_capture(ep):
+    """Its callers' use: captured in a HIP graph.  One eager call first (the per-device set-up), then the call and
+    a combine captured, the graph replayed three times with eager work in between (the outputs reset to canaries);
+    every replay's outputs equal the eager ones bit for bit."""
+    inp = W.make_inputs("decode")
+    c = inp["cfg"]
+    T, E, A, H = c.num_tokens, c.num_experts, c.expert_alignment, c.hidden
+    idx, x, w = inp["topk_idx"].to(DEV), inp["x"].to(DEV), inp["topk_weights"].to(DEV)
+    h_ref, _ = ep.ep_get_layout(idx, E, 1, 0, A)                 # only to size the outputs
+    out = Hn.dispatch_outputs_with_canary(ep, h_ref, H, True, DEV)
+    lay = _layout_outputs(T, E, 1)
+    y = W.random_expert_outputs(h_ref.recv_capacity, H, seed=21, device=DEV)
+    res = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    h, _, _ = ep.ep_layout_dispatch_noalloc(idx, x, E, out, 1, 0, A, w, fp8=True, outputs=lay)
+    ep.ep_combine(h, y, w, out=res)
+    torch.cuda.synchronize()
+    ref = {k: t.clone() for k, t in list(out.items()) + list(lay.items()) if t is not None}
+    ref["res"] = res.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        hg, _, _ = ep.ep_layout_dispatch_noalloc(idx, x, E, out, 1, 0, A, w, fp8=True, outputs=lay)
+        ep.ep_combine(hg, y, w, out=res)
+    for rep in range(3):
+        Hn.fill_canaries(out)
+        Hn.fill_canaries(lay)
+        res.view(torch.int16).fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = dict(list(out.items()) + list(lay.items()), res=res)
+        for k, t in ref.items():
+            assert torch.equal(got[k].view(torch.uint8), t.view(torch.uint8)), (rep, k)
+        Hn.assert_guards(out)
+    h_ref.free()
