@@ -62,15 +62,28 @@ __device__ __forceinline__ TokenEntry token_entry(const Params& p, int t, int la
     return te;
 }
 
+// token_entry's loads with the entry index clamped into the token's entries and a valid address in place of
+// absent weights, so that they need no branch.  The values are raw (lanes >= K hold entry K - 1, and the weight
+// is a bit pattern of the ids without weights): token_meta applies the masks when it uses them, so that no
+// early use makes a wait for these loads wait for every load issued before them.
+__device__ __forceinline__ TokenEntry token_entry_clamped(const Params& p, int t, int lane) {
+    const int64_t j = (int64_t)t * p.K + min(lane, p.K - 1);
+    const float* w = p.w != nullptr ? p.w : reinterpret_cast<const float*>(p.topk_idx);   // T*K*8 bytes
+    TokenEntry te;
+    te.w = w[j];
+    te.e = p.topk_idx[j];
+    return te;
+}
+
 __device__ __forceinline__ void token_meta(const Params& p, int t, int lane, int ds, int js, uint64_t lmask,
                                            uint64_t smask, const TokenEntry* pre = nullptr) {
     const bool need_e = (smask != 0 && p.send_topk_idx != nullptr) ||
                         (p.token_major && lmask != 0 && p.recv_topk_idx != nullptr);
     float wk;
     int64_t e;
-    if (pre != nullptr) {
-        wk = pre->w;
-        e = pre->e;
+    if (pre != nullptr) {   // masks as in token_entry (a no-op on its values; needed for token_entry_clamped's)
+        wk = (lane < p.K && p.w != nullptr) ? pre->w : 1.0f;
+        e = lane < p.K ? pre->e : -1;
     } else {
         wk = (lane < p.K && p.w != nullptr) ? p.w[(int64_t)t * p.K + lane] : 1.0f;
         e = (need_e && lane < p.K) ? p.topk_idx[(int64_t)t * p.K + lane] : -1;
@@ -123,6 +136,17 @@ __device__ __forceinline__ Fp8Src fp8_load(const Params& p, int t, int st, int l
         v.a = ld_nt(src);
         v.b = ld_nt(src + 1);
     }
+    return v;
+}
+
+// fp8_load with the lane's channel clamped into the row (H is a multiple of 128, so a lane past the row belongs to
+// a group past the row, whose bytes and scale are never stored): no branch around the loads.
+__device__ __forceinline__ Fp8Src fp8_load_clamped(const Params& p, int t, int st, int lane) {
+    const int ch = min((st * kWave + lane) * 16, p.H - 16);
+    const u32x4* src = reinterpret_cast<const u32x4*>(p.src + ((int64_t)t * p.H + ch) * 2);
+    Fp8Src v;
+    v.a = ld_nt(src);
+    v.b = ld_nt(src + 1);
     return v;
 }
 
@@ -190,6 +214,12 @@ __device__ __forceinline__ u32x4 raw_load(const Params& p, int t, int st, int la
     u32x4 v = {0u, 0u, 0u, 0u};
     if (c < p.row_bytes / 16) v = ld_nt(reinterpret_cast<const u32x4*>(p.src + (int64_t)t * p.row_bytes) + c);
     return v;
+}
+
+// raw_load with the chunk clamped into the row (row_bytes >= 16; chunks past the row are never stored).
+__device__ __forceinline__ u32x4 raw_load_clamped(const Params& p, int t, int st, int lane) {
+    const int c = min(st * kWave + lane, p.row_bytes / 16 - 1);
+    return ld_nt(reinterpret_cast<const u32x4*>(p.src + (int64_t)t * p.row_bytes) + c);
 }
 
 __device__ __forceinline__ void raw_emit(const Params& p, int t, int st, int lane, u32x4 v, int ds, int js,

@@ -12,16 +12,17 @@
 //
 // The handle's workspace and the layout outputs are written along the way, so the handle is complete
 // afterwards (ep_dispatch and ep_combine can reuse it as if ep_get_layout had built it): block 0 writes the
-// counts and the psum; wave 0 of token t's workgroup writes its slots, its per-rank token rows and its
-// membership; the padding waves write the padding-row list.
-//   token segments          segment s of token t on wave s % 16 of workgroup t, as in the dispatch kernels (FP8
-//                           cast, or 16-byte copies); the first segment's loads are issued before the layout
-//                           work, so they overlap it;
+// counts and the psum; the first token wave of token t's workgroup writes its slots, its per-rank token rows and
+// its membership; the padding waves write the padding-row list.
+//   token segments          segment s of token t on wave 16 - nt + s % 16 of workgroup t (nt = min(segments, 16):
+//                           the last waves, clear of the scan on wave 0), as in the dispatch kernels (FP8 cast,
+//                           or 16-byte copies); the first segment's loads are issued before the layout work, so
+//                           they overlap it, and its FP8 cast runs while wave 0 scans;
 //   padding-list lanes      lane q of the pass over padding row numbers finds its row by a binary search of
 //                           the padding prefix in LDS, writes the list entry and (without zero padding) the
 //                           row's metadata;
 //   zero-padding items      (row number, segment) pairs, zeros written as in the dispatch kernels.
-// The padding runs on the waves that have no token segment (at hidden 7168, 9 of the 16 waves of every token's
+// The padding runs on the waves that have no token segment (at hidden 7168, waves 0..8 of every token's
 // workgroup), beside the token segments instead of after them.
 #include <algorithm>
 
@@ -44,40 +45,50 @@ struct FusedArgs {
 
 template <bool FP8>
 __global__ __launch_bounds__(kThreads) void k_layout_dispatch_small(FusedArgs f, Params p) {
+    touch_kernargs<sizeof(FusedArgs) + sizeof(Params)>();
     const int T = p.T, K = p.K, R = p.R, E = f.E, epr = p.epr, lo = p.rank * epr;
     const TokLds L = carve_tok(layout_smem, E, K, R, epr);
     const int lane = lane_id(), w = threadIdx.x >> 6;
     const int t = blockIdx.x;                         // this workgroup's token (the grid has >= T workgroups)
     const bool tok = t < T;
+    // the token's segments go to the last nt waves (segment s on wave 16 - nt + s % 16), clear of wave 0, which
+    // runs the scan, and of the waves that count the tokens' ranks (tid < T)
+    const int nt = min(p.nstep, kWaves);
+    const int tw = w - (kWaves - nt);                 // >= 0 on the token's waves
+    const bool seg = tok && tw >= 0;
 
-    // the token's first segments (segment s on wave s % 16) and its metadata do not depend on the layout: their
-    // loads are issued with the routing table's and stay in flight through the layout work
+    // the token's first segments and its metadata do not depend on the layout: their loads are issued with the
+    // routing table's and stay in flight through the layout work
     Fp8Src v8;
     Fp8Row c8;
     u32x4 vr;
     TokenEntry te;
+    TokRow tr;
     tok_counts(f.idx, T, K, E, R, epr, f.A, lo, t, L, [&] {
-        if (tok && w < p.nstep) {
-            if (FP8) v8 = fp8_load(p, t, w, lane);
-            else vr = raw_load(p, t, w, lane);
-            if (w == 0) te = token_entry(p, t, lane);
-        }
+        // every wave issues them, with clamped operands (T >= 1 here): loads behind a branch would make the
+        // staging of the table wait for them too
+        const int tc = tok ? t : 0, sc = min(max(tw, 0), p.nstep - 1);
+        if (FP8) v8 = fp8_load_clamped(p, tc, sc, lane);
+        else vr = raw_load_clamped(p, tc, sc, lane);
+        te = token_entry_clamped(p, tc, lane);
     }, [&] {
-        // the FP8 cast needs only the token's bytes: done while the other waves count
-        if (FP8 && tok && w < p.nstep) c8 = fp8_cast(v8);
+        // while wave 0 scans: the FP8 cast of the segment and the token's rows up to the experts' starts
+        if (seg) {
+            if (FP8) c8 = fp8_cast(v8);
+            tr = tok_row_counts(L, t, K);
+        }
     });
     if (blockIdx.x == 0) write_counts(E, R, lo, epr, L.tot, L.psum, L.padpre, f.o);
 
     // token t: its rows (lane k < K: expert-major row of entry k; lane r < R: row in rank r's window), then its
-    // segments, segment s on wave s % 16
-    if (tok && w < p.nstep) {
-        int sexp, own;
-        tok_rows(L, t, K, R, lo, epr, sexp, own);
+    // segments
+    if (seg) {
+        const int sexp = tok_row_slot(L, tr, K, lo, epr), own = tok_row_own(L, tr, R);
         const int own_here = readlane(own, p.rank);        // the token's row among this rank's tokens
         const int ds = p.token_major ? (lane == 0 ? own_here : -1) : sexp;
         const int js = (p.send_slot != nullptr && lane < R && lane != p.rank) ? own : -1;
         const uint64_t lmask = ballot(ds >= 0), smask = ballot(js >= 0);
-        if (w == 0) {
+        if (tw == 0) {
             if (lane < K) f.slot_ws[(int64_t)t * K + lane] = sexp;
             if (lane < R) {
                 f.rows_ws[(int64_t)t * R + lane] = own;
@@ -86,19 +97,18 @@ __global__ __launch_bounds__(kThreads) void k_layout_dispatch_small(FusedArgs f,
             token_meta(p, t, lane, ds, js, lmask, smask, &te);
         }
         if ((lmask | smask) != 0) {
-            for (int s = w; s < p.nstep; s += kWaves) {
-                if (FP8) fp8_store(p, s, lane, s == w ? c8 : fp8_cast(fp8_load(p, t, s, lane)), ds, js, lmask, smask);
-                else raw_emit(p, t, s, lane, s == w ? vr : raw_load(p, t, s, lane), ds, js, lmask, smask);
+            for (int s = tw; s < p.nstep; s += kWaves) {
+                if (FP8) fp8_store(p, s, lane, s == tw ? c8 : fp8_cast(fp8_load(p, t, s, lane)), ds, js, lmask, smask);
+                else raw_emit(p, t, s, lane, s == tw ? vr : raw_load(p, t, s, lane), ds, js, lmask, smask);
             }
         }
+        return;
     }
 
-    // padding, on the waves without a token segment (waves nt.. of the token workgroups, every wave of the
-    // workgroups past T), so that it runs beside the token segments: the row list (and, without zero padding,
-    // the rows' metadata), one row number per lane; then, with zero padding, (row number, segment) items
-    const int nt = min(p.nstep, kWaves);
-    if (tok && w < nt) return;
-    const int64_t iw = tok ? (int64_t)blockIdx.x * (kWaves - nt) + (w - nt)
+    // padding, on the waves without a token segment (waves 0 .. 15 - nt of the token workgroups, every wave of
+    // the workgroups past T), so that it runs beside the token segments: the row list (and, without zero
+    // padding, the rows' metadata), one row number per lane; then, with zero padding, (row number, segment) items
+    const int64_t iw = tok ? (int64_t)blockIdx.x * (kWaves - nt) + w
                            : (int64_t)T * (kWaves - nt) + ((int64_t)blockIdx.x - T) * kWaves + w;
     const int npad = L.padpre[epr];
     const bool meta_only = !p.token_major && !p.zero_pad && (p.recv_src != nullptr || p.recv_w != nullptr);

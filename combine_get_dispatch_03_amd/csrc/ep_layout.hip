@@ -373,19 +373,27 @@ __global__ __launch_bounds__(kThreads) void k_layout_finalize(
 }
 
 // ---- single-tile path (T <= 256): one launch, one workgroup per token -------------------------------------
-// Workgroup t stages the table and counts in LDS (tok_counts in ep_layout_core.hpp), then its wave 0 writes
+// Workgroup t stages the table and counts in LDS (tok_counts in ep_layout_core.hpp), then its last wave writes
 // token t's slots, per-rank rows and membership; block 0 writes the counts; wave g of the grid writes the
 // padding rows of the local experts g, g + waves, ...
 __global__ __launch_bounds__(kThreads) void k_layout_tokens(
     const int64_t* __restrict__ idx, int T, int K, int E, int R, int rank, int epr, int A,
     int32_t* __restrict__ slot, int32_t* __restrict__ send_slot, uint8_t* __restrict__ in_rank_out, Outputs o) {
+    // idx, 7 ints (+ 4 bytes of alignment), 3 pointers, then o
+    constexpr int kArgBytes = 8 + 7 * 4 + 4 + 3 * 8 + (int)sizeof(Outputs);
+    static_assert(kArgBytes == 128, "k_layout_tokens arguments");
+    touch_kernargs<kArgBytes>();
     const TokLds L = carve_tok(layout_smem, E, K, R, epr);
     const int lo = rank * epr, t = blockIdx.x, lane = lane_id(), w = threadIdx.x >> 6;
-    tok_counts(idx, T, K, E, R, epr, A, lo, t, L, [] {}, [] {});
+    // the token's rows on the last wave: their counting part runs while wave 0 scans
+    const bool mine = t < T && w == kWaves - 1;
+    TokRow tr;
+    tok_counts(idx, T, K, E, R, epr, A, lo, t, L, [] {}, [&] {
+        if (mine) tr = tok_row_counts(L, t, K);
+    });
     if (blockIdx.x == 0) write_counts(E, R, lo, epr, L.tot, L.psum, L.padpre, o);
-    if (t < T && w == 0) {
-        int sexp, own;
-        tok_rows(L, t, K, R, lo, epr, sexp, own);
+    if (mine) {
+        const int sexp = tok_row_slot(L, tr, K, lo, epr), own = tok_row_own(L, tr, R);
         if (lane < K) slot[(int64_t)t * K + lane] = sexp;
         if (lane < R) {
             send_slot[(int64_t)t * R + lane] = own;

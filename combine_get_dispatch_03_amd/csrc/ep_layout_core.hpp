@@ -57,6 +57,16 @@ struct Outputs {
     int32_t* invalid;         // caller, nullable
 };
 
+// ceil(c / A) * A for 0 <= c and c + A - 1 <= INT32_MAX (the receive-capacity limit), 1 <= A <= 65536: the fp64
+// product n * (1 / A) is within 2^-21 of n / A, so its floor is off only when n / A is a whole number, and then
+// by one, which the correction restores.  A few instructions instead of an integer division.
+__device__ __forceinline__ int align_up(int c, int A, double inv_a) {
+    const uint32_t n = (uint32_t)c + (uint32_t)A - 1u;
+    uint32_t q = (uint32_t)((double)n * inv_a);
+    if ((q + 1u) * (uint32_t)A <= n) ++q;
+    return (int)(q * (uint32_t)A);
+}
+
 // Aligned exclusive scan of the local experts' counts (total[lo + j]) into psum[0..epr] and of their padding
 // counts into padpre[0..epr], in LDS.  Every thread of the block calls it; it ends with a barrier.  Up to 256
 // local experts one wave does it (4 consecutive experts per lane, two DPP wave scans, one barrier); beyond
@@ -65,13 +75,15 @@ __device__ void local_scan(int epr, int lo, int A, const int* total, int* psum, 
     const int tid = threadIdx.x;
     if (epr <= 4 * kWave) {
         if (tid < kWave) {
-            int pad[4], gap[4], s0 = 0, s1 = 0;
+            int c[4], pad[4], gap[4], s0 = 0, s1 = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) c[j] = total[lo + min(4 * tid + j, epr - 1)];   // issued together
+            const double inv_a = 1.0 / (double)A;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int e = 4 * tid + j;
-                const int c = e < epr ? total[lo + e] : 0;
-                pad[j] = ((c + A - 1) / A) * A;
-                gap[j] = pad[j] - c;
+                const int cj = 4 * tid + j < epr ? c[j] : 0;
+                pad[j] = align_up(cj, A, inv_a);
+                gap[j] = pad[j] - cj;
                 s0 += pad[j];
                 s1 += gap[j];
             }
@@ -96,7 +108,7 @@ __device__ void local_scan(int epr, int lo, int A, const int* total, int* psum, 
         return;
     }
     const int c = tid < epr ? total[lo + tid] : 0;
-    const int padded = ((c + A - 1) / A) * A;
+    const int padded = align_up(c, A, 1.0 / (double)A);
     int ex, expad, all, allpad;
     block_exclusive_scan2(padded, padded - c, scratch, ex, expad, all, allpad);
     if (tid < epr) {
@@ -150,6 +162,7 @@ __device__ __forceinline__ int pad_row_of(int q, int epr, const int* psum, const
 // these counts with LDS atomic adds (the order of the adds does not change a count, so the result is
 // deterministic), then the aligned scan of the local experts.
 struct TokLds {
+    uint64_t* tmask;   // [256]    the ranks each token has an expert on (atomic ORs of its entries)
     int* ent;       // [256 * K]   staged expert ids (-1 none, kBad invalid)
     int* tot;       // [E + R + 1] column totals: entries per expert | tokens per rank | invalid entries
     int* bef;       // [E]         entries per expert in the tokens before t
@@ -160,13 +173,15 @@ struct TokLds {
 };
 
 __host__ __device__ inline size_t tok_lds_bytes(int E, int K, int R, int epr) {
-    return sizeof(int) * ((size_t)kTile * K + 2 * (size_t)E + 2 * (size_t)R + 1 + 2 * (size_t)(epr + 1) +
+    return sizeof(uint64_t) * kTile +
+           sizeof(int) * ((size_t)kTile * K + 2 * (size_t)E + 2 * (size_t)R + 1 + 2 * (size_t)(epr + 1) +
                           2 * (size_t)kWaves);
 }
 
 __device__ inline TokLds carve_tok(unsigned char* base, int E, int K, int R, int epr) {
     TokLds L;
-    L.ent = reinterpret_cast<int*>(base);
+    L.tmask = reinterpret_cast<uint64_t*>(base);
+    L.ent = reinterpret_cast<int*>(L.tmask + kTile);
     L.tot = L.ent + kTile * K;
     L.bef = L.tot + E + R + 1;
     L.rbef = L.bef + E;
@@ -180,12 +195,12 @@ __device__ inline TokLds carve_tok(unsigned char* base, int E, int K, int R, int
 __device__ __forceinline__ int rank_of(int e, float inv_epr) { return (int)(((float)e + 0.5f) * inv_epr); }
 
 // Stage the table, count (totals and counts before token t; t >= T counts nothing before), scan.  `pre` runs
-// right after the entry loads are issued (loads that do not depend on the layout go there), `mid` after this
-// thread's counting (work on those loads' data can overlap the other waves' counting there).  Every thread of
-// the block calls it; it ends with a barrier.
-template <class Pre, class Mid>
+// right after the entry loads are issued (loads that do not depend on the layout go there), `post` once the
+// counts are complete, before the scan, which wave 0 runs alone (work of the other waves that needs the counts
+// but not the scan overlaps it there).  Every thread of the block calls it; it ends with a barrier.
+template <class Pre, class Post>
 __device__ inline void tok_counts(const int64_t* __restrict__ idx, int T, int K, int E, int R, int epr, int A,
-                                  int lo, int t, const TokLds& L, Pre pre, Mid mid) {
+                                  int lo, int t, const TokLds& L, Pre pre, Post post) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int nent = T * K;
     const int tb = t < T ? t : 0;                    // tokens counted as before: none for a workgroup past T
@@ -200,6 +215,7 @@ __device__ inline void tok_counts(const int64_t* __restrict__ idx, int T, int K,
     for (int i = tid; i < E + R + 1; i += kThreads) L.tot[i] = 0;
     for (int i = tid; i < E; i += kThreads) L.bef[i] = 0;
     if (tid < R) L.rbef[tid] = 0;
+    if (tid < kTile) L.tmask[tid] = 0ull;
     int st[kMaxEntriesPerThread];
 #pragma unroll
     for (int u = 0; u < kMaxEntriesPerThread; ++u) {
@@ -208,6 +224,8 @@ __device__ inline void tok_counts(const int64_t* __restrict__ idx, int T, int K,
         if (j < nent) L.ent[j] = st[u];
     }
     __syncthreads();
+    // per entry: its expert's total, its expert's count before token t, and its rank's bit in its token's mask
+    const float inv_epr = 1.0f / (float)epr, inv_k = 1.0f / (float)K;
     int inv = 0;
 #pragma unroll
     for (int u = 0; u < kMaxEntriesPerThread; ++u) {
@@ -216,52 +234,73 @@ __device__ inline void tok_counts(const int64_t* __restrict__ idx, int T, int K,
         if (e >= 0) {
             atomicAdd(&L.tot[e], 1);
             if (j < tb * K) atomicAdd(&L.bef[e], 1);
+            // token of entry j = floor((j + 0.5) / K) in fp32: exact for j < 2^13, K <= 32
+            atomicOr(reinterpret_cast<unsigned long long*>(&L.tmask[(int)(((float)j + 0.5f) * inv_k)]),
+                     1ull << rank_of(e, inv_epr));
         }
         inv += popc64(ballot(e == kBad));
     }
     if (lane == 0 && inv != 0) atomicAdd(&L.tot[E + R], inv);
-    const float inv_epr = 1.0f / (float)epr;
-    if ((tid & ~(kWave - 1)) < T) {                  // waves holding tokens (token tid on thread tid)
-        uint64_t m = 0ull;                           // the ranks token tid goes to
-        if (tid < T)
-            for (int k = 0; k < K; ++k) {
-                const int e = L.ent[tid * K + k];
-                if (e >= 0) m |= 1ull << rank_of(e, inv_epr);
-            }
-        // per rank present in the wave: one ballot for its tokens, one for those before t, one LDS add each
+    __syncthreads();
+    // tokens per rank and those before t, from the token masks, on waves 4..7 (token tid - 256) while wave 0
+    // scans: per rank present in the wave, one ballot for its tokens, one for those before t, one LDS add each
+    // (nothing reads these counts before the scan's barrier)
+    const int rt = tid - kTile;
+    if (rt >= 0 && rt < kTile && (rt & ~(kWave - 1)) < T) {
+        const uint64_t m = rt < T ? L.tmask[rt] : 0ull;
         const uint64_t present = R > 32 ? ((uint64_t)wave_or((uint32_t)(m >> 32)) << 32) | wave_or((uint32_t)m)
                                         : (uint64_t)wave_or((uint32_t)m);
         for (uint64_t rr = present; rr != 0; rr &= rr - 1) {
             const int r = __builtin_ctzll(rr);
             const bool bit = (m >> r) & 1ull;
-            const int all = popc64(ballot(bit)), before = popc64(ballot(bit && tid < tb));
+            const int all = popc64(ballot(bit)), before = popc64(ballot(bit && rt < tb));
             if (lane == 0) {
                 atomicAdd(&L.tot[E + r], all);
                 if (before != 0) atomicAdd(&L.rbef[r], before);
             }
         }
     }
-    mid();
-    __syncthreads();
+    post();
     local_scan(epr, lo, A, L.tot, L.psum, L.padpre, L.scratch);
 }
 
 // Token t's rows (t < T), in one wave: lane k < K gets the expert-major row of entry k (-1 if the expert is not
 // local or the entry not valid), lane r < R the token's row in rank r's window (-1 if it has no expert on r).
-// Each lane reads one entry from LDS; the other entries are read back from their lanes as scalars.
-__device__ inline void tok_rows(const TokLds& L, int t, int K, int R, int lo, int epr, int& sexp, int& own) {
+// tok_row_counts needs the expert counts only (it can run while wave 0 scans); tok_row_slot adds the expert's
+// aligned start from the scan, and tok_row_own reads the rank's count before t (complete, like the scan, at
+// the scan's barrier).  Every lane reads all K entries of the token (the same LDS words for every lane, so
+// broadcast reads issued together) and counts the copies of its own entry before it.
+struct TokRow {
+    int e;            // lane k < K: entry k
+    int before;       // lane k < K: entries of e in the tokens before t, plus copies of e among entries 0..k-1
+    uint64_t ranks;   // the ranks the token has an expert on
+};
+
+__device__ inline TokRow tok_row_counts(const TokLds& L, int t, int K) {
     const int lane = lane_id();
-    const float inv_epr = 1.0f / (float)epr;
-    const int e = lane < K ? L.ent[t * K + lane] : -1;
-    int dup = 0;                                     // copies of e among entries 0..lane-1
-    bool has = false;                                // lane < R: an entry of the token is on rank `lane`
-    for (int k = 0; k < K; ++k) {
-        const int ek = readlane(e, k);
-        dup += (k < lane && ek == e) ? 1 : 0;
-        has = has || (ek >= 0 && rank_of(ek, inv_epr) == lane);
+    const int* ent = L.ent + t * K;
+    TokRow r;
+    r.e = lane < K ? ent[lane] : -1;
+    r.ranks = L.tmask[t];
+    int dup = 0;
+    for (int k0 = 0; k0 < K; k0 += 8) {
+        int q[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) q[u] = ent[min(k0 + u, K - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) dup += (k0 + u < lane && q[u] == r.e) ? 1 : 0;
     }
-    sexp = (lane < K && e >= lo && e < lo + epr) ? L.psum[e - lo] + L.bef[e] + dup : -1;
-    own = (lane < R && has) ? L.rbef[lane] : -1;
+    r.before = r.e >= 0 ? L.bef[r.e] + dup : 0;
+    return r;
+}
+
+__device__ inline int tok_row_slot(const TokLds& L, const TokRow& r, int K, int lo, int epr) {
+    return (lane_id() < K && r.e >= lo && r.e < lo + epr) ? L.psum[r.e - lo] + r.before : -1;
+}
+
+__device__ inline int tok_row_own(const TokLds& L, const TokRow& r, int R) {
+    const int lane = lane_id();
+    return (lane < R && ((r.ranks >> lane) & 1ull) != 0) ? L.rbef[lane] : -1;
 }
 
 }  // namespace
