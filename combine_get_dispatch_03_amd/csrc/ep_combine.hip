@@ -108,6 +108,9 @@ __device__ __forceinline__ void gather_all(float* acc, const u32x4* base, int64_
 }
 
 __global__ __launch_bounds__(kBlock) void k_combine(Params p) {
+    // both argument lines in one round trip (the fields are read on demand otherwise, one miss after another):
+    // decode combine 3.29 -> 3.12 us, prefill 87.1 -> 86.4 us (in the dispatch kernels the same cost time)
+    touch_kernargs<sizeof(Params)>();
     __shared__ int cs_lds[kWavesPerBlock][kWave];
     __shared__ float cw_lds[kWavesPerBlock][kWave];
     const int lane = lane_id(), wv = threadIdx.x >> 6;
@@ -160,6 +163,7 @@ struct ReduceParams {
 };
 
 __global__ __launch_bounds__(kBlock) void k_combine_reduce(ReduceParams p) {
+    touch_kernargs<sizeof(ReduceParams)>();
     __shared__ int cs_lds[kWavesPerBlock][kWave];
     const int lane = lane_id(), wv = threadIdx.x >> 6;
     const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + wv;

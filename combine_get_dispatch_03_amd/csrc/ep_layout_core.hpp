@@ -203,13 +203,14 @@ __device__ inline void tok_counts(const int64_t* __restrict__ idx, int T, int K,
                                   int lo, int t, const TokLds& L, Pre pre, Post post) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int nent = T * K;
+    const int npass = (nent + kThreads - 1) / kThreads;   // entries per thread (uniform): passes past it are skipped
     const int tb = t < T ? t : 0;                    // tokens counted as before: none for a workgroup past T
     static_assert(kTile * kMaxTopk <= kMaxEntriesPerThread * kThreads, "one staging pass per tile");
     int64_t v[kMaxEntriesPerThread];
 #pragma unroll
     for (int u = 0; u < kMaxEntriesPerThread; ++u) {
         const int j = u * kThreads + tid;
-        v[u] = j < nent ? idx[j] : -1;
+        v[u] = (u < npass && j < nent) ? idx[j] : -1;
     }
     pre();
     for (int i = tid; i < E + R + 1; i += kThreads) L.tot[i] = 0;
@@ -221,7 +222,7 @@ __device__ inline void tok_counts(const int64_t* __restrict__ idx, int T, int K,
     for (int u = 0; u < kMaxEntriesPerThread; ++u) {
         const int j = u * kThreads + tid;
         st[u] = (v[u] >= 0 && v[u] < E) ? (int)v[u] : (v[u] == -1 ? -1 : kBad);
-        if (j < nent) L.ent[j] = st[u];
+        if (u < npass && j < nent) L.ent[j] = st[u];
     }
     __syncthreads();
     // per entry: its expert's total, its expert's count before token t, and its rank's bit in its token's mask
@@ -229,6 +230,7 @@ __device__ inline void tok_counts(const int64_t* __restrict__ idx, int T, int K,
     int inv = 0;
 #pragma unroll
     for (int u = 0; u < kMaxEntriesPerThread; ++u) {
+        if (u >= npass) break;
         const int j = u * kThreads + tid;
         const int e = j < nent ? st[u] : -1;
         if (e >= 0) {
