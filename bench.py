@@ -269,6 +269,8 @@ class Probe:
         self.lib.probe_dispatch_writes.argtypes = [Pt, I, I, Pt, I, Pt, Pt, Pt, Pt, I, Pt]
         self.lib.probe_dispatch_reads.restype = I
         self.lib.probe_dispatch_reads.argtypes = [Pt, Pt, I, I, I, Pt, Pt]
+        self.lib.probe_copy.restype = I
+        self.lib.probe_copy.argtypes = [Pt, Pt, I64, Pt]
         self.junk = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev).fill_(3)
         self.sink = torch.zeros(1, dtype=torch.int32, device=dev)
 
@@ -281,6 +283,11 @@ class Probe:
         rc = self.lib.probe_flush(self.junk.data_ptr(), self.junk.numel(), self.sink.data_ptr(), self._stream())
         if rc != 0:
             raise RuntimeError("probe_flush failed (%d)" % rc)
+
+    def copy(self, src, dst):
+        rc = self.lib.probe_copy(src.data_ptr(), dst.data_ptr(), src.numel() * src.element_size(), self._stream())
+        if rc != 0:
+            raise RuntimeError("probe_copy failed (%d)" % rc)
 
 
 def events_us(fn, n):
@@ -602,20 +609,28 @@ def measure_epilogues(ep, W, dev, n):
                             partial_rows=n_part))
 
 
-def measure_copy_ceiling(dev, n, mib=1024):
-    """A plain device-to-device copy of `mib` MiB (torch's copy_, the runtime's copy kernel), timed with events
-    over n back-to-back copies: the streaming rate this GPU reaches on a flat read + flat write, as context for
-    the kernels' rates (not the roofline's denominator, which is the published 8 TB/s)."""
+def measure_copy_ceiling(dev, n, probe, mib=1024):
+    """A plain device-to-device copy of `mib` MiB, timed with events over n back-to-back copies: the streaming rate
+    this GPU reaches on a flat read + flat write, as context for the kernels' rates (not the roofline's
+    denominator, which is the published 8 TB/s).  `us` / `GBps` time a flat copy kernel (bench_probe.hip: one wave
+    per 1 KiB, non-temporal 16-byte loads and stores); torch's copy_ (the runtime's copy kernel) is reported beside
+    it and is slower on this chip."""
     import torch
 
     a = torch.empty(mib << 20, dtype=torch.uint8, device=dev).fill_(1)
     b = torch.empty_like(a)
     for _ in range(3):
+        probe.copy(a, b)
         b.copy_(a)
-    us = events_us(lambda: b.copy_(a), n)
+    us = events_us(lambda: probe.copy(a, b), n)
+    us_torch = events_us(lambda: b.copy_(a), n)
+    ok = bool(torch.equal(a[:1 << 20], b[:1 << 20]))
     del a, b
-    return dict(bytes_per_copy=2 * (mib << 20), us=round(us, 2), GBps=round(rate(2 * (mib << 20), us), 1),
-                note="device copy of %d MiB (read + write bytes), events around %d copies" % (mib, n))
+    nb = 2 * (mib << 20)
+    return dict(bytes_per_copy=nb, us=round(us, 2), GBps=round(rate(nb, us), 1), torch_copy_us=round(us_torch, 2),
+                torch_copy_GBps=round(rate(nb, us_torch), 1), copied=ok,
+                note="device copy of %d MiB (read + write bytes), events around %d copies: a flat copy kernel (one "
+                     "wave per 1 KiB) and torch's copy_" % (mib, n))
 
 
 def measure_decode(ep, W, dev, n):
@@ -783,7 +798,7 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     # per-call table of every workload (the headline one first)
-    probe = Probe(dev) if (args.flushed or args.bound) else None
+    probe = Probe(dev) if (args.flushed or args.bound or args.copy_ceiling) else None
     names = [args.workload] + ([n for n in ALL_WORKLOADS if n != args.workload] if args.workloads else [])
     table = {}
     for name in names:
@@ -809,7 +824,7 @@ def main():
         else None
     epi = measure_epilogues(ep, W, dev, args.steps) if args.epilogues else None
     decode = measure_decode(ep, W, dev, args.steps) if args.decode else None
-    copy_ceiling = measure_copy_ceiling(dev, 20) if args.copy_ceiling else None
+    copy_ceiling = measure_copy_ceiling(dev, 20, probe) if args.copy_ceiling else None
     del probe
 
     cpu = None

@@ -1,15 +1,18 @@
 // bench_probe.hip -- measurement probes for bench.py (not part of the library, and not behind include/ep.h).
 //
-// Each probe replays one half of the FP8 dispatch's memory traffic with the dispatch's own work split and
-// launch shape (one wave per 1024-channel segment of a token, then padding segments), so that bench.py can
-// time what the hardware gives for that address stream alone:
+// The two dispatch probes each replay one half of the FP8 dispatch's memory traffic with the dispatch's own work
+// split and launch shape (one wave per 1024-channel segment of a token, then padding segments), so that bench.py
+// can time what the hardware gives for that address stream alone; the other two are a cache flush and a plain
+// copy:
 //   probe_dispatch_writes  every store of an FP8 dispatch with zero padding -- the routed rows' e4m3 bytes
 //                          (16-byte non-temporal stores to each destination row), their scales and row metadata,
 //                          and the zero-padding rows -- and no source reads;
 //   probe_dispatch_reads   every source read of that dispatch -- the token rows (32 bytes per lane, non-temporal)
 //                          and the slot map -- and no stores;
-//   probe_flush            plain loads over a large buffer (a cache flush between timed samples).
-// The bytes stored are a constant pattern, so these say nothing about correctness; they bound the dispatch's
+//   probe_flush            plain loads over a large buffer (a cache flush between timed samples);
+//   probe_copy             a flat copy, one wave per 1 KiB (a 16-byte non-temporal load, then a store per lane):
+//                          the rate this chip gives a 1 : 1 read / write stream, as context for the kernels.
+// The dispatch probes store a constant pattern, so they say nothing about correctness; they bound the dispatch's
 // time from below: on HBM the reads and the writes share each channel's data bus.
 #include <hip/hip_runtime.h>
 
@@ -118,6 +121,12 @@ __global__ __launch_bounds__(kBlock) void k_probe_flush(const u32x4* p, int64_t 
     if (acc == never) sink[0] = (int32_t)acc;
 }
 
+__global__ __launch_bounds__(kBlock) void k_probe_copy(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                       int64_t n16) {
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i < n16) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
 }  // namespace
 
 extern "C" {
@@ -169,6 +178,14 @@ int probe_flush(const void* buf, int64_t bytes, int32_t* sink, void* stream) {
     if (bytes < 16) return -1;
     hipLaunchKernelGGL(k_probe_flush, dim3(2048), dim3(kBlock), 0, static_cast<hipStream_t>(stream),
                        static_cast<const u32x4*>(buf), bytes / 16, sink, 0x9E3779B9u);
+    return (int)hipGetLastError();
+}
+
+int probe_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+    if (bytes < 16 || bytes % 16 != 0 || bytes / 16 / kBlock >= (int64_t)1 << 31) return -1;
+    const int64_t n16 = bytes / 16;
+    hipLaunchKernelGGL(k_probe_copy, dim3((unsigned)((n16 + kBlock - 1) / kBlock)), dim3(kBlock), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16);
     return (int)hipGetLastError();
 }
 
