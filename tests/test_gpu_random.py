@@ -18,8 +18,8 @@ NCASES = 40
 
 def _case(seed):
     rng = np.random.default_rng(1000 + seed)
-    R = int(rng.choice([1, 1, 2, 4, 8, 16]))
-    epr = int(rng.integers(1, 1024 // R + 1)) if rng.random() < 0.3 else int(rng.integers(1, 65))
+    R = int(rng.choice([1, 1, 2, 4, 8, 16, 32, 64]))   # R > 32 uses the upper half of the 64-bit rank sets
+    epr = int(rng.integers(1, 1024 // R + 1)) if rng.random() < 0.3 else int(rng.integers(1, min(64, 1024 // R) + 1))
     E = R * epr
     T = int(rng.choice([0, 1, int(rng.integers(2, 256)), 256, int(rng.integers(257, 700))]))
     K = int(rng.integers(1, min(E, 12) + 1)) if rng.random() < 0.8 else int(rng.integers(1, 33))
