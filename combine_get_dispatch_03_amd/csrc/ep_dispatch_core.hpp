@@ -49,24 +49,17 @@ struct Params {
 
 // Metadata of token t's rows, written by the wave of its segment 0.  ds (lanes < K expert-major, lane 0
 // token-major) and js (lanes < R) are the token's local and send rows, lmask / smask their ballots.
-// The token's routing weight and expert id for lane k < K (weight 1 without weights, id -1 past K).
+// The token's routing weight and expert id for lane k < K, as loaded ahead of token_meta by token_entry.  The
+// loads take the entry index clamped into the token's entries and a valid address in place of absent weights, so
+// that they need no branch; the values are raw (lanes >= K hold entry K - 1, and without weights the weight is a
+// bit pattern of the ids), and token_meta applies the masks where it uses them, so that no early use makes a wait
+// for these loads wait for every load issued before them.
 struct TokenEntry {
     float w;
     int64_t e;
 };
 
 __device__ __forceinline__ TokenEntry token_entry(const Params& p, int t, int lane) {
-    TokenEntry te;
-    te.w = (lane < p.K && p.w != nullptr) ? p.w[(int64_t)t * p.K + lane] : 1.0f;
-    te.e = lane < p.K ? p.topk_idx[(int64_t)t * p.K + lane] : -1;
-    return te;
-}
-
-// token_entry's loads with the entry index clamped into the token's entries and a valid address in place of
-// absent weights, so that they need no branch.  The values are raw (lanes >= K hold entry K - 1, and the weight
-// is a bit pattern of the ids without weights): token_meta applies the masks when it uses them, so that no
-// early use makes a wait for these loads wait for every load issued before them.
-__device__ __forceinline__ TokenEntry token_entry_clamped(const Params& p, int t, int lane) {
     const int64_t j = (int64_t)t * p.K + min(lane, p.K - 1);
     const float* w = p.w != nullptr ? p.w : reinterpret_cast<const float*>(p.topk_idx);   // T*K*8 bytes
     TokenEntry te;
@@ -81,7 +74,7 @@ __device__ __forceinline__ void token_meta(const Params& p, int t, int lane, int
                         (p.token_major && lmask != 0 && p.recv_topk_idx != nullptr);
     float wk;
     int64_t e;
-    if (pre != nullptr) {   // masks as in token_entry (a no-op on its values; needed for token_entry_clamped's)
+    if (pre != nullptr) {   // token_entry's raw values, masked here
         wk = (lane < p.K && p.w != nullptr) ? pre->w : 1.0f;
         e = lane < p.K ? pre->e : -1;
     } else {

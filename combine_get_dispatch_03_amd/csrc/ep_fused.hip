@@ -70,7 +70,7 @@ __global__ __launch_bounds__(kThreads) void k_layout_dispatch_small(FusedArgs f,
         const int tc = tok ? t : 0, sc = min(max(tw, 0), p.nstep - 1);
         if (FP8) v8 = fp8_load_clamped(p, tc, sc, lane);
         else vr = raw_load_clamped(p, tc, sc, lane);
-        te = token_entry_clamped(p, tc, lane);
+        te = token_entry(p, tc, lane);
     }, [&] {
         // while wave 0 scans: the FP8 cast of the segment and the token's rows up to the experts' starts
         if (seg) {
