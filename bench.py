@@ -271,6 +271,8 @@ class Probe:
         self.lib.probe_dispatch_reads.argtypes = [Pt, Pt, I, I, I, Pt, Pt]
         self.lib.probe_copy.restype = I
         self.lib.probe_copy.argtypes = [Pt, Pt, I64, Pt]
+        self.lib.probe_send_writes.restype = I
+        self.lib.probe_send_writes.argtypes = [Pt, Pt, I, I, I, Pt, Pt, Pt, Pt, Pt, Pt, Pt, I, Pt]
         self.junk = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev).fill_(3)
         self.sink = torch.zeros(1, dtype=torch.int32, device=dev)
 
@@ -488,7 +490,6 @@ def measure_dispatch_bound(ep, W, dev, n, probe):
       sum bounds the dispatch from below;
     * the product dispatch without zero padding (routed rows only) and with alignment 1 (no padding rows at
       all), and the increment that zero padding adds."""
-    import numpy as np
     import torch
 
     inp = W.make_inputs("prefill")
@@ -499,17 +500,8 @@ def measure_dispatch_bound(ep, W, dev, n, probe):
     h, lay = ep.ep_get_layout(idx, E, 1, 0, A)
     d = ep.ep_dispatch(h, x, w, fp8=True, do_zero_padding=True)
     torch.cuda.synchronize()
-    src = d["recv_src_idx"].cpu().numpy()
     used = int(lay["psum_num_recv_tokens_per_expert"][-1].item())
-    rows = np.nonzero(src[:used] >= 0)[0]
-    pads = np.nonzero(src[:used] < 0)[0].astype(np.int32)
-    toks = src[rows]
-    order = np.lexsort((rows, toks))
-    token_rows = np.full((T, K), -1, np.int32)
-    kpos = np.zeros(T, np.int64)
-    for r, t in zip(rows[order], toks[order]):
-        token_rows[t, kpos[t]] = r
-        kpos[t] += 1
+    token_rows, V, pads = local_rows_by_token(d["recv_src_idx"].cpu().numpy(), used, T, K)
     tr = torch.from_numpy(token_rows).to(dev)
     pr = torch.from_numpy(pads).to(dev) if pads.size else torch.zeros(1, dtype=torch.int32, device=dev)
     lib, stream = probe.lib, probe._stream
@@ -524,7 +516,7 @@ def measure_dispatch_bound(ep, W, dev, n, probe):
         rc = lib.probe_dispatch_reads(x.data_ptr(), tr.data_ptr(), T, K, H, probe.sink.data_ptr(), stream())
         assert rc == 0, rc
 
-    V, P = rows.size, pads.size
+    P = pads.size
     wbytes = (V + P) * (H + 4 * G + 8)
     rbytes = T * 2 * H + T * K * 4
     full = lambda: ep.ep_dispatch(h, x, w, fp8=True, do_zero_padding=True, out=d)
@@ -607,6 +599,80 @@ def measure_epilogues(ep, W, dev, n):
                            received_rows=n_valid, placed_rows=V),
         combine_reduce=dict(us=round(t_red, 2), bytes=b_red, GBps=round(rate(b_red, t_red), 1),
                             partial_rows=n_part))
+
+
+def local_rows_by_token(recv_src, used, T, K):
+    """[T, K] expert-major rows of each token's local entries (in row order, -1 past them) and the padding rows,
+    from the dispatch's recv_src_idx over the rows in use."""
+    import numpy as np
+
+    src = recv_src[:used]
+    rows = np.nonzero(src >= 0)[0]
+    pads = np.nonzero(src < 0)[0].astype(np.int32)
+    toks = src[rows]
+    order = np.lexsort((rows, toks))
+    token_rows = np.full((T, K), -1, np.int32)
+    kpos = np.zeros(T, np.int64)
+    for r, t in zip(rows[order], toks[order]):
+        token_rows[t, kpos[t]] = r
+        kpos[t] += 1
+    return token_rows, rows.size, pads
+
+
+def measure_send_bound(ep, W, dev, n, probe):
+    """The FP8 dispatch with send windows on the ep8 workload (rank 0 of 8, no zero padding), taken apart like the
+    prefill dispatch: its stores alone (probe_send_writes: the same local expert-major rows and window rows with
+    their scales, the local rows' metadata and the window rows' source index, in the same work split, no reads)
+    and its source reads alone (probe_dispatch_reads: the token rows and the slot map)."""
+    import numpy as np
+    import torch
+
+    inp = W.make_inputs("ep8")
+    cfg = inp["cfg"]
+    T, K, E, R, A, H = (cfg.num_tokens, cfg.num_topk, cfg.num_experts, cfg.num_ranks, cfg.expert_alignment,
+                        cfg.hidden)
+    G = H // 128
+    idx, w, x = inp["topk_idx"].to(dev), inp["topk_weights"].to(dev), inp["x"].to(dev)
+    h, lay = ep.ep_get_layout(idx, E, R, cfg.rank, A)
+    d = ep.ep_dispatch(h, x, w, fp8=True)
+    torch.cuda.synchronize()
+    used = int(lay["psum_num_recv_tokens_per_expert"][-1].item())
+    token_rows, V, _ = local_rows_by_token(d["recv_src_idx"].cpu().numpy(), used, T, K)
+    in_rank = lay["is_token_in_rank"].cpu().numpy().astype(bool)
+    send_rows = np.where(in_rank, np.cumsum(in_rank, axis=0) - 1, -1).astype(np.int32)   # row in rank r's window
+    send_rows[:, cfg.rank] = -1
+    S = int((send_rows >= 0).sum())
+    tr = torch.from_numpy(token_rows).to(dev)
+    sr = torch.from_numpy(send_rows).to(dev)
+    lib, stream = probe.lib, probe._stream
+
+    def writes():
+        rc = lib.probe_send_writes(tr.data_ptr(), sr.data_ptr(), T, K, R, d["recv_x"].data_ptr(),
+                                   d["recv_x_scales"].data_ptr(), d["recv_src_idx"].data_ptr(),
+                                   d["recv_topk_weights"].data_ptr(), d["send_x"].data_ptr(),
+                                   d["send_x_scales"].data_ptr(), d["send_src_idx"].data_ptr(), H, stream())
+        assert rc == 0, rc
+
+    def reads():
+        rc = lib.probe_dispatch_reads(x.data_ptr(), tr.data_ptr(), T, K, H, probe.sink.data_ptr(), stream())
+        assert rc == 0, rc
+
+    full = lambda: ep.ep_dispatch(h, x, w, fp8=True, out=d)
+    us = {k: events_us(f, n) for k, f in (("writes", writes), ("reads", reads), ("dispatch", full))}
+    wbytes = V * (H + 4 * G + 8) + S * (H + 4 * G + 4)
+    rbytes = T * 2 * H + T * K * 4
+    bm = bytes_model(cfg, dict(V=V, P=used - V, N_send=S))
+    s_us = us["writes"] + us["reads"]
+    h.free()
+    return dict(
+        note="ep8 FP8 dispatch with 7 send windows: its stores alone and its source reads alone (bench_probe.hip, "
+             "same destination rows and work split), back to back, events",
+        local_rows=V, window_rows=S,
+        write_only_us=round(us["writes"], 2), write_bytes=wbytes, write_only_GBps=round(rate(wbytes, us["writes"]), 1),
+        read_only_us=round(us["reads"], 2), read_bytes=rbytes, read_only_GBps=round(rate(rbytes, us["reads"]), 1),
+        sum_us=round(s_us, 2), dispatch_us=round(us["dispatch"], 2), dispatch_bytes=bm["dispatch"],
+        bound_GBps=round(rate(bm["dispatch"], s_us), 1),
+        bound_pct_peak=round(100 * rate(bm["dispatch"], s_us) / HBM_PEAK_GBPS, 1))
 
 
 def measure_copy_ceiling(dev, n, probe, mib=1024):
@@ -820,8 +886,11 @@ def main():
         roofline["frac_in_step"] = round(rate(bm[dom], step_kernels[dom_kernel]) / HBM_PEAK_GBPS, 4)
 
     progress("dispatch bound, epilogues, decode, copy ceiling")
-    bound = measure_dispatch_bound(ep, W, dev, args.steps, probe) if (args.bound and args.workload == "prefill") \
-        else None
+    bound = None
+    if args.bound and args.workload == "prefill":
+        bound = measure_dispatch_bound(ep, W, dev, args.steps, probe)
+    elif args.bound and args.workload == "ep8":
+        bound = measure_send_bound(ep, W, dev, args.steps, probe)
     epi = measure_epilogues(ep, W, dev, args.steps) if args.epilogues else None
     decode = measure_decode(ep, W, dev, args.steps) if args.decode else None
     copy_ceiling = measure_copy_ceiling(dev, 20, probe) if args.copy_ceiling else None

@@ -9,6 +9,10 @@
 //                          and the zero-padding rows -- and no source reads;
 //   probe_dispatch_reads   every source read of that dispatch -- the token rows (32 bytes per lane, non-temporal)
 //                          and the slot map -- and no stores;
+//   probe_send_writes      the stores of an FP8 dispatch with send windows and no zero padding -- each token's
+//                          e4m3 bytes and scales to its local expert-major rows and to its row in every other
+//                          rank's window, the local rows' metadata and the window rows' source index -- and no
+//                          source reads;
 //   probe_flush            plain loads over a large buffer (a cache flush between timed samples);
 //   probe_copy             a flat copy, one wave per 1 KiB (a 16-byte non-temporal load, then a store per lane):
 //                          the rate this chip gives a 1 : 1 read / write stream, as context for the kernels.
@@ -79,6 +83,52 @@ __global__ __launch_bounds__(kBlock) void k_probe_writes(WriteArgs a) {
             a.recv_src[prow[j]] = -1;
             a.recv_w[prow[j]] = 0.0f;
         }
+    }
+}
+
+struct SendArgs {
+    const int32_t* token_rows;   // [T, K] local expert-major row of each entry, -1 none
+    const int32_t* send_rows;    // [T, R] row in rank r's window, -1 none (the own rank's column is -1)
+    uint8_t* recv_x;
+    float* recv_scales;
+    int32_t* recv_src;
+    float* recv_w;
+    uint8_t* send_x;             // [R * T, H]
+    float* send_scales;          // [R * T, H / 128]
+    int32_t* send_src;           // [R * T]
+    int T, K, R, H, nstep;
+    int64_t ntok_items;
+};
+
+__global__ __launch_bounds__(kBlock) void k_probe_send_writes(SendArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    if (gw >= a.ntok_items) return;
+    const int G = a.H / 128;
+    const int t = (int)(gw / a.nstep), s = (int)(gw % a.nstep);
+    const int d = lane < a.K ? a.token_rows[(int64_t)t * a.K + lane] : -1;
+    const int j = lane < a.R ? a.send_rows[(int64_t)t * a.R + lane] : -1;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(d >= 0), ms = __builtin_amdgcn_ballot_w64(j >= 0);
+    const u32x4 q = {0x3C3C3C3Cu, 0x3C3C3C3Cu, 0x3C3C3C3Cu, 0x3C3C3C3Cu};
+    const bool sc_lane = (lane & 7) == 0;
+    const int g = s * 8 + (lane >> 3);
+    for (uint64_t mm = m; mm != 0; mm &= mm - 1) {
+        const int row = __builtin_amdgcn_readlane(d, __builtin_ctzll(mm));
+        __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(a.recv_x + (int64_t)row * a.H) + s * kWave + lane);
+        if (sc_lane && g < G) a.recv_scales[(int64_t)row * G + g] = 1.0f;
+    }
+    for (uint64_t mm = ms; mm != 0; mm &= mm - 1) {
+        const int r = __builtin_ctzll(mm);
+        const int64_t row = (int64_t)r * a.T + __builtin_amdgcn_readlane(j, r);
+        __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(a.send_x + row * a.H) + s * kWave + lane);
+        if (sc_lane && g < G) a.send_scales[row * G + g] = 1.0f;
+    }
+    if (s == 0) {
+        if (d >= 0) {
+            a.recv_src[d] = t;
+            a.recv_w[d] = 0.125f;
+        }
+        if (j >= 0) a.send_src[(int64_t)lane * a.T + j] = t;
     }
 }
 
@@ -154,6 +204,33 @@ int probe_dispatch_writes(const int32_t* token_rows, int T, int K, const int32_t
     const int64_t nblocks = (nwaves + kWavesPerBlock - 1) / kWavesPerBlock;
     a.nwaves = nblocks * kWavesPerBlock;
     hipLaunchKernelGGL(k_probe_writes, dim3((unsigned)nblocks), dim3(kBlock), 0, static_cast<hipStream_t>(stream), a);
+    return (int)hipGetLastError();
+}
+
+// Returns 0, or -1 on an argument outside what the probe handles (nothing is launched then), or the HIP error.
+int probe_send_writes(const int32_t* token_rows, const int32_t* send_rows, int T, int K, int R, void* recv_x,
+                      float* recv_scales, int32_t* recv_src, float* recv_w, void* send_x, float* send_scales,
+                      int32_t* send_src, int H, void* stream) {
+    if (T < 1 || K < 1 || K > kWave || R < 1 || R > kWave || H < 1024 || H % 1024 != 0) return -1;
+    SendArgs a;
+    a.token_rows = token_rows;
+    a.send_rows = send_rows;
+    a.recv_x = static_cast<uint8_t*>(recv_x);
+    a.recv_scales = recv_scales;
+    a.recv_src = recv_src;
+    a.recv_w = recv_w;
+    a.send_x = static_cast<uint8_t*>(send_x);
+    a.send_scales = send_scales;
+    a.send_src = send_src;
+    a.T = T;
+    a.K = K;
+    a.R = R;
+    a.H = H;
+    a.nstep = H / 1024;
+    a.ntok_items = (int64_t)T * a.nstep;
+    const int64_t nblocks = (a.ntok_items + kWavesPerBlock - 1) / kWavesPerBlock;
+    hipLaunchKernelGGL(k_probe_send_writes, dim3((unsigned)nblocks), dim3(kBlock), 0, static_cast<hipStream_t>(stream),
+                       a);
     return (int)hipGetLastError();
 }
 

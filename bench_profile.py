@@ -34,7 +34,7 @@ SKIP = ("--no-graph --no-trace --no-cpu-baseline --no-epilogues --no-decode --no
 
 def commands(workload, out, repo="<repo>"):
     """The rocprofv3 runs a summary is made from (run from /tmp)."""
-    bound = "" if workload == "prefill" else " --no-bound"
+    bound = "" if workload in ("prefill", "ep8") else " --no-bound"   # the dispatch taken apart (probes)
     b = "python3 %s/bench.py --workload %s %s%s" % (repo, workload, SKIP, bound)
     cmds = [
         "rocprofv3 --kernel-trace --stats --output-format csv -d %s/%s_kt -o kt -- %s --steps 50 --warmup 10 "
@@ -180,6 +180,13 @@ def summarize(workload, out, traffic_json=None):
                   "; eager step %.1f us; roofline kernel %s, avg_launch_us %.2f, frac %.4f." % (
                       line["ms_per_step"] * 1e3, line["roofline"]["kernel"], line["roofline"]["avg_launch_us"],
                       line["roofline"]["frac"])]
+        b = line.get("dispatch_bound")
+        if b:
+            lines += ["", "The dispatch taken apart in the same run (bench.py `dispatch_bound`, events, us): its stores "
+                      "alone %.2f (%.1f MB, %.0f GB/s), its source reads alone %.2f (%.1f MB, %.0f GB/s), their sum "
+                      "%.2f; the dispatch %.2f." % (b["write_only_us"], b["write_bytes"] / 1e6, b["write_only_GBps"],
+                                                    b["read_only_us"], b["read_bytes"] / 1e6, b["read_only_GBps"],
+                                                    b["sum_us"], b["dispatch_us"])]
 
     fetch = counters(os.path.join(out, "%s_fetch" % workload), "FETCH_SIZE")
     write = counters(os.path.join(out, "%s_write" % workload), "WRITE_SIZE")
