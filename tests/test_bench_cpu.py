@@ -70,3 +70,23 @@ def test_all_cores_leg_computes_the_oracle():
         assert np.array_equal(got["recv_src"][:used], ref["recv_src"][:used])
         assert np.array_equal(got["recv_w"][:used].view(np.uint32), ref["recv_w"][:used].view(np.uint32))
         assert np.array_equal(got["out"], ref_out)
+
+
+def test_local_rows_by_token_inverts_the_source_index():
+    """The write probes' destination map: every row in use whose source index is a token goes to that token's
+    list, in row order, and the others are the padding rows."""
+    import numpy as np
+
+    rng = np.random.default_rng(3)
+    T, K, cap, used = 40, 6, 400, 360
+    src = np.full(cap, -1, np.int64)
+    rows = rng.choice(used, 150, replace=False)
+    src[rows] = rng.integers(0, T, rows.size)
+    src[used + 5] = 7                                    # past the rows in use: ignored
+    token_rows, V, pads = bench.local_rows_by_token(src, used, T, K * 8)
+    assert V == int((src[:used] >= 0).sum())
+    assert pads.tolist() == [i for i in range(used) if src[i] < 0]
+    for t in range(T):
+        mine = [r for r in range(used) if src[r] == t]
+        assert token_rows[t, :len(mine)].tolist() == mine
+        assert (token_rows[t, len(mine):] == -1).all()
