@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kThreads) void k_layout_dispatch_small(FusedArgs f,
     const int t = blockIdx.x;                         // this workgroup's token (the grid has >= T workgroups)
     const bool tok = t < T;
     // the token's segments go to the last nt waves (segment s on wave 16 - nt + s % 16), clear of wave 0, which
-    // runs the scan, and of the waves that count the tokens' ranks (tid < T)
+    // runs the scan (and, up to 6 segments, of waves 4..7, which count the tokens per rank meanwhile)
     const int nt = min(p.nstep, kWaves);
     const int tw = w - (kWaves - nt);                 // >= 0 on the token's waves
     const bool seg = tok && tw >= 0;

@@ -159,17 +159,17 @@ __device__ __forceinline__ int pad_row_of(int q, int epr, const int* psum, const
 // expert-major row of its entry k is the aligned start of the expert, plus the expert's entries in the tokens
 // before it, plus the copies of the expert among its entries 0..k-1; its row in rank r's window is the number
 // of tokens before it with an expert on r.  A workgroup that writes token t stages the routing table and builds
-// these counts with LDS atomic adds (the order of the adds does not change a count, so the result is
-// deterministic), then the aligned scan of the local experts.
+// these counts with LDS atomic adds, and each token's set of ranks with atomic ORs (their order changes neither a
+// count nor a set, so the result is deterministic), then the aligned scan of the local experts.
 struct TokLds {
-    uint64_t* tmask;   // [256]    the ranks each token has an expert on (atomic ORs of its entries)
-    int* ent;       // [256 * K]   staged expert ids (-1 none, kBad invalid)
-    int* tot;       // [E + R + 1] column totals: entries per expert | tokens per rank | invalid entries
-    int* bef;       // [E]         entries per expert in the tokens before t
-    int* rbef;      // [R]         tokens before t with an expert on rank r
-    int* psum;      // [epr + 1]   aligned prefix of the local experts
-    int* padpre;    // [epr + 1]   padding prefix of the local experts
-    int* scratch;   // [2 * kWaves]
+    uint64_t* tmask;   // [256]         the ranks each token has an expert on
+    int* ent;          // [256 * K]     staged expert ids (-1 none, kBad invalid)
+    int* tot;          // [E + R + 1]   column totals: entries per expert | tokens per rank | invalid entries
+    int* bef;          // [E]           entries per expert in the tokens before t
+    int* rbef;         // [R]           tokens before t with an expert on rank r
+    int* psum;         // [epr + 1]     aligned prefix of the local experts
+    int* padpre;       // [epr + 1]     padding prefix of the local experts
+    int* scratch;      // [2 * kWaves]
 };
 
 __host__ __device__ inline size_t tok_lds_bytes(int E, int K, int R, int epr) {
