@@ -81,6 +81,9 @@ CASES = [
     (300, 4, 32, 2, 0, 8, 256, False, True, "uniform"),       # two tiles: the two-launch path
     (256, 32, 1024, 64, 5, 128, 256, True, True, "dup"),      # the largest K, E and ranks in one launch
     (256, 32, 1024, 2, 1, 300, 64, False, True, "invalid"),   # 512 local experts, long padding list, invalid ids
+    (128, 8, 256, 1, 0, 128, 16384, True, True, "uniform"),   # 16 segments: every wave carries one, padding in extra blocks
+    (64, 4, 64, 4, 2, 16, 32768, True, False, "uniform"),     # 32 segments: two per wave, send windows
+    (32, 2, 16, 2, 1, 8, 32768, False, True, "dup"),          # BF16 rows of 64 KiB: 64 copy segments, four per wave
 ]
 
 
