@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kBlock) void k_dispatch_raw(Params p) {
 #pragma unroll
             for (int j = 0; j < kRawSegs; ++j) {
                 const int c = (it * kRawSegs + j) * kWave + lane;
-                v[j] = ld_nt(reinterpret_cast<const u32x4*>(p.src + (int64_t)t * p.row_bytes) + (c < nchunk ? c : 0));
+                v[j] = reinterpret_cast<const u32x4*>(p.src + (int64_t)t * p.row_bytes)[c < nchunk ? c : 0];
             }
             if (it == 0) token_meta(p, t, lane, ds, js, lmask, smask);
 #pragma unroll

@@ -115,6 +115,9 @@ __device__ __forceinline__ void token_meta(const Params& p, int t, int lane, int
 // with the segment's 8 group scales.
 // The segment's source bytes, loaded by fp8_load before the destinations are known (so the loads can overlap
 // other work) and consumed by fp8_emit.
+// Source rows are read with plain (cached) loads, here and in raw_load: each row is read once, but unlike
+// non-temporal loads they leave it in the memory-side cache, where a dispatch of the same rows right after finds
+// it (prefill: 75.9 -> 66.9 us back to back); with the cache cleared first they are also faster (80.1 -> 78.7 us).
 struct Fp8Src {
     u32x4 a, b;
 };
@@ -126,8 +129,8 @@ __device__ __forceinline__ Fp8Src fp8_load(const Params& p, int t, int st, int l
     const int ch = (st * kWave + lane) * 16;      // first channel of this lane
     if (ch < p.H) {
         const u32x4* src = reinterpret_cast<const u32x4*>(p.src + ((int64_t)t * p.H + ch) * 2);
-        v.a = ld_nt(src);
-        v.b = ld_nt(src + 1);
+        v.a = src[0];
+        v.b = src[1];
     }
     return v;
 }
@@ -138,8 +141,8 @@ __device__ __forceinline__ Fp8Src fp8_load_clamped(const Params& p, int t, int s
     const int ch = min((st * kWave + lane) * 16, p.H - 16);
     const u32x4* src = reinterpret_cast<const u32x4*>(p.src + ((int64_t)t * p.H + ch) * 2);
     Fp8Src v;
-    v.a = ld_nt(src);
-    v.b = ld_nt(src + 1);
+    v.a = src[0];
+    v.b = src[1];
     return v;
 }
 
@@ -205,14 +208,14 @@ __device__ __forceinline__ void fp8_emit(const Params& p, int st, int lane, cons
 __device__ __forceinline__ u32x4 raw_load(const Params& p, int t, int st, int lane) {
     const int c = st * kWave + lane;                  // 16-byte chunk of the row
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (c < p.row_bytes / 16) v = ld_nt(reinterpret_cast<const u32x4*>(p.src + (int64_t)t * p.row_bytes) + c);
+    if (c < p.row_bytes / 16) v = reinterpret_cast<const u32x4*>(p.src + (int64_t)t * p.row_bytes)[c];
     return v;
 }
 
 // raw_load with the chunk clamped into the row (row_bytes >= 16; chunks past the row are never stored).
 __device__ __forceinline__ u32x4 raw_load_clamped(const Params& p, int t, int st, int lane) {
     const int c = min(st * kWave + lane, p.row_bytes / 16 - 1);
-    return ld_nt(reinterpret_cast<const u32x4*>(p.src + (int64_t)t * p.row_bytes) + c);
+    return reinterpret_cast<const u32x4*>(p.src + (int64_t)t * p.row_bytes)[c];
 }
 
 __device__ __forceinline__ void raw_emit(const Params& p, int t, int st, int lane, u32x4 v, int ds, int js,
