@@ -1,9 +1,9 @@
 """Benchmark of the MoE expert-parallel layout / dispatch / combine path on one MI355X.
 
 A step is one pass of the whole path over one batch of the prefill workload: the layout and the FP8 dispatch
-with zero padding (one ep_layout_dispatch call, whose layout kernels also read the token rows ahead of the
-dispatch), then the weighted BF16 combine (4096 tokens, hidden 7168, 256 experts in 8 groups with group-limited
-top-4-group / top-8 routing, alignment 128).  Inputs and expert outputs are resident in HBM before timing
+with zero padding (one ep_layout_dispatch call: the layout kernels, then the dispatch), then the weighted BF16
+combine (4096 tokens, hidden 7168, 256 experts in 8 groups with group-limited top-4-group / top-8 routing,
+alignment 128).  Inputs and expert outputs are resident in HBM before timing
 starts.  W untimed warm-up steps, then exactly K timed steps bracketed by device syncs; the host enqueues the
 calls of a step far faster than the GPU runs them, so no step waits on the host.  The same step captured in a
 HIP graph and replayed K times is reported too (`step_graph_replay_us`).
@@ -811,8 +811,7 @@ def main():
         del a, b
 
     def step():
-        """One pass of the path: the one-call layout + dispatch (the layout kernels read the token rows into the
-        memory-side cache while the layout runs), then the combine."""
+        """One pass of the path: the one-call layout + dispatch, then the combine."""
         h, _, _ = ep.ep_layout_dispatch(idx, x, E, R, cfg.rank, cfg.expert_alignment, w, fp8=cfg.fp8,
                                         do_zero_padding=cfg.zero_padding, out=dout, workspace=ws, outputs=lay_out)
         ep.ep_combine(h, y, w, bias, out=out)
@@ -912,7 +911,7 @@ def main():
                     A_pad=round(int(psum[-1]) / max(V, 1), 4),
                     data_dtypes="x bf16 -> recv e4m3 + fp32 scales; y bf16 -> out bf16 (fp32 accumulate)"),
         tokens_per_s=round(T / (ms_per_step * 1e-3), 1),
-        timing="step: K eager steps of ep_layout_dispatch (layout kernels reading x ahead, then the dispatch) + "
+        timing="step: K eager steps of ep_layout_dispatch (the layout kernels, then the dispatch) + "
                "ep_combine between device syncs, host clock; per call: events around K back-to-back launches, "
                "and flushed (2 GiB read sweep before each of 10 + 50 samples, kernel durations from a trace)",
         step_graph_replay_us=step_graph_us,

@@ -131,9 +131,7 @@ __global__ __launch_bounds__(kThreads) void k_layout_dispatch_small(FusedArgs f,
 hipError_t launch_layout_dispatch(const Handle& h, const LayoutOutputs& out, const DispatchArgs& a,
                                   hipStream_t stream) {
     if (h.ntiles != 1 || a.mode == DispatchArgs::kRows) {   // T == 0, or more than one tile: two launches
-        // the layout launches read the dispatch's source rows ahead of it (into the memory-side cache)
-        const size_t src_bytes = (size_t)h.T * (a.mode == DispatchArgs::kRows ? (size_t)a.row_bytes : 2 * (size_t)a.hidden);
-        const hipError_t e = launch_layout(h, out, stream, a.x, src_bytes);
+        const hipError_t e = launch_layout(h, out, stream);
         if (e != hipSuccess) return e;
         return launch_dispatch(h, a, stream);
     }

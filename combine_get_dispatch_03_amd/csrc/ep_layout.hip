@@ -218,54 +218,12 @@ __device__ void finalize_core(int E, int R, int rank, int epr, int A, const int*
     }
 }
 
-// ---- multi-tile path: source prefetch and kernels ----------------------------------------------------------
-
-// Source prefetch.  The two layout kernels run one block per 256-token tile, on a few CUs, and leave HBM nearly
-// idle; the dispatch that follows reads every source row once.  When the caller hands the span it reads next
-// (ep_layout_dispatch: the token rows), blocks beyond the tiles read it with plain loads, which leave it in the
-// memory-side cache: the dispatch then finds its sources there and HBM serves only its writes.  Nothing is
-// written; the count kernel reads one share of the span, the finalize kernel the rest.
-struct Prefetch {
-    const u32x4* p;     // the span, 16-byte units
-    int64_t lo, hi;     // this kernel's share [lo, hi)
-    int nblk;           // prefetch blocks
-};
-
-// Measured on the 4096 x 7168 FP8 prefill after a combine (x cold): layout + dispatch 89.3 -> 85.3 us with
-// 224 blocks and 60% of the span read by the count kernel (50-70% within 1 us of it; all of it in one kernel
-// 87-89 us; 448 or 896 blocks no better).
-constexpr int kPrefetchBlocks = 224;
-constexpr int64_t kPrefetchCountPct = 60;
-// The span is read only if it is at most this long: about what HBM moves in the ~11 us the layout takes.  All
-// or nothing, as measured: prefill (58.7 MB of rows) step 2.2% faster reading all of it, but 32 MiB of it made
-// the step slower than none; for a 235 MB span (16,384 tokens) reading all of it made the step 8% slower and
-// reading the first 32 or 64 MiB 1% slower than none.
-constexpr int64_t kPrefetchMaxBytes = 64ll << 20;
-// ... and at least this long: below it the extra blocks cost more than the reads save (1024 tokens, 14.7 MB of
-// rows: layout + dispatch 1-2 us slower; 2048 tokens: no change).
-constexpr int64_t kPrefetchMinBytes = 16ll << 20;
-
-__device__ void prefetch_share(const Prefetch& pf, int b) {
-    const int64_t stride = (int64_t)pf.nblk * kThreads;
-    unsigned acc = 0;
-    for (int64_t i = pf.lo + (int64_t)b * kThreads + threadIdx.x; i < pf.hi; i += 4 * stride) {
-        u32x4 v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = pf.p[i + u * stride < pf.hi ? i + u * stride : i];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) acc ^= v[u][0];
-    }
-    asm volatile("" ::"v"(acc));   // keeps the loads; nothing is stored
-}
+// ---- multi-tile path -------------------------------------------------------------------------------------
 
 __global__ __launch_bounds__(kThreads) void k_layout_count(
     const int64_t* __restrict__ idx, int T, int K, int E, int R, int epr, int nbits,
     int32_t* __restrict__ tile_hist, int32_t* __restrict__ packed_out, int32_t* __restrict__ send_tmp,
-    uint8_t* __restrict__ in_rank_out, int ntiles, Prefetch pf) {
-    if ((int)blockIdx.x >= ntiles) {
-        prefetch_share(pf, (int)blockIdx.x - ntiles);
-        return;
-    }
+    uint8_t* __restrict__ in_rank_out) {
     const CountLds L = carve_count(layout_smem, E, K, R);
     const int tid = threadIdx.x;
     const int tile = blockIdx.x;
@@ -286,11 +244,7 @@ __global__ __launch_bounds__(kThreads) void k_layout_count(
 
 __global__ __launch_bounds__(kThreads) void k_layout_finalize(
     int T, int K, int E, int R, int rank, int epr, int A, int ntiles, const int32_t* __restrict__ tile_hist,
-    int32_t* __restrict__ slot, int32_t* __restrict__ send_slot, Outputs o, int nlayout, Prefetch pf) {
-    if ((int)blockIdx.x >= nlayout) {
-        prefetch_share(pf, (int)blockIdx.x - nlayout);
-        return;
-    }
+    int32_t* __restrict__ slot, int32_t* __restrict__ send_slot, Outputs o) {
     __shared__ int part_before[kMaxCols];
     __shared__ int part_total[kMaxCols];
     __shared__ int before[kMaxCols];
@@ -347,7 +301,7 @@ __global__ __launch_bounds__(kThreads) void k_layout_finalize(
     }
     __syncthreads();
 
-    finalize_core(E, R, rank, epr, A, total, psum, padpre, scan_scratch, o, nlayout);
+    finalize_core(E, R, rank, epr, A, total, psum, padpre, scan_scratch, o, (int)gridDim.x);
     if (tile >= ntiles) return;   // T == 0: the single block only wrote the global outputs
 
     // final rows of this tile's entries
@@ -413,8 +367,7 @@ __global__ __launch_bounds__(kThreads) void k_layout_tokens(
 
 }  // namespace
 
-hipError_t launch_layout(const Handle& h, const LayoutOutputs& out, hipStream_t stream, const void* prefetch,
-                         size_t prefetch_bytes) {
+hipError_t launch_layout(const Handle& h, const LayoutOutputs& out, hipStream_t stream) {
     const int epr = h.El;
     int nbits = 0;
     while ((1 << nbits) < h.E) ++nbits;
@@ -434,31 +387,21 @@ hipError_t launch_layout(const Handle& h, const LayoutOutputs& out, hipStream_t 
                            out.is_token_in_rank, o);
         return hipGetLastError();
     }
-    // the span the caller reads next, in 16-byte units: the count kernel's extra blocks read the first
-    // kPrefetchCountPct percent of it, the finalize kernel's the rest
-    const bool read_ahead = prefetch != nullptr && (int64_t)prefetch_bytes >= kPrefetchMinBytes &&
-                            (int64_t)prefetch_bytes <= kPrefetchMaxBytes;
-    const int64_t n16 = read_ahead ? (int64_t)prefetch_bytes / 16 : 0;
-    const int64_t split = n16 * kPrefetchCountPct / 100;
-    const Prefetch pf_count{static_cast<const u32x4*>(prefetch), 0, split, kPrefetchBlocks};
-    const Prefetch pf_final{static_cast<const u32x4*>(prefetch), split, n16, kPrefetchBlocks};
-    const int nb_count = h.ntiles + (split > 0 ? kPrefetchBlocks : 0);
-    const int nlayout = h.ntiles > 0 ? h.ntiles : 1;
-    const int nb_final = nlayout + (n16 > split ? kPrefetchBlocks : 0);
     if (h.ntiles > 1) {
         const size_t lds = count_lds_bytes(h.E, h.K, h.R);
         if (lds > 65536) {
             const hipError_t err = allow_dynamic_lds(reinterpret_cast<const void*>(k_layout_count), (int)lds);
             if (err != hipSuccess) return err;
         }
-        hipLaunchKernelGGL(k_layout_count, dim3(nb_count), dim3(kThreads), lds, stream, h.topk_idx, h.T, h.K, h.E,
-                           h.R, epr, nbits, h.ws.tile_hist, h.ws.slot, send, out.is_token_in_rank, h.ntiles, pf_count);
+        hipLaunchKernelGGL(k_layout_count, dim3((unsigned)h.ntiles), dim3(kThreads), lds, stream, h.topk_idx, h.T,
+                           h.K, h.E, h.R, epr, nbits, h.ws.tile_hist, h.ws.slot, send, out.is_token_in_rank);
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
     // T == 0 lands here with ntiles == 0: one finalize block writes the (zero) global outputs
+    const unsigned nb_final = h.ntiles > 0 ? (unsigned)h.ntiles : 1u;
     hipLaunchKernelGGL(k_layout_finalize, dim3(nb_final), dim3(kThreads), 0, stream, h.T, h.K, h.E, h.R, h.rank,
-                       epr, h.A, h.ntiles, h.ws.tile_hist, h.ws.slot, send, o, nlayout, pf_final);
+                       epr, h.A, h.ntiles, h.ws.tile_hist, h.ws.slot, send, o);
     return hipGetLastError();
 }
 

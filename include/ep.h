@@ -181,9 +181,8 @@ ep_status_t ep_dispatch(ep_handle_t handle, const void* x, int hidden, const flo
  * same handle, bit for bit.  For num_tokens <= 256 (the decode shape) both run in a single kernel launch:
  * workgroup t counts in LDS what token t's rows follow from and dispatches token t, so no workgroup waits for another
  * ([DeepEP->MegaMoE] §4.3: at small batches launch overhead, not bytes, sets the time; [DeepEP-hotdry]
- * 性能基准: the low-latency decode path).  Larger batches run the layout and the dispatch launches back to back;
- * when x is 16 to 64 MiB the layout launches also read it (and store nothing) while the layout runs, so that
- * the dispatch finds its rows in the memory-side cache.  x is only read, as by ep_dispatch.
+ * 性能基准: the low-latency decode path).  Larger batches run the layout and the dispatch launches back to
+ * back.  x is only read, as by ep_dispatch.
  *
  *   Arguments as in ep_get_layout (topk_idx .. num_invalid_topk, handle_out) and ep_dispatch (x .. out).
  *   Every argument of both is validated before anything is enqueued; on an error no handle is created.
