@@ -486,8 +486,9 @@ def measure_dispatch_bound(ep, W, dev, n, probe):
     """The FP8 dispatch with zero padding on the prefill workload, taken apart:
     * the dispatch's stores alone (probe_dispatch_writes: the same destination rows, scales, row metadata and
       padding rows, in the same work split, no reads) and its source reads alone (probe_dispatch_reads: the
-      token rows and the slot map, no stores).  Reads and writes share each HBM channel's data bus, so their
-      sum bounds the dispatch from below;
+      token rows and the slot map, no stores).  Both use the dispatch's own load and store kinds.  When both
+      streams come from HBM their sum bounds the dispatch from below (reads and writes share each channel's
+      data bus); back to back, the source rows come from the memory-side cache instead;
     * the product dispatch without zero padding (routed rows only) and with alignment 1 (no padding rows at
       all), and the increment that zero padding adds."""
     import torch
@@ -533,7 +534,8 @@ def measure_dispatch_bound(ep, W, dev, n, probe):
     h1.free()
     return dict(
         note="prefill FP8 dispatch with zero padding: its stores alone and its source reads alone "
-             "(bench_probe.hip, same destination rows and work split), back to back, events",
+             "(bench_probe.hip, same destination rows and work split), back to back, events; bound_* price "
+             "the dispatch's bytes on the sum of the two",
         write_only_us=round(us["writes"], 2), write_bytes=wbytes, write_only_GBps=round(rate(wbytes, us["writes"]), 1),
         read_only_us=round(us["reads"], 2), read_bytes=rbytes, read_only_GBps=round(rate(rbytes, us["reads"]), 1),
         sum_us=round(s, 2), dispatch_us=round(us["dispatch"], 2), dispatch_bytes=bm["dispatch"],

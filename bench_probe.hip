@@ -7,8 +7,8 @@
 //   probe_dispatch_writes  every store of an FP8 dispatch with zero padding -- the routed rows' e4m3 bytes
 //                          (16-byte non-temporal stores to each destination row), their scales and row metadata,
 //                          and the zero-padding rows -- and no source reads;
-//   probe_dispatch_reads   every source read of that dispatch -- the token rows (32 bytes per lane, non-temporal)
-//                          and the slot map -- and no stores;
+//   probe_dispatch_reads   every source read of that dispatch -- the token rows (32 bytes per lane, plain loads
+//                          as in the dispatch) and the slot map -- and no stores;
 //   probe_send_writes      the stores of an FP8 dispatch with send windows and no zero padding -- each token's
 //                          e4m3 bytes and scales to its local expert-major rows and to its row in every other
 //                          rank's window, the local rows' metadata and the window rows' source index -- and no
@@ -151,8 +151,8 @@ __global__ __launch_bounds__(kBlock) void k_probe_reads(ReadArgs a) {
     uint32_t acc = (uint32_t)d;
     if (ch < a.H) {
         const u32x4* src = reinterpret_cast<const u32x4*>(a.x + ((int64_t)t * a.H + ch) * 2);
-        const u32x4 v0 = __builtin_nontemporal_load(src);
-        const u32x4 v1 = __builtin_nontemporal_load(src + 1);
+        const u32x4 v0 = src[0];
+        const u32x4 v1 = src[1];
         acc ^= v0[0] ^ v0[1] ^ v0[2] ^ v0[3] ^ v1[0] ^ v1[1] ^ v1[2] ^ v1[3];
     }
     if (acc == a.never) a.sink[0] = (int32_t)acc;
