@@ -36,7 +36,8 @@ constexpr int64_t kStreamMinWaves = 16384;
 // share HBM with its writes (interleaved, those cost about 10 us of the prefill combine).  Measured on one box,
 // back to back / cache flushed first / eager step: prefill combine 88.7 -> 85.3, 93.4 -> 87.3 us, step 169.9 ->
 // 164.9 us; ep8 22.7 -> 21.2, 25.6 -> 24.2 us.  A 235 MB output (16,384 tokens) crowds out everything else the
-// cache holds: back to back 291 -> 331 us, so larger outputs (above kCachedWriteMaxBytes) stay non-temporal.
+// cache holds: back to back 291 -> 331 us, so larger outputs stay non-temporal.
+constexpr int64_t kCachedOutMaxBytes = 128ll << 20;
 
 // Stores the 16-byte chunk c of output row t: into the memory-side cache (CACHED) or non-temporal.
 template <bool CACHED>
@@ -230,7 +231,7 @@ hipError_t launch_combine_reduce(const Handle& h, const ReduceArgs& a, hipStream
     p.nitems = (int64_t)h.T * p.nseg;
     p.stream_min = p.nitems >= kStreamMinWaves ? kReduceStreamRows : INT_MAX;
     const unsigned nblocks = (unsigned)((p.nitems + kWavesPerBlock - 1) / kWavesPerBlock);
-    if ((int64_t)h.T * a.hidden * 2 <= kCachedWriteMaxBytes)
+    if ((int64_t)h.T * a.hidden * 2 <= kCachedOutMaxBytes)
         hipLaunchKernelGGL(k_combine_reduce<true>, dim3(nblocks), dim3(kBlock), 0, stream, p);
     else
         hipLaunchKernelGGL(k_combine_reduce<false>, dim3(nblocks), dim3(kBlock), 0, stream, p);
@@ -260,7 +261,7 @@ hipError_t launch_combine(const Handle& h, const CombineArgs& a, hipStream_t str
     p.nitems = (int64_t)h.T * p.nseg;
     p.stream_min = p.nitems >= kStreamMinWaves ? kCombineStreamRows : INT_MAX;
     const unsigned nblocks = (unsigned)((p.nitems + kWavesPerBlock - 1) / kWavesPerBlock);
-    if ((int64_t)h.T * a.hidden * 2 <= kCachedWriteMaxBytes)
+    if ((int64_t)h.T * a.hidden * 2 <= kCachedOutMaxBytes)
         hipLaunchKernelGGL(k_combine<true>, dim3(nblocks), dim3(kBlock), 0, stream, p);
     else
         hipLaunchKernelGGL(k_combine<false>, dim3(nblocks), dim3(kBlock), 0, stream, p);

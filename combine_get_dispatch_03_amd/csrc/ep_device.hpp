@@ -131,9 +131,6 @@ __device__ __forceinline__ void st_nt(u32x4* p, u32x4 v) { __builtin_nontemporal
 // to HBM later.  `row` must be the same for every lane of the wave (it becomes a buffer resource in scalar
 // registers); offsets at or past row_bytes are dropped by the hardware's range check.
 constexpr int kBufferRsrcWord3 = 0x00020000;   // raw (untyped) buffer, 32-bit data format
-// Largest write stream a kernel stores into the memory-side cache (st_sc1): half of its 256 MB, so that the
-// rows stay there beside the other operands instead of evicting them.
-constexpr int64_t kCachedWriteMaxBytes = 128ll << 20;
 constexpr int kCachePolicySc1 = 16;
 __device__ __forceinline__ void st_sc1(void* row, int row_bytes, int off, u32x4 v) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(row, 0, row_bytes, kBufferRsrcWord3);

@@ -63,7 +63,7 @@ __device__ __forceinline__ void pad_prefetch(const Params& p, int64_t gw, int la
     }
 }
 
-template <bool FP8, bool CACHED>
+template <bool FP8>
 __device__ __forceinline__ void pad_items(const Params& p, int64_t gw, int lane, const PadWork& pw) {
     if (!p.zero_pad) {
         if (gw * kWave + lane < pw.nitems) pad_meta_row(p, pw.row[0]);
@@ -73,7 +73,7 @@ __device__ __forceinline__ void pad_items(const Params& p, int64_t gw, int lane,
     for (int j = 0; j < kPadItemsPerWave; ++j) {
         const int64_t i = gw + j * p.nwaves;
         if (i >= pw.nitems) break;
-        pad_zero_segment<FP8, CACHED>(p, pw.row[j], (int)(i % p.pad_sub), lane);
+        pad_zero_segment<FP8>(p, pw.row[j], (int)(i % p.pad_sub), lane);
     }
 }
 
@@ -84,7 +84,7 @@ __device__ __forceinline__ void pad_items(const Params& p, int64_t gw, int lane,
 // template parameter, not a runtime flag: with both paths in one kernel the compiler cannot tell that the
 // early loads' registers are never pending on the late path, and puts a full wait (for every load and store
 // in flight, the segment-0 metadata stores included) in front of the late loads.
-template <int SPW, bool EARLY, bool CACHED>
+template <int SPW, bool EARLY>
 __global__ __launch_bounds__(kBlock) void k_dispatch_fp8(Params p) {
     const int lane = lane_id();
     const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
@@ -113,13 +113,12 @@ __global__ __launch_bounds__(kBlock) void k_dispatch_fp8(Params p) {
         if (any) {
 #pragma unroll
             for (int j = 0; j < SPW; ++j)
-                if (it * SPW + j < p.nstep) fp8_emit<CACHED>(p, it * SPW + j, lane, v[j], ds, js, lmask, smask);
+                if (it * SPW + j < p.nstep) fp8_emit(p, it * SPW + j, lane, v[j], ds, js, lmask, smask);
         }
     }
-    pad_items<true, CACHED>(p, gw, lane, pw);
+    pad_items<true>(p, gw, lane, pw);
 }
 
-template <bool CACHED>
 __global__ __launch_bounds__(kBlock) void k_dispatch_raw(Params p) {
     const int lane = lane_id();
     const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
@@ -144,13 +143,12 @@ __global__ __launch_bounds__(kBlock) void k_dispatch_raw(Params p) {
             if (it == 0) token_meta(p, t, lane, ds, js, lmask, smask);
 #pragma unroll
             for (int j = 0; j < kRawSegs; ++j)
-                if (it * kRawSegs + j < p.nstep)
-                    raw_emit<CACHED>(p, t, it * kRawSegs + j, lane, v[j], ds, js, lmask, smask);
+                if (it * kRawSegs + j < p.nstep) raw_emit(p, t, it * kRawSegs + j, lane, v[j], ds, js, lmask, smask);
         } else if (it == 0) {
             token_meta(p, t, lane, ds, js, lmask, smask);
         }
     }
-    pad_items<false, CACHED>(p, gw, lane, pw);
+    pad_items<false>(p, gw, lane, pw);
 }
 
 }  // namespace
@@ -168,18 +166,13 @@ hipError_t launch_dispatch(const Handle& h, const DispatchArgs& a, hipStream_t s
     if (pad_waves > nwaves) nwaves = pad_waves;
     const int64_t nblocks = (nwaves + kWavesPerBlock - 1) / kWavesPerBlock;
     p.nwaves = nblocks * kWavesPerBlock;
-    const dim3 grid((unsigned)nblocks), block(kBlock);
-    const bool cached = rows_cached(h, p);
-    if (fp8 && p.send_slot != nullptr) {
-        if (cached) hipLaunchKernelGGL((k_dispatch_fp8<kFp8SegsPerItem, true, true>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((k_dispatch_fp8<kFp8SegsPerItem, true, false>), grid, block, 0, stream, p);
-    } else if (fp8) {
-        if (cached) hipLaunchKernelGGL((k_dispatch_fp8<kFp8SegsPerItem, false, true>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((k_dispatch_fp8<kFp8SegsPerItem, false, false>), grid, block, 0, stream, p);
-    } else {
-        if (cached) hipLaunchKernelGGL(k_dispatch_raw<true>, grid, block, 0, stream, p);
-        else hipLaunchKernelGGL(k_dispatch_raw<false>, grid, block, 0, stream, p);
-    }
+    if (fp8 && p.send_slot != nullptr)
+        hipLaunchKernelGGL((k_dispatch_fp8<kFp8SegsPerItem, true>), dim3((unsigned)nblocks), dim3(kBlock), 0, stream, p);
+    else if (fp8)
+        hipLaunchKernelGGL((k_dispatch_fp8<kFp8SegsPerItem, false>), dim3((unsigned)nblocks), dim3(kBlock), 0, stream,
+                           p);
+    else
+        hipLaunchKernelGGL(k_dispatch_raw, dim3((unsigned)nblocks), dim3(kBlock), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -47,23 +47,6 @@ struct Params {
     int64_t nwaves;   // waves in the grid
 };
 
-// Stores 16-byte chunk `chunk` of data row `row` of `base` (rows of `stride` bytes); `row` is the same on every
-// lane of the wave.  CACHED: into the memory-side cache, chosen when the call's rows fit in half of it
-// (rows_cached; a template parameter, since a runtime test in the store loops cost the prefill dispatch 1%):
-// the kernel then ends without waiting for HBM to take them (decode, 128 tokens, 7.3 MB of rows: one-launch
-// layout + dispatch 6.52 -> 6.30 us); non-temporal for larger calls, whose rows would evict each other there
-// (prefill dispatch 67 -> 87 us back to back), and for calls of under kCachedRowsMinBytes: such stores cost
-// about 0.2 us more per call, which is more than HBM needs for 1 MiB (128 tokens x 256 BF16 channels, 192 KB
-// of rows: 4.95 -> 5.15 us).
-constexpr int64_t kCachedRowsMinBytes = 1ll << 20;
-template <bool CACHED>
-__device__ __forceinline__ void put_row(uint8_t* base, int64_t row, int stride, int chunk, u32x4 v) {
-    if (CACHED)
-        st_sc1(base + (int64_t)__builtin_amdgcn_readfirstlane((int)row) * stride, stride, chunk * 16, v);
-    else
-        st_nt(reinterpret_cast<u32x4*>(base + row * stride) + chunk, v);
-}
-
 // Metadata of token t's rows, written by the wave of its segment 0.  ds (lanes < K expert-major, lane 0
 // token-major) and js (lanes < R) are the token's local and send rows, lmask / smask their ballots.
 // The token's routing weight and expert id for lane k < K, as loaded ahead of token_meta by token_entry.  The
@@ -194,7 +177,6 @@ __device__ __forceinline__ Fp8Row fp8_cast(const Fp8Src& v) {
 }
 
 // Stores of segment st's cast bytes and scales to every destination row (local rows, then send rows).
-template <bool CACHED>
 __device__ __forceinline__ void fp8_store(const Params& p, int st, int lane, const Fp8Row& c, int ds, int js,
                                           uint64_t lmask, uint64_t smask) {
     const int H = p.H, G = H / 128;
@@ -204,21 +186,20 @@ __device__ __forceinline__ void fp8_store(const Params& p, int st, int lane, con
     const bool sc_lane = (lane & 7) == 0 && g < G;
     for (uint64_t mm = lmask; mm != 0; mm &= mm - 1) {
         const int s = readlane(ds, __builtin_ctzll(mm));
-        if (active) put_row<CACHED>(p.recv_x, s, H, st * kWave + lane, c.q);
+        if (active) st_nt(reinterpret_cast<u32x4*>(p.recv_x + (int64_t)s * H) + st * kWave + lane, c.q);
         if (sc_lane) p.recv_scales[(int64_t)s * G + g] = c.scale;
     }
     for (uint64_t mm = smask; mm != 0; mm &= mm - 1) {
         const int r = __builtin_ctzll(mm);
         const int64_t row = (int64_t)r * p.T + readlane(js, r);
-        if (active) put_row<CACHED>(p.send_x, row, H, st * kWave + lane, c.q);
+        if (active) st_nt(reinterpret_cast<u32x4*>(p.send_x + row * H) + st * kWave + lane, c.q);
         if (sc_lane) p.send_scales[row * G + g] = c.scale;
     }
 }
 
-template <bool CACHED>
 __device__ __forceinline__ void fp8_emit(const Params& p, int st, int lane, const Fp8Src& v, int ds, int js,
                                          uint64_t lmask, uint64_t smask) {
-    fp8_store<CACHED>(p, st, lane, fp8_cast(v), ds, js, lmask, smask);
+    fp8_store(p, st, lane, fp8_cast(v), ds, js, lmask, smask);
 }
 
 
@@ -237,19 +218,19 @@ __device__ __forceinline__ u32x4 raw_load_clamped(const Params& p, int t, int st
     return reinterpret_cast<const u32x4*>(p.src + (int64_t)t * p.row_bytes)[c];
 }
 
-template <bool CACHED>
 __device__ __forceinline__ void raw_emit(const Params& p, int t, int st, int lane, u32x4 v, int ds, int js,
                                          uint64_t lmask, uint64_t smask) {
     const int c = st * kWave + lane;                  // 16-byte chunk of the row
     const bool active = c < p.row_bytes / 16;
+    const int64_t rb = p.row_bytes;
     for (uint64_t mm = lmask; mm != 0; mm &= mm - 1) {
         const int s = readlane(ds, __builtin_ctzll(mm));
-        if (active) put_row<CACHED>(p.recv_x, s, p.row_bytes, c, v);
+        if (active) st_nt(reinterpret_cast<u32x4*>(p.recv_x + (int64_t)s * rb) + c, v);
     }
     for (uint64_t mm = smask; mm != 0; mm &= mm - 1) {
         const int r = __builtin_ctzll(mm);
         const int64_t row = (int64_t)r * p.T + readlane(js, r);
-        if (active) put_row<CACHED>(p.send_x, row, p.row_bytes, c, v);
+        if (active) st_nt(reinterpret_cast<u32x4*>(p.send_x + row * rb) + c, v);
     }
     if (st == 0 && p.G > 0) {
         for (int g = lane; g < p.G; g += kWave) {
@@ -267,13 +248,13 @@ __device__ __forceinline__ void raw_emit(const Params& p, int t, int st, int lan
 
 // Zero-padding item: segment s of padding row `row` gets zero bytes (and its share of the scales); segment 0
 // also writes the row's metadata.
-template <bool FP8, bool CACHED>
+template <bool FP8>
 __device__ __forceinline__ void pad_zero_segment(const Params& p, int row, int s, int lane) {
     const int G = p.G;
     const int nchunk = p.row_bytes / 16;            // 16-byte chunks per row
     const u32x4 z = {0u, 0u, 0u, 0u};
     const int c = s * kWave + lane;
-    if (c < nchunk) put_row<CACHED>(p.recv_x, row, p.row_bytes, c, z);
+    if (c < nchunk) st_nt(reinterpret_cast<u32x4*>(p.recv_x + (int64_t)row * p.row_bytes) + c, z);
     if (FP8) {
         if (lane < 8 && s * 8 + lane < G) p.recv_scales[(int64_t)row * G + s * 8 + lane] = 0.0f;
     } else if (s == 0) {
@@ -340,17 +321,6 @@ inline Params dispatch_params(const Handle& h, const DispatchArgs& a) {
     p.pad_sub = (h.A > 1 && !token_major) ? (a.zero_pad ? p.nstep : (meta ? 1 : 0)) : 0;
     p.nwaves = 0;
     return p;
-}
-
-// Whether the call's data rows go into the memory-side cache (the kernels' CACHED variant): the most data-row
-// bytes it can store (the counts are on the device) -- every entry's row, every send-window row and, with zero
-// padding, every padding row the alignment allows -- lie in [kCachedRowsMinBytes, kCachedWriteMaxBytes].
-inline bool rows_cached(const Handle& h, const Params& p) {
-    const int64_t rows_max = (int64_t)h.T * (p.token_major ? 1 : h.K) +
-                             (p.send_slot != nullptr ? (int64_t)(h.R - 1) * h.T : 0) +
-                             (p.zero_pad && !p.token_major ? (int64_t)h.El * (h.A - 1) : 0);
-    const int64_t bytes_max = rows_max * p.row_bytes;
-    return bytes_max >= kCachedRowsMinBytes && bytes_max <= kCachedWriteMaxBytes;
 }
 
 }  // namespace

@@ -43,7 +43,7 @@ struct FusedArgs {
     uint8_t* in_rank;        // [T, R] caller output, nullable
 };
 
-template <bool FP8, bool CACHED>
+template <bool FP8>
 __global__ __launch_bounds__(kThreads) void k_layout_dispatch_small(FusedArgs f, Params p) {
     touch_kernargs<sizeof(FusedArgs) + sizeof(Params)>();
     const int T = p.T, K = p.K, R = p.R, E = f.E, epr = p.epr, lo = p.rank * epr;
@@ -98,11 +98,8 @@ __global__ __launch_bounds__(kThreads) void k_layout_dispatch_small(FusedArgs f,
         }
         if ((lmask | smask) != 0) {
             for (int s = tw; s < p.nstep; s += kWaves) {
-                if (FP8)
-                    fp8_store<CACHED>(p, s, lane, s == tw ? c8 : fp8_cast(fp8_load(p, t, s, lane)), ds, js, lmask,
-                                      smask);
-                else
-                    raw_emit<CACHED>(p, t, s, lane, s == tw ? vr : raw_load(p, t, s, lane), ds, js, lmask, smask);
+                if (FP8) fp8_store(p, s, lane, s == tw ? c8 : fp8_cast(fp8_load(p, t, s, lane)), ds, js, lmask, smask);
+                else raw_emit(p, t, s, lane, s == tw ? vr : raw_load(p, t, s, lane), ds, js, lmask, smask);
             }
         }
         return;
@@ -124,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void k_layout_dispatch_small(FusedArgs f,
         const int64_t nitems = (int64_t)npad * p.nstep;
         for (int64_t i = iw; i < nitems; i += p.nwaves) {
             const int q = (int)(i / p.nstep);
-            pad_zero_segment<FP8, CACHED>(p, pad_row_of(q, epr, L.psum, L.padpre), (int)(i % p.nstep), lane);
+            pad_zero_segment<FP8>(p, pad_row_of(q, epr, L.psum, L.padpre), (int)(i % p.nstep), lane);
         }
     }
 }
@@ -164,15 +161,16 @@ hipError_t launch_layout_dispatch(const Handle& h, const LayoutOutputs& out, con
     f.in_rank = out.is_token_in_rank;
 
     const size_t lds = tok_lds_bytes(h.E, h.K, h.R, h.El);
-    const bool cached = rows_cached(h, p);
-    using Kernel = void (*)(FusedArgs, Params);
-    const Kernel k = fp8 ? (cached ? k_layout_dispatch_small<true, true> : k_layout_dispatch_small<true, false>)
-                         : (cached ? k_layout_dispatch_small<false, true> : k_layout_dispatch_small<false, false>);
     if (lds > 65536) {
-        const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(k), (int)lds);
+        const void* k = fp8 ? reinterpret_cast<const void*>(k_layout_dispatch_small<true>)
+                            : reinterpret_cast<const void*>(k_layout_dispatch_small<false>);
+        const hipError_t e = allow_dynamic_lds(k, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k, dim3((unsigned)nblocks), dim3(kThreads), lds, stream, f, p);
+    if (fp8)
+        hipLaunchKernelGGL(k_layout_dispatch_small<true>, dim3((unsigned)nblocks), dim3(kThreads), lds, stream, f, p);
+    else
+        hipLaunchKernelGGL(k_layout_dispatch_small<false>, dim3((unsigned)nblocks), dim3(kThreads), lds, stream, f, p);
     return hipGetLastError();
 }
 
