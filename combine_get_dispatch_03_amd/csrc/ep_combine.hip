@@ -31,22 +31,6 @@ constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kCombineStreamRows = 8;
 constexpr int kReduceStreamRows = 4;
 constexpr int64_t kStreamMinWaves = 16384;
-// Outputs of at most half the 256 MB memory-side cache are stored into that cache (st_sc1) instead of
-// streamed past it: the cache takes the writes and drains them to HBM later, so the kernel's gathers no longer
-// share HBM with its writes (interleaved, those cost about 10 us of the prefill combine).  Measured on one box,
-// back to back / cache flushed first / eager step: prefill combine 88.7 -> 85.3, 93.4 -> 87.3 us, step 169.9 ->
-// 164.9 us; ep8 22.7 -> 21.2, 25.6 -> 24.2 us.  A 235 MB output (16,384 tokens) crowds out everything else the
-// cache holds: back to back 291 -> 331 us, so larger outputs stay non-temporal.
-constexpr int64_t kCachedOutMaxBytes = 128ll << 20;
-
-// Stores the 16-byte chunk c of output row t: into the memory-side cache (CACHED) or non-temporal.
-template <bool CACHED>
-__device__ __forceinline__ void store_out(uint16_t* out, int t, int H, int c, u32x4 v) {
-    if (CACHED)
-        st_sc1(out + (int64_t)__builtin_amdgcn_readfirstlane(t) * H, H * 2, c * 16, v);
-    else
-        st_nt(reinterpret_cast<u32x4*>(out + (int64_t)t * H) + c, v);
-}
 
 struct Params {
     const uint16_t* y;
@@ -123,7 +107,6 @@ __device__ __forceinline__ void gather_all(float* acc, const u32x4* base, int64_
     }
 }
 
-template <bool CACHED>
 __global__ __launch_bounds__(kBlock) void k_combine(Params p) {
     // both argument lines in one round trip (the fields are read on demand otherwise, one miss after another):
     // decode combine 3.29 -> 3.12 us, prefill 87.1 -> 86.4 us (in the dispatch kernels the same cost time)
@@ -159,7 +142,7 @@ __global__ __launch_bounds__(kBlock) void k_combine(Params p) {
     gather_all<true>(acc, reinterpret_cast<const u32x4*>(p.y) + (active ? c : 0), p.H / 8, cs, cw, nv, p.stream_min);
     if (!active) return;
     if (p.bias != nullptr) add8(acc, reinterpret_cast<const u32x4*>(p.bias + (int64_t)t * p.H)[c]);
-    store_out<CACHED>(p.out, t, p.H, c, pack8(acc));
+    st_nt(reinterpret_cast<u32x4*>(p.out + (int64_t)t * p.H) + c, pack8(acc));
 }
 
 // Source-side reduce after the combine exchange ([DeepEP->MegaMoE] §2.5: the reduce epilogue adds the rows
@@ -179,7 +162,6 @@ struct ReduceParams {
     int stream_min;
 };
 
-template <bool CACHED>
 __global__ __launch_bounds__(kBlock) void k_combine_reduce(ReduceParams p) {
     touch_kernargs<sizeof(ReduceParams)>();
     __shared__ int cs_lds[kWavesPerBlock][kWave];
@@ -210,7 +192,7 @@ __global__ __launch_bounds__(kBlock) void k_combine_reduce(ReduceParams p) {
                       p.stream_min);
     if (!active) return;
     if (p.bias != nullptr) add8(acc, reinterpret_cast<const u32x4*>(p.bias + (int64_t)t * p.H)[c]);
-    store_out<CACHED>(p.out, t, p.H, c, pack8(acc));
+    st_nt(reinterpret_cast<u32x4*>(p.out + (int64_t)t * p.H) + c, pack8(acc));
 }
 
 }  // namespace
@@ -231,10 +213,7 @@ hipError_t launch_combine_reduce(const Handle& h, const ReduceArgs& a, hipStream
     p.nitems = (int64_t)h.T * p.nseg;
     p.stream_min = p.nitems >= kStreamMinWaves ? kReduceStreamRows : INT_MAX;
     const unsigned nblocks = (unsigned)((p.nitems + kWavesPerBlock - 1) / kWavesPerBlock);
-    if ((int64_t)h.T * a.hidden * 2 <= kCachedOutMaxBytes)
-        hipLaunchKernelGGL(k_combine_reduce<true>, dim3(nblocks), dim3(kBlock), 0, stream, p);
-    else
-        hipLaunchKernelGGL(k_combine_reduce<false>, dim3(nblocks), dim3(kBlock), 0, stream, p);
+    hipLaunchKernelGGL(k_combine_reduce, dim3(nblocks), dim3(kBlock), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -261,10 +240,7 @@ hipError_t launch_combine(const Handle& h, const CombineArgs& a, hipStream_t str
     p.nitems = (int64_t)h.T * p.nseg;
     p.stream_min = p.nitems >= kStreamMinWaves ? kCombineStreamRows : INT_MAX;
     const unsigned nblocks = (unsigned)((p.nitems + kWavesPerBlock - 1) / kWavesPerBlock);
-    if ((int64_t)h.T * a.hidden * 2 <= kCachedOutMaxBytes)
-        hipLaunchKernelGGL(k_combine<true>, dim3(nblocks), dim3(kBlock), 0, stream, p);
-    else
-        hipLaunchKernelGGL(k_combine<false>, dim3(nblocks), dim3(kBlock), 0, stream, p);
+    hipLaunchKernelGGL(k_combine, dim3(nblocks), dim3(kBlock), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -107,6 +107,7 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
 // 16-byte vector of four 32-bit words (a native vector type, so it maps to dwordx4 loads and stores).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Streaming 16-byte global accesses (non-temporal: the data is touched once).
 // Reads one dword of every 64-byte line of the kernel's first `bytes` argument bytes, all issued before one wait.
 // The compiler fetches argument fields on demand (it re-reads them rather than hold them in scalar registers),
 // one wait each; a launch's arguments are new memory, so without this each wait on a line not yet read is a
@@ -121,20 +122,7 @@ __device__ __forceinline__ void touch_kernargs() {
     asm volatile("" ::"s"(s));
 }
 
-// Streaming 16-byte global accesses (non-temporal: the data is touched once, and is not kept in the
-// memory-side cache).
 __device__ __forceinline__ u32x4 ld_nt(const u32x4* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void st_nt(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
-
-// 16-byte store at byte offset `off` of a row of `row_bytes` bytes, written at device scope (the sc1 cache
-// policy, not non-temporal): it passes through L2 and is kept in the 256 MB memory-side cache, which writes it
-// to HBM later.  `row` must be the same for every lane of the wave (it becomes a buffer resource in scalar
-// registers); offsets at or past row_bytes are dropped by the hardware's range check.
-constexpr int kBufferRsrcWord3 = 0x00020000;   // raw (untyped) buffer, 32-bit data format
-constexpr int kCachePolicySc1 = 16;
-__device__ __forceinline__ void st_sc1(void* row, int row_bytes, int off, u32x4 v) {
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(row, 0, row_bytes, kBufferRsrcWord3);
-    __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, kCachePolicySc1);
-}
 
 }  // namespace ep
