@@ -107,7 +107,6 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
 // 16-byte vector of four 32-bit words (a native vector type, so it maps to dwordx4 loads and stores).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Streaming 16-byte global accesses (non-temporal: the data is touched once).
 // Reads one dword of every 64-byte line of the kernel's first `bytes` argument bytes, all issued before one wait.
 // The compiler fetches argument fields on demand (it re-reads them rather than hold them in scalar registers),
 // one wait each; a launch's arguments are new memory, so without this each wait on a line not yet read is a
@@ -122,6 +121,7 @@ __device__ __forceinline__ void touch_kernargs() {
     asm volatile("" ::"s"(s));
 }
 
+// Streaming 16-byte global accesses (non-temporal: the data is touched once).
 __device__ __forceinline__ u32x4 ld_nt(const u32x4* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void st_nt(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
 
