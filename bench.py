@@ -548,10 +548,12 @@ def measure_dispatch_bound(ep, W, dev, n, probe):
 
 # ---- context measurements -----------------------------------------------------------------------------------
 
-def measure_epilogues(ep, W, dev, n):
+def measure_epilogues(ep, W, dev, n, probe=None):
     """Receiver-side placement and source-side reduce at the EP8 shapes: rank 0 (experts 0..31 of 256) receiving
     the rows of 7 other ranks of 4096 tokens each (top-8 uniform routing, FP8 rows + 56 scales, alignment 128),
-    and the reduce of 8 returned windows of 4096 x 7168 BF16 rows with the local part and a bias."""
+    and the reduce of 8 returned windows of 4096 x 7168 BF16 rows with the local part and a bias.  Back to back
+    (events), and with a probe also flushed (the placement's 140 MB of received rows stay in the memory-side
+    cache between back-to-back calls, so the flushed figure is the one with them coming from HBM)."""
     import torch
 
     cfg = W.CONFIGS["ep8"]
@@ -581,8 +583,10 @@ def measure_epilogues(ep, W, dev, n):
     V = int(cnt.sum())
     P = int(lr["psum_num_recv_tokens_per_expert"][-1].item()) - V
     row_b = H + 4 * G
-    t_rows = events_us(lambda: ep.ep_dispatch_rows(hr, rows, sc, tw, do_zero_padding=False, out=out), n)
+    place = lambda: ep.ep_dispatch_rows(hr, rows, sc, tw, do_zero_padding=False, out=out)
+    t_rows = events_us(place, n)
     b_rows = n_valid * row_b + R * T * K * 12 + V * (row_b + 8) + P * 8
+    f_rows = flushed_us(place, probe)[0] if probe is not None else None
 
     inp = W.make_inputs("ep8")
     h0, l0 = ep.ep_get_layout(inp["topk_idx"].to(dev), E, R, 0, A)
@@ -590,17 +594,23 @@ def measure_epilogues(ep, W, dev, n):
     local = W.random_expert_outputs(T, H, seed=4, device=dev)
     bias = W.random_expert_outputs(T, H, seed=5, device=dev)
     red = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    t_red = events_us(lambda: ep.ep_combine_reduce(h0, parts, local, bias, out=red), n)
+    reduce = lambda: ep.ep_combine_reduce(h0, parts, local, bias, out=red)
+    t_red = events_us(reduce, n)
+    f_red = flushed_us(reduce, probe)[0] if probe is not None else None
     ntr = l0["num_tokens_per_rank"].cpu().numpy()
     n_part = int(sum(ntr[r] for r in range(1, R)))
     b_red = n_part * 2 * H + 3 * T * 2 * H + T * R * 4
     hr.free()
     h0.free()
-    return dict(
+    res = dict(
         dispatch_rows=dict(us=round(t_rows, 2), bytes=b_rows, GBps=round(rate(b_rows, t_rows), 1),
                            received_rows=n_valid, placed_rows=V),
         combine_reduce=dict(us=round(t_red, 2), bytes=b_red, GBps=round(rate(b_red, t_red), 1),
                             partial_rows=n_part))
+    for k, f, b in (("dispatch_rows", f_rows, b_rows), ("combine_reduce", f_red, b_red)):
+        if f is not None:
+            res[k].update(us_flushed_median=round(f, 2), GBps_flushed=round(rate(b, f), 1))
+    return res
 
 
 def local_rows_by_token(recv_src, used, T, K):
@@ -892,7 +902,7 @@ def main():
         bound = measure_dispatch_bound(ep, W, dev, args.steps, probe)
     elif args.bound and args.workload == "ep8":
         bound = measure_send_bound(ep, W, dev, args.steps, probe)
-    epi = measure_epilogues(ep, W, dev, args.steps) if args.epilogues else None
+    epi = measure_epilogues(ep, W, dev, args.steps, probe if args.flushed else None) if args.epilogues else None
     decode = measure_decode(ep, W, dev, args.steps) if args.decode else None
     copy_ceiling = measure_copy_ceiling(dev, 20, probe) if args.copy_ceiling else None
     del probe
