@@ -863,6 +863,31 @@ def main():
         step_graph_us = round((time.perf_counter() - g0) * 1e6 / args.steps, 2)
         del graph
 
+    # the same eager step with x taken in turn from 8 copies (470 MB at prefill, more than the 256 MB
+    # memory-side cache), so that the dispatch never finds rows an earlier step left in that cache: context for
+    # the headline step, which reads the same x every step, as a layer's router leaves its x there just before
+    step_x_cold_us = None
+    if args.trace:
+        progress("steps with x cold")
+        xs = [x.clone() for _ in range(8)]
+
+        def step_x(i):
+            h, _, _ = ep.ep_layout_dispatch(idx, xs[i % len(xs)], E, R, cfg.rank, cfg.expert_alignment, w,
+                                            fp8=cfg.fp8, do_zero_padding=cfg.zero_padding, out=dout, workspace=ws,
+                                            outputs=lay_out)
+            ep.ep_combine(h, y, w, bias, out=out)
+            return h
+
+        for i in range(len(xs)):
+            step_x(i)
+        torch.cuda.synchronize()
+        c0 = time.perf_counter()
+        for i in range(args.steps):
+            step_x(i)
+        torch.cuda.synchronize()
+        step_x_cold_us = round((time.perf_counter() - c0) * 1e6 / args.steps, 2)
+        del xs
+
     # device counts after the timed loop
     cnt = lay_out["num_tokens_per_expert"].cpu().numpy()
     psum = lay_out["psum_num_recv_tokens_per_expert"].cpu().numpy()
@@ -927,6 +952,7 @@ def main():
                "ep_combine between device syncs, host clock; per call: events around K back-to-back launches, "
                "and flushed (2 GiB read sweep before each of 10 + 50 samples, kernel durations from a trace)",
         step_graph_replay_us=step_graph_us,
+        step_x_cold_us=step_x_cold_us,
         step_kernels_us=step_kernels,
         kernels=head,
         roofline=roofline,
