@@ -20,7 +20,8 @@ move: every token row read once, every routed row written once, padding rows whe
 the expert rows gathered once by combine and the output written once (bytes_model()).  `roofline` is for the
 dominant kernel, `cpu_baseline` the oracle timed on the host (one pinned core, and all cores over token
 ranges).  `workloads` has every workload (tiny, decode, prefill, ep8, skewed) measured the same way;
-`dispatch_bound` times the prefill dispatch's write stream and read stream on their own (bench_probe.hip).
+`dispatch_bound` times the prefill dispatch's write stream and read stream on their own, `combine_bound` the
+prefill combine's gathers and output writes on their own (bench_probe.hip).
 `step_kernels_us` gives each kernel's GPU time inside the step (a kernel trace of K more eager steps), and
 `roofline.frac_in_step` the dominant kernel's rate there.
 
@@ -273,6 +274,10 @@ class Probe:
         self.lib.probe_copy.argtypes = [Pt, Pt, I64, Pt]
         self.lib.probe_send_writes.restype = I
         self.lib.probe_send_writes.argtypes = [Pt, Pt, I, I, I, Pt, Pt, Pt, Pt, Pt, Pt, Pt, I, Pt]
+        self.lib.probe_combine_gathers.restype = I
+        self.lib.probe_combine_gathers.argtypes = [Pt, Pt, I, I, I, Pt, Pt]
+        self.lib.probe_row_writes.restype = I
+        self.lib.probe_row_writes.argtypes = [Pt, I, I, Pt]
         self.junk = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev).fill_(3)
         self.sink = torch.zeros(1, dtype=torch.int32, device=dev)
 
@@ -631,6 +636,48 @@ def local_rows_by_token(recv_src, used, T, K):
     return token_rows, rows.size, pads
 
 
+def measure_combine_bound(ep, W, dev, n, probe):
+    """The weighted combine on the prefill workload, taken apart like the dispatch: its gathers alone
+    (probe_combine_gathers: the same rows of y for every token, one wave per (token, 1 KiB segment), issued as the
+    combine issues them, no stores) and its output stream alone (probe_row_writes: the [T, H] bf16 rows, one wave
+    per (token, 1 KiB segment), nothing read), against the combine itself.  Back to back, events."""
+    import torch
+
+    inp = W.make_inputs("prefill")
+    cfg = inp["cfg"]
+    T, K, E, A, H = cfg.num_tokens, cfg.num_topk, cfg.num_experts, cfg.expert_alignment, cfg.hidden
+    idx, w, x = inp["topk_idx"].to(dev), inp["topk_weights"].to(dev), inp["x"].to(dev)
+    h, lay = ep.ep_get_layout(idx, E, 1, 0, A)
+    d = ep.ep_dispatch(h, x, w, fp8=True, do_zero_padding=True)
+    torch.cuda.synchronize()
+    used = int(lay["psum_num_recv_tokens_per_expert"][-1].item())
+    token_rows, V, _ = local_rows_by_token(d["recv_src_idx"].cpu().numpy(), used, T, K)
+    tr = torch.from_numpy(token_rows).to(dev)
+    y = W.random_expert_outputs(h.recv_capacity, H, seed=99, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    lib, stream = probe.lib, probe._stream
+
+    def gathers():
+        rc = lib.probe_combine_gathers(y.data_ptr(), tr.data_ptr(), T, K, H, probe.sink.data_ptr(), stream())
+        assert rc == 0, rc
+
+    def writes():
+        rc = lib.probe_row_writes(out.data_ptr(), T, H, stream())
+        assert rc == 0, rc
+
+    us = {k: events_us(f, n) for k, f in (("gathers", gathers), ("writes", writes),
+                                          ("combine", lambda: ep.ep_combine(h, y, w, out=out)))}
+    gbytes, wbytes = V * 2 * H + T * K * 4, T * 2 * H
+    h.free()
+    return dict(
+        note="prefill weighted combine: its gathers alone and its output writes alone (bench_probe.hip, same rows "
+             "and work split), back to back, events",
+        gathers_only_us=round(us["gathers"], 2), gather_bytes=gbytes,
+        gathers_only_GBps=round(rate(gbytes, us["gathers"]), 1),
+        writes_only_us=round(us["writes"], 2), write_bytes=wbytes, writes_only_GBps=round(rate(wbytes, us["writes"]), 1),
+        sum_us=round(us["gathers"] + us["writes"], 2), combine_us=round(us["combine"], 2))
+
+
 def measure_send_bound(ep, W, dev, n, probe):
     """The FP8 dispatch with send windows on the ep8 workload (rank 0 of 8, no zero padding), taken apart like the
     prefill dispatch: its stores alone (probe_send_writes: the same local expert-major rows and window rows with
@@ -923,8 +970,10 @@ def main():
 
     progress("dispatch bound, epilogues, decode, copy ceiling")
     bound = None
+    combine_bound = None
     if args.bound and args.workload == "prefill":
         bound = measure_dispatch_bound(ep, W, dev, args.steps, probe)
+        combine_bound = measure_combine_bound(ep, W, dev, args.steps, probe)
     elif args.bound and args.workload == "ep8":
         bound = measure_send_bound(ep, W, dev, args.steps, probe)
     epi = measure_epilogues(ep, W, dev, args.steps, probe if args.flushed else None) if args.epilogues else None
@@ -958,6 +1007,7 @@ def main():
         roofline=roofline,
         cpu_baseline=cpu,
         dispatch_bound=bound,
+        combine_bound=combine_bound,
         workloads=table,
         epilogues=epi,
         decode=decode,

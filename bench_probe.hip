@@ -13,11 +13,18 @@
 //                          e4m3 bytes and scales to its local expert-major rows and to its row in every other
 //                          rank's window, the local rows' metadata and the window rows' source index -- and no
 //                          source reads;
+//   probe_combine_gathers  every gather of the weighted combine -- 16-byte non-temporal loads of each token's rows
+//                          of y, one wave per (token, 1 KiB segment), issued as the combine issues them (one row
+//                          at a time for 8 or more rows in a grid of 16,384 waves or more, else in batches of up
+//                          to 8) -- and no stores;
+//   probe_row_writes       the combine's output stream alone: one wave per (token, 1 KiB segment), one 16-byte
+//                          non-temporal store per lane, nothing read;
 //   probe_flush            plain loads over a large buffer (a cache flush between timed samples);
 //   probe_copy             a flat copy, one wave per 1 KiB (a 16-byte non-temporal load, then a store per lane):
 //                          the rate this chip gives a 1 : 1 read / write stream, as context for the kernels.
-// The dispatch probes store a constant pattern, so they say nothing about correctness; they bound the dispatch's
-// time from below: on HBM the reads and the writes share each channel's data bus.
+// The dispatch and combine probes store a constant pattern (or nothing), so they say nothing about correctness;
+// with both streams coming from HBM, a kernel's reads alone plus its writes alone bound its time from below: the
+// reads and the writes share each channel's data bus.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -158,6 +165,67 @@ __global__ __launch_bounds__(kBlock) void k_probe_reads(ReadArgs a) {
     if (acc == a.never) a.sink[0] = (int32_t)acc;
 }
 
+struct GatherArgs {
+    const u32x4* y;              // [rows, nchunk] bf16 rows as 16-byte chunks
+    const int32_t* token_rows;   // [T, K] rows of each token's entries, valid ones first, -1 past them
+    int T, K, nchunk, nseg;      // nchunk: 16-byte chunks per row; nseg: 1 KiB segments per row
+    int64_t nitems;
+    int stream_one;              // a wave with 8 or more rows loads them one at a time
+    int32_t* sink;               // written only if the loads' xor equals `never` (it does not)
+    uint32_t never;
+};
+
+template <int N>
+__device__ __forceinline__ uint32_t gather_xor(const u32x4* base, int rows, int nchunk, int kb) {
+    u32x4 v[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        v[i] = __builtin_nontemporal_load(base + (int64_t)__builtin_amdgcn_readlane(rows, kb + i) * nchunk);
+    uint32_t x = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) x ^= v[i][0] ^ v[i][1] ^ v[i][2] ^ v[i][3];
+    return x;
+}
+
+__global__ __launch_bounds__(kBlock) void k_probe_gathers(GatherArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    if (gw >= a.nitems) return;
+    const int t = (int)(gw / a.nseg), s = (int)(gw % a.nseg);
+    const int r = lane < a.K ? a.token_rows[(int64_t)t * a.K + lane] : -1;
+    const int nv = __builtin_popcountll(__builtin_amdgcn_ballot_w64(r >= 0));
+    const int c = s * kWave + lane;
+    const u32x4* base = a.y + (c < a.nchunk ? c : 0);
+    uint32_t acc = 0;
+    if (a.stream_one && nv >= 8) {
+        for (int k = 0; k < nv; ++k) acc ^= gather_xor<1>(base, r, a.nchunk, k);
+    } else {
+        int kb = 0;
+        for (; kb + 8 <= nv; kb += 8) acc ^= gather_xor<8>(base, r, a.nchunk, kb);
+        switch (nv - kb) {
+            case 1: acc ^= gather_xor<1>(base, r, a.nchunk, kb); break;
+            case 2: acc ^= gather_xor<2>(base, r, a.nchunk, kb); break;
+            case 3: acc ^= gather_xor<3>(base, r, a.nchunk, kb); break;
+            case 4: acc ^= gather_xor<4>(base, r, a.nchunk, kb); break;
+            case 5: acc ^= gather_xor<5>(base, r, a.nchunk, kb); break;
+            case 6: acc ^= gather_xor<6>(base, r, a.nchunk, kb); break;
+            case 7: acc ^= gather_xor<7>(base, r, a.nchunk, kb); break;
+            default: break;
+        }
+    }
+    if (acc == a.never) a.sink[0] = (int32_t)acc;
+}
+
+__global__ __launch_bounds__(kBlock) void k_probe_row_writes(u32x4* out, int nchunk, int nseg, int64_t nitems) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    if (gw >= nitems) return;
+    const int64_t t = gw / nseg;
+    const int c = (int)(gw % nseg) * kWave + lane;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    if (c < nchunk) __builtin_nontemporal_store(z, out + t * nchunk + c);
+}
+
 __global__ __launch_bounds__(kBlock) void k_probe_flush(const u32x4* p, int64_t n16, int32_t* sink, uint32_t never) {
     const int64_t stride = (int64_t)gridDim.x * kBlock;
     uint32_t acc = 0;
@@ -248,6 +316,36 @@ int probe_dispatch_reads(const void* x, const int32_t* token_rows, int T, int K,
     a.never = 0x9E3779B9u;
     const int64_t nblocks = (a.ntok_items + kWavesPerBlock - 1) / kWavesPerBlock;
     hipLaunchKernelGGL(k_probe_reads, dim3((unsigned)nblocks), dim3(kBlock), 0, static_cast<hipStream_t>(stream), a);
+    return (int)hipGetLastError();
+}
+
+// y: rows of H bf16 values; token_rows [T, K] as for probe_dispatch_reads.
+int probe_combine_gathers(const void* y, const int32_t* token_rows, int T, int K, int H, int32_t* sink, void* stream) {
+    if (T < 1 || K < 1 || K > kWave || H < 8 || H % 8 != 0) return -1;
+    GatherArgs a;
+    a.y = static_cast<const u32x4*>(y);
+    a.token_rows = token_rows;
+    a.T = T;
+    a.K = K;
+    a.nchunk = H / 8;
+    a.nseg = (a.nchunk + kWave - 1) / kWave;
+    a.nitems = (int64_t)T * a.nseg;
+    a.stream_one = a.nitems >= 16384 ? 1 : 0;
+    a.sink = sink;
+    a.never = 0x9E3779B9u;
+    const int64_t nblocks = (a.nitems + kWavesPerBlock - 1) / kWavesPerBlock;
+    hipLaunchKernelGGL(k_probe_gathers, dim3((unsigned)nblocks), dim3(kBlock), 0, static_cast<hipStream_t>(stream), a);
+    return (int)hipGetLastError();
+}
+
+// out: [T, H] bf16 rows, overwritten with zeros.
+int probe_row_writes(void* out, int T, int H, void* stream) {
+    if (T < 1 || H < 8 || H % 8 != 0) return -1;
+    const int nchunk = H / 8, nseg = (nchunk + kWave - 1) / kWave;
+    const int64_t nitems = (int64_t)T * nseg;
+    const int64_t nblocks = (nitems + kWavesPerBlock - 1) / kWavesPerBlock;
+    hipLaunchKernelGGL(k_probe_row_writes, dim3((unsigned)nblocks), dim3(kBlock), 0, static_cast<hipStream_t>(stream),
+                       static_cast<u32x4*>(out), nchunk, nseg, nitems);
     return (int)hipGetLastError();
 }
 

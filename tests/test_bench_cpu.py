@@ -90,3 +90,21 @@ def test_local_rows_by_token_inverts_the_source_index():
         mine = [r for r in range(used) if src[r] == t]
         assert token_rows[t, :len(mine)].tolist() == mine
         assert (token_rows[t, len(mine):] == -1).all()
+
+
+def test_probe_library_exports_what_bench_calls():
+    """libbench_probe.so (built by __graft_entry__.build()) exports every probe bench.py declares: the Probe class
+    sets argtypes on each of them, so a missing symbol would only surface on the GPU machine."""
+    import ctypes
+    import re
+
+    import pytest
+
+    if not os.path.exists(bench.PROBE_LIB):
+        pytest.skip("libbench_probe.so is not built")
+    lib = ctypes.CDLL(bench.PROBE_LIB)
+    src = open(os.path.join(ROOT, "bench.py")).read()
+    names = sorted(set(re.findall(r"self\.lib\.(probe_\w+)\.argtypes", src)))
+    assert {"probe_combine_gathers", "probe_row_writes", "probe_dispatch_writes", "probe_flush"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
