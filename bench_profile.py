@@ -187,6 +187,13 @@ def summarize(workload, out, traffic_json=None):
                       "%.2f; the dispatch %.2f." % (b["write_only_us"], b["write_bytes"] / 1e6, b["write_only_GBps"],
                                                     b["read_only_us"], b["read_bytes"] / 1e6, b["read_only_GBps"],
                                                     b["sum_us"], b["dispatch_us"])]
+        c = line.get("combine_bound")
+        if c:
+            lines += ["", "The combine taken apart in the same run (bench.py `combine_bound`, events, us): its gathers "
+                      "alone %.2f (%.1f MB, %.0f GB/s), its output writes alone %.2f (%.1f MB, %.0f GB/s), their sum "
+                      "%.2f; the combine %.2f." % (c["gathers_only_us"], c["gather_bytes"] / 1e6, c["gathers_only_GBps"],
+                                                   c["writes_only_us"], c["write_bytes"] / 1e6, c["writes_only_GBps"],
+                                                   c["sum_us"], c["combine_us"])]
 
     fetch = counters(os.path.join(out, "%s_fetch" % workload), "FETCH_SIZE")
     write = counters(os.path.join(out, "%s_write" % workload), "WRITE_SIZE")
